@@ -1,0 +1,128 @@
+/*
+ * pivot.h - C ABI of the PIVOT group-shared sparse-attention indexer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (PIVOT paper summary page, picx.dev):
+ *   eq. (1)  I_{t,s} = sum_{j<H} w_{t,j} ReLU(q_{t,j} . k_s),   T_t = TopK(I_{t,:}, k)
+ *   eq. (2)  prefill groups: g consecutive query rows
+ *   eq. (3)  decode groups: the current token and its d drafts, g = d + 1
+ *   eq. (4)  proxy: per-head mean of the group's q and w
+ *   eq. (5)  proxy scan: Ibar_s = sum_j wbar_j ReLU(qbar_j . k_s), s <= t
+ *   eq. (6)  PIVOT-Reuse: the proxy's top-k is every member's T_t
+ *   eq. (7)  PIVOT-Refine candidates: C = TopK(Ibar, c), c = 2k by default
+ *   eqs. (8)-(9)  each member re-scores only C with its own q, w; TopK(., k)
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   - a query row r of a sequence sits at position t = lk - lq + r; it scores
+ *     keys s <= t (inclusive);
+ *   - a group's proxy scans s <= t_last (its last member's position) once;
+ *     Reuse gives that one row to every member (so an earlier member may get
+ *     positions in (t, t_last]); a Refine member at t drops candidates s > t;
+ *   - the proxy is an fp32 sum over members in order, one division by the
+ *     member count (a short last group uses its own count), rounded to the
+ *     q storage type (RNE); wbar stays fp32;
+ *   - selection order: higher score first, equal scores by lower position;
+ *   - every output row lists the selected positions in ASCENDING order,
+ *     followed by -1 (scores: the matching values, then -INFINITY);
+ *   - a row holds min(k, #eligible keys) valid entries; |C| = min(c, t_last+1).
+ *
+ * Layouts (dense, row-major, device memory unless stated):
+ *   q        [batch, lq, heads, dim]   dtype (bf16 or f32)
+ *   w        [batch, lq, heads]        f32
+ *   k        [batch, lk, dim]          dtype; one key per token, shared by all heads
+ *   indices  [batch, lq, topk]         int32 (required output)
+ *   scores   [batch, lq, topk]         f32 (optional output, may be NULL)
+ *   candidates        [batch, G, c]    int32 (optional Refine output, ascending, -1 pad)
+ *   candidate_counts  [batch, G]       int32 (optional Refine output, |C|)
+ *   where G = ceil(lq / g).
+ *
+ * Ownership and execution: the caller owns every buffer (the library never
+ * allocates or frees device memory). All work is enqueued on `stream` (a
+ * hipStream_t passed as void*; NULL = default stream) and the call returns
+ * without synchronising. Arguments are validated before anything is enqueued;
+ * on error nothing is written and a status is returned; pivot_last_error()
+ * then describes it (thread-local). Calls are re-entrant; calls that share a
+ * workspace must not overlap on different streams.
+ *
+ * Fast path: bf16 with heads == 64 and dim == 128 runs on bf16 MFMA with fp32
+ * accumulation. Every other shape, and f32 inputs, runs the general kernels,
+ * whose scores follow the exact fp32 order of the definition above (heads
+ * ascending, dims ascending, one rounding per product and per sum).
+ */
+#ifndef PIVOT_H
+#define PIVOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PIVOT_ABI_VERSION 1
+
+typedef enum {
+    PIVOT_OK = 0,
+    PIVOT_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad relation between sizes */
+    PIVOT_ERR_UNSUPPORTED = 2, /* a shape or mode this build has no kernel for */
+    PIVOT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pivot_workspace_size() */
+    PIVOT_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} pivot_status;
+
+typedef enum { PIVOT_F32 = 0, PIVOT_BF16 = 1 } pivot_dtype;
+
+typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2 } pivot_variant;
+
+/* Problem shape. Prefill: batch = 1 (or more independent sequences), lq = lk.
+ * Decode (eq. 3): lq = g rows at the last g positions of each sequence. */
+typedef struct {
+    int64_t batch; /* >= 1 */
+    int64_t lq;    /* query rows per sequence, 1 <= lq <= lk */
+    int64_t lk;    /* key rows per sequence, lk < 2^31 */
+    int32_t heads; /* H_I >= 1 */
+    int32_t dim;   /* d >= 1 (multiple of 8 for bf16, of 4 for f32) */
+    int32_t dtype; /* pivot_dtype of q and k */
+} pivot_problem;
+
+/* Bytes of device workspace a call needs (variant: pivot_variant; g, c are
+ * ignored where the variant has no such parameter). */
+pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32_t g, int32_t topk, int32_t c,
+                                  size_t *bytes);
+
+/* eq. (1) with T_t = TopK(I_{t,:}, topk): the dense DSA indexer (PIVOT with
+ * g = 1). indices/scores as above. */
+pivot_status pivot_index_dense(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t topk,
+                               int32_t *indices, float *scores, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* eqs. (4)-(6): PIVOT-Reuse with groups of g rows (g >= 1). */
+pivot_status pivot_index_reuse(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
+                               int32_t topk, int32_t *indices, float *scores, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* eqs. (4)-(5), (7)-(9): PIVOT-Refine with groups of g rows and c >= topk
+ * candidates per group. candidates / candidate_counts may be NULL. */
+pivot_status pivot_index_refine(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
+                                int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates,
+                                int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
+
+/* eq. (4) alone: qbar [batch, G, heads, dim] in the q dtype, wbar [batch, G,
+ * heads] f32. Needs no workspace. */
+pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const float *w, void *qbar, float *wbar,
+                        void *stream);
+
+/* eq. (5) alone, for inspection: out [batch, G, lk] f32 receives the proxy
+ * score of every key s <= t_last of each group and -INFINITY after it.
+ * qbar/wbar as produced by pivot_pool (pass q, w with g = 1 for eq. 1). */
+pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *qbar, const float *wbar,
+                                const void *k, float *out, void *stream);
+
+const char *pivot_status_str(pivot_status s);
+const char *pivot_last_error(void);
+int32_t pivot_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIVOT_H */

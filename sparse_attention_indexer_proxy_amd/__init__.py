@@ -1,0 +1,226 @@
+"""PIVOT group-shared sparse-attention indexer on MI355X (gfx950).
+
+Thin Python binding of ``libpivot.so`` (C ABI in ``include/pivot.h``): it
+checks tensors, allocates outputs and workspace with torch and passes raw
+device pointers plus the current HIP stream. Every step of the indexer runs
+in the library's HIP kernels; there is no other implementation behind these
+functions, and they raise if the library is missing.
+
+Tensors: q [B, Lq, H, d] (or [Lq, H, d]) bf16/f32, w [B, Lq, H] f32,
+k [B, Lk, d] (or [Lk, d]) in q's dtype, all on one CUDA (HIP) device.
+Outputs: int32 indices [B, Lq, topk], each row the selected positions in
+ascending order followed by -1; optional f32 scores aligned with them.
+Query row r of a sequence sits at position Lk - Lq + r.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "pool", "proxy_scores",
+           "workspace_size", "library_path", "load_library", "DENSE", "REUSE", "REFINE"]
+
+DENSE, REUSE, REFINE = 0, 1, 2
+_F32, _BF16 = 0, 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libpivot.so")
+_lib = None
+
+EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
+            "pivot_pool", "pivot_proxy_scores", "pivot_status_str", "pivot_last_error",
+            "pivot_abi_version")
+
+
+class PivotError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pivot status {status}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("lq", ctypes.c_int64), ("lk", ctypes.c_int64),
+                ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load libpivot.so (built in-tree by ``build.py``); raise if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m sparse_attention_indexer_proxy_amd.build`")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(Problem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.pivot_workspace_size.argtypes = [P, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.pivot_index_dense.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.pivot_index_reuse.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.pivot_index_refine.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.pivot_pool.argtypes = [P, i32, vp, vp, vp, vp, vp]
+    lib.pivot_proxy_scores.argtypes = [P, i32, vp, vp, vp, vp, vp]
+    for name in ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
+                 "pivot_pool", "pivot_proxy_scores"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pivot_status_str.argtypes = [ctypes.c_int]
+    lib.pivot_status_str.restype = ctypes.c_char_p
+    lib.pivot_last_error.restype = ctypes.c_char_p
+    lib.pivot_abi_version.restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise PivotError(status, f"{lib.pivot_status_str(status).decode()}: {lib.pivot_last_error().decode()}")
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return _BF16
+    if dt == torch.float32:
+        return _F32
+    raise TypeError(f"q and k must be bfloat16 or float32 (got {dt})")
+
+
+def _prepare(q, w, k):
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, w = q.unsqueeze(0), w.unsqueeze(0)
+        k = k.unsqueeze(0) if k.dim() == 2 else k
+    if q.dim() != 4 or w.dim() != 3 or k.dim() != 3:
+        raise ValueError("expected q [B,Lq,H,d], w [B,Lq,H], k [B,Lk,d]")
+    B, Lq, H, D = q.shape
+    if tuple(w.shape) != (B, Lq, H) or k.shape[0] != B or k.shape[2] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, w {tuple(w.shape)}, k {tuple(k.shape)}")
+    if k.dtype != q.dtype:
+        raise TypeError("k must have q's dtype")
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    for name, t in (("q", q), ("w", w), ("k", k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != q.device:
+            raise ValueError("q, w and k must be on one device")
+    q, w, k = q.contiguous(), w.contiguous(), k.contiguous()
+    prob = Problem(B, Lq, k.shape[1], H, D, _dtype_code(q.dtype))
+    return prob, q, w, k, squeeze
+
+
+def workspace_size(variant: int, B: int, Lq: int, Lk: int, H: int, D: int, dtype, g: int = 1, topk: int = 1,
+                   c: int = 0) -> int:
+    prob = Problem(B, Lq, Lk, H, D, _dtype_code(dtype))
+    out = ctypes.c_size_t(0)
+    _check(load_library().pivot_workspace_size(ctypes.byref(prob), variant, g, topk, c, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(prob, variant, g, topk, c, device, workspace):
+    need = ctypes.c_size_t(0)
+    _check(load_library().pivot_workspace_size(ctypes.byref(prob), variant, g, topk, c, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _outputs(prob, topk, device, return_scores):
+    idx = torch.empty((prob.batch, prob.lq, topk), dtype=torch.int32, device=device)
+    sc = torch.empty((prob.batch, prob.lq, topk), dtype=torch.float32, device=device) if return_scores else None
+    return idx, sc
+
+
+def _finish(squeeze, *ts):
+    out = tuple(t[0] if (squeeze and t is not None) else t for t in ts)
+    return out if len(out) > 1 else out[0]
+
+
+def index_dense(q, w, k, topk: int, *, return_scores: bool = False, workspace=None, stream=None):
+    """eq. (1): every query keeps the top-k of its prefix s <= t."""
+    prob, q, w, k, sq = _prepare(q, w, k)
+    ws, wsb = _workspace(prob, DENSE, 1, topk, 0, q.device, workspace)
+    idx, sc = _outputs(prob, topk, q.device, return_scores)
+    _check(load_library().pivot_index_dense(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k), topk, _ptr(idx),
+                                            _ptr(sc), _ptr(ws), wsb, _stream_ptr(stream, q.device)))
+    return _finish(sq, idx, sc) if return_scores else _finish(sq, idx)
+
+
+def index_reuse(q, w, k, g: int, topk: int, *, return_scores: bool = False, workspace=None, stream=None):
+    """eqs. (4)-(6): one proxy scan per group of g rows; its top-k is every
+    member's row."""
+    prob, q, w, k, sq = _prepare(q, w, k)
+    ws, wsb = _workspace(prob, REUSE, g, topk, 0, q.device, workspace)
+    idx, sc = _outputs(prob, topk, q.device, return_scores)
+    _check(load_library().pivot_index_reuse(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k), g, topk, _ptr(idx),
+                                            _ptr(sc), _ptr(ws), wsb, _stream_ptr(stream, q.device)))
+    return _finish(sq, idx, sc) if return_scores else _finish(sq, idx)
+
+
+def index_refine(q, w, k, g: int, topk: int, c: int | None = None, *, return_scores: bool = False,
+                 return_candidates: bool = False, workspace=None, stream=None):
+    """eqs. (4)-(5), (7)-(9): one proxy scan per group keeps c candidates
+    (default 2k); each member re-scores them and keeps its own top-k.
+    With return_candidates, also returns C [B, G, c] (ascending, -1 pad) and
+    |C| [B, G]."""
+    c = 2 * topk if c is None else c
+    prob, q, w, k, sq = _prepare(q, w, k)
+    ws, wsb = _workspace(prob, REFINE, g, topk, c, q.device, workspace)
+    idx, sc = _outputs(prob, topk, q.device, return_scores)
+    G = -(-prob.lq // g)
+    cand = cand_n = None
+    if return_candidates:
+        cand = torch.empty((prob.batch, G, c), dtype=torch.int32, device=q.device)
+        cand_n = torch.empty((prob.batch, G), dtype=torch.int32, device=q.device)
+    _check(load_library().pivot_index_refine(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k), g, topk, c, _ptr(idx),
+                                             _ptr(sc), _ptr(cand), _ptr(cand_n), _ptr(ws), wsb,
+                                             _stream_ptr(stream, q.device)))
+    outs = [idx]
+    if return_scores:
+        outs.append(sc)
+    if return_candidates:
+        outs += [cand, cand_n]
+    return _finish(sq, *outs)
+
+
+def pool(q, w, g: int, stream=None):
+    """eq. (4): proxies qbar [B, G, H, d] (q dtype) and wbar [B, G, H] f32."""
+    prob, q, w, _, sq = _prepare(q, w, q[..., 0, :] if q.dim() == 4 else q[:, 0, :])
+    G = -(-prob.lq // g)
+    qbar = torch.empty((prob.batch, G, prob.heads, prob.dim), dtype=q.dtype, device=q.device)
+    wbar = torch.empty((prob.batch, G, prob.heads), dtype=torch.float32, device=q.device)
+    _check(load_library().pivot_pool(ctypes.byref(prob), g, _ptr(q), _ptr(w), _ptr(qbar), _ptr(wbar),
+                                     _stream_ptr(stream, q.device)))
+    return _finish(sq, qbar, wbar)
+
+
+def proxy_scores(qbar, wbar, k, g: int, lq: int, stream=None):
+    """eq. (5): score rows [B, G, Lk] of the proxies (-inf after t_last).
+    ``lq`` is the query row count the groups were formed from."""
+    if qbar.dim() == 3:
+        qbar, wbar = qbar.unsqueeze(0), wbar.unsqueeze(0)
+        k = k.unsqueeze(0) if k.dim() == 2 else k
+    B, G, H, D = qbar.shape
+    if G != -(-lq // g):
+        raise ValueError("qbar's group count does not match lq and g")
+    qbar, wbar, k = qbar.contiguous(), wbar.contiguous(), k.contiguous()
+    prob = Problem(B, lq, k.shape[1], H, D, _dtype_code(qbar.dtype))
+    out = torch.empty((B, G, k.shape[1]), dtype=torch.float32, device=qbar.device)
+    _check(load_library().pivot_proxy_scores(ctypes.byref(prob), g, _ptr(qbar), _ptr(wbar), _ptr(k), _ptr(out),
+                                             _stream_ptr(stream, qbar.device)))
+    return out

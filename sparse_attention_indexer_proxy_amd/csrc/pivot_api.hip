@@ -1,0 +1,276 @@
+// C ABI of the PIVOT indexer: argument checks, workspace layout and the
+// launch sequence (pool -> scan/select -> refine) on the caller's stream.
+// Declarations and conventions: include/pivot.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "pivot.h"
+#include "pivot_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pivot_status fail(pivot_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxSel = int64_t(1) << 28;  // bound on topk and c (keeps buffer indices in int32)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+pivot_status check_problem(const pivot_problem *p)
+{
+    if (!p) return fail(PIVOT_ERR_INVALID_ARG, "problem is NULL");
+    if (p->batch < 1 || p->lq < 1 || p->lk < 1) return fail(PIVOT_ERR_INVALID_ARG, "batch, lq and lk must be >= 1");
+    if (p->lq > p->lk) return fail(PIVOT_ERR_INVALID_ARG, "lq (%lld) must not exceed lk (%lld)", (long long)p->lq,
+                                   (long long)p->lk);
+    if (p->lk >= (int64_t(1) << 31)) return fail(PIVOT_ERR_INVALID_ARG, "lk must be < 2^31");
+    if (p->heads < 1 || p->dim < 1) return fail(PIVOT_ERR_INVALID_ARG, "heads and dim must be >= 1");
+    if (p->dtype != PIVOT_F32 && p->dtype != PIVOT_BF16) return fail(PIVOT_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    const int vec = p->dtype == PIVOT_BF16 ? 8 : 4;
+    if (p->dim % vec != 0)
+        return fail(PIVOT_ERR_UNSUPPORTED, "dim must be a multiple of %d for this dtype (got %d)", vec, p->dim);
+    if (p->heads > 4096 || p->dim > 4096) return fail(PIVOT_ERR_UNSUPPORTED, "heads and dim are limited to 4096");
+    return PIVOT_OK;
+}
+
+pivot::LaunchShape shape_of(const pivot_problem *p)
+{
+    return pivot::LaunchShape{p->batch, p->lq, p->lk, p->heads, p->dim, p->dtype == PIVOT_BF16};
+}
+
+struct Layout {
+    int64_t G;
+    int g, K, cap;
+    bool pool;
+    size_t qbar, wbar, buf_s, buf_i, cand, cand_n, scratch, total;
+};
+
+pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, int32_t c, Layout *L)
+{
+    pivot_status st = check_problem(p);
+    if (st != PIVOT_OK) return st;
+    if (variant < PIVOT_DENSE || variant > PIVOT_REFINE) return fail(PIVOT_ERR_INVALID_ARG, "unknown variant %d", variant);
+    if (variant == PIVOT_DENSE) g = 1;
+    if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
+    if (topk < 1 || topk > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "topk must be in [1, 2^28] (got %d)", topk);
+    if (variant == PIVOT_REFINE) {
+        if (c < topk) return fail(PIVOT_ERR_INVALID_ARG, "refine needs c >= topk (c=%d, topk=%d)", c, topk);
+        if (c > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "c must be <= 2^28");
+    }
+    const pivot::LaunchShape sh = shape_of(p);
+    if (variant == PIVOT_REFINE && pivot::mfma_shape(sh) && g > 1024)
+        return fail(PIVOT_ERR_UNSUPPORTED, "refine supports g <= 1024");
+    Layout l{};
+    l.g = g;
+    l.G = (p->lq + g - 1) / g;
+    l.K = variant == PIVOT_REFINE ? c : topk;
+    int64_t cap = 2 * int64_t(l.K);
+    if (cap < l.K + 64) cap = l.K + 64;
+    cap = (cap + 63) / 64 * 64;
+    l.cap = static_cast<int>(cap);
+    l.pool = g > 1;
+    const size_t elt = p->dtype == PIVOT_BF16 ? 2 : 4;
+    const size_t groups = static_cast<size_t>(p->batch) * static_cast<size_t>(l.G);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
+    l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
+    l.buf_s = take(groups * cap * sizeof(float));
+    l.buf_i = take(groups * cap * sizeof(int32_t));
+    if (variant == PIVOT_REFINE) {
+        l.cand = take(groups * static_cast<size_t>(c) * sizeof(int32_t));
+        l.cand_n = take(groups * sizeof(int32_t));
+        l.scratch = take(groups * static_cast<size_t>(g) * static_cast<size_t>(c) * sizeof(float));
+    }
+    l.total = off;
+    *L = l;
+    return PIVOT_OK;
+}
+
+pivot_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return PIVOT_OK;
+    return fail(PIVOT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+pivot_status run(const pivot_problem *p, int variant, const void *q, const float *w, const void *k, int32_t g,
+                 int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts,
+                 void *ws, size_t ws_bytes, void *stream)
+{
+    Layout L;
+    pivot_status st = plan(p, variant, g, topk, c, &L);
+    if (st != PIVOT_OK) return st;
+    if (!q || !w || !k || !indices) return fail(PIVOT_ERR_INVALID_ARG, "q, w, k and indices must be non-NULL");
+    if (!ws || ws_bytes < L.total)
+        return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total, ws ? ws_bytes : size_t(0));
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+        return fail(PIVOT_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0)
+        return fail(PIVOT_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+
+    const pivot::LaunchShape sh = shape_of(p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+
+    const void *qsrc = q;
+    const float *wsrc = w;
+    if (L.pool) {
+        void *qbar = base + L.qbar;
+        float *wbar = reinterpret_cast<float *>(base + L.wbar);
+        st = hip_status(pivot::launch_pool(sh, L.g, L.G, q, w, qbar, wbar, s), "pool launch");
+        if (st != PIVOT_OK) return st;
+        qsrc = qbar;
+        wsrc = wbar;
+    }
+
+    int32_t *cand = candidates ? candidates : reinterpret_cast<int32_t *>(base + L.cand);
+    int32_t *cand_n = cand_counts ? cand_counts : reinterpret_cast<int32_t *>(base + L.cand_n);
+
+    pivot::ScanLaunch sl{};
+    sl.qsrc = qsrc;
+    sl.wsrc = wsrc;
+    sl.k = k;
+    sl.G = L.G;
+    sl.g = L.g;
+    sl.K = L.K;
+    sl.cap = L.cap;
+    sl.buf_s = reinterpret_cast<float *>(base + L.buf_s);
+    sl.buf_i = reinterpret_cast<int32_t *>(base + L.buf_i);
+    if (variant == PIVOT_REFINE) {
+        sl.out_idx = cand;
+        sl.out_sc = nullptr;
+        sl.out_count = cand_n;
+        sl.out_stride = c;
+        sl.to_candidates = 1;
+    } else {
+        sl.out_idx = indices;
+        sl.out_sc = scores;
+        sl.out_count = nullptr;
+        sl.out_stride = topk;
+        sl.to_candidates = 0;
+    }
+    sl.rows = nullptr;
+    st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
+    if (st != PIVOT_OK || variant != PIVOT_REFINE) return st;
+
+    pivot::RefineLaunch rl{};
+    rl.q = q;
+    rl.w = w;
+    rl.k = k;
+    rl.G = L.G;
+    rl.g = L.g;
+    rl.topk = topk;
+    rl.c = c;
+    rl.cand = cand;
+    rl.cand_n = cand_n;
+    rl.scratch = reinterpret_cast<float *>(base + L.scratch);
+    rl.out_idx = indices;
+    rl.out_sc = scores;
+    return hip_status(pivot::launch_refine(sh, rl, s), "refine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32_t g, int32_t topk, int32_t c,
+                                  size_t *bytes)
+{
+    if (!bytes) return fail(PIVOT_ERR_INVALID_ARG, "bytes is NULL");
+    Layout L;
+    pivot_status st = plan(p, variant, g, topk, c, &L);
+    if (st != PIVOT_OK) return st;
+    *bytes = L.total;
+    return PIVOT_OK;
+}
+
+pivot_status pivot_index_dense(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t topk,
+                               int32_t *indices, float *scores, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run(p, PIVOT_DENSE, q, w, k, 1, topk, 0, indices, scores, nullptr, nullptr, workspace, workspace_bytes,
+               stream);
+}
+
+pivot_status pivot_index_reuse(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
+                               int32_t topk, int32_t *indices, float *scores, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    return run(p, PIVOT_REUSE, q, w, k, g, topk, 0, indices, scores, nullptr, nullptr, workspace, workspace_bytes,
+               stream);
+}
+
+pivot_status pivot_index_refine(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
+                                int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates,
+                                int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run(p, PIVOT_REFINE, q, w, k, g, topk, c, indices, scores, candidates, candidate_counts, workspace,
+               workspace_bytes, stream);
+}
+
+pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const float *w, void *qbar, float *wbar,
+                        void *stream)
+{
+    pivot_status st = check_problem(p);
+    if (st != PIVOT_OK) return st;
+    if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
+    if (!q || !w || !qbar || !wbar) return fail(PIVOT_ERR_INVALID_ARG, "q, w, qbar and wbar must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(qbar) % 16 != 0)
+        return fail(PIVOT_ERR_INVALID_ARG, "q and qbar must be 16-byte aligned");
+    const int64_t G = (p->lq + g - 1) / g;
+    return hip_status(pivot::launch_pool(shape_of(p), g, G, q, w, qbar, wbar, static_cast<hipStream_t>(stream)),
+                      "pool launch");
+}
+
+pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *qbar, const float *wbar, const void *k,
+                                float *out, void *stream)
+{
+    pivot_status st = check_problem(p);
+    if (st != PIVOT_OK) return st;
+    if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
+    if (!qbar || !wbar || !k || !out) return fail(PIVOT_ERR_INVALID_ARG, "qbar, wbar, k and out must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(qbar) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0)
+        return fail(PIVOT_ERR_INVALID_ARG, "qbar and k must be 16-byte aligned");
+    pivot::ScanLaunch sl{};
+    sl.qsrc = qbar;
+    sl.wsrc = wbar;
+    sl.k = k;
+    sl.G = (p->lq + g - 1) / g;
+    sl.g = g;
+    sl.rows = out;
+    return hip_status(pivot::launch_scan(shape_of(p), sl, static_cast<hipStream_t>(stream)), "scan launch");
+}
+
+const char *pivot_status_str(pivot_status s)
+{
+    switch (s) {
+    case PIVOT_OK: return "ok";
+    case PIVOT_ERR_INVALID_ARG: return "invalid argument";
+    case PIVOT_ERR_UNSUPPORTED: return "unsupported";
+    case PIVOT_ERR_WORKSPACE: return "workspace too small";
+    case PIVOT_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *pivot_last_error(void) { return g_last_error; }
+
+int32_t pivot_abi_version(void) { return PIVOT_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pivot {
+
+struct LaunchShape {
+    int64_t B, Lq, Lk;
+    int H, D;
+    bool bf16;
+};
+
+// One scan launch: eq. (5) for every group, then either the streaming
+// selection of the best K (rows != nullptr selects the score-row output).
+struct ScanLaunch {
+    const void *qsrc;   // [B, G, H, D]
+    const float *wsrc;  // [B, G, H]
+    const void *k;      // [B, Lk, D]
+    int64_t G;
+    int g;
+    int K, cap;         // selection size and per-group buffer capacity
+    float *buf_s;       // [B*G, cap]
+    int32_t *buf_i;     // [B*G, cap]
+    int32_t *out_idx;   // rows [B, Lq, stride] or candidates [B, G, stride]
+    float *out_sc;      // rows only, nullable
+    int32_t *out_count; // candidates only, nullable
+    int out_stride;
+    int to_candidates;
+    float *rows;        // [B, G, Lk] score rows, or nullptr for selection
+};
+
+struct RefineLaunch {
+    const void *q;
+    const float *w;
+    const void *k;
+    int64_t G;
+    int g;
+    int topk, c;
+    const int32_t *cand;
+    const int32_t *cand_n;
+    float *scratch;     // [B*G, g, c]
+    int32_t *out_idx;
+    float *out_sc;
+};
+
+bool mfma_shape(const LaunchShape &sh);
+hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
+                       float *wbar, hipStream_t st);
+hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st);
+hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st);
+
+}  // namespace pivot

@@ -1,0 +1,892 @@
+// PIVOT group-shared sparse-attention indexer: HIP kernels for gfx950.
+//
+// Method (PIVOT paper summary page, picx.dev, sections "Introduction and
+// Theoretical Foundation" and "Methodology"):
+//   eq. (1)  I_{t,s} = sum_j w_{t,j} ReLU(q_{t,j} . k_s)      (dense indexer)
+//   eq. (4)  proxy qbar_j, wbar_j = per-head mean over the group
+//   eq. (5)  Ibar_s = sum_j wbar_j ReLU(qbar_j . k_s), s <= t_last
+//   eq. (6)  Reuse: TopK(Ibar, k) for every member
+//   eq. (7)  Refine candidates C = TopK(Ibar, c)
+//   eqs. (8)-(9)  member re-score over C and per-member TopK(., k)
+//
+// Kernels:
+//   k_pool                  eq. (4), HBM-bound streaming mean
+//   k_scan_mfma<Mode>       eq. (5) on bf16 MFMA (heads on the M axis, keys on
+//                           N, d as the contraction), ReLU + weighted head
+//                           reduction in registers, then either the streaming
+//                           top-K filter (Mode = kFilter, eqs. 6-7) or a plain
+//                           score row (Mode = kRows)
+//   k_scan_exact<T, Mode>   the same for any shape/dtype, in the exact fp32
+//                           order of the definition (heads, then dims ascending)
+//   k_refine_mfma           eqs. (8)-(9) over a gathered candidate tile
+//   k_refine_exact<T>       the same in exact order
+//
+// Selection: a wave keeps its group's survivors (score > tau) in a private
+// buffer in HBM, appended in ascending position. When the buffer is full the
+// wave radix-selects the K-th best (score desc, position asc), compacts the
+// buffer in place (stable) to exactly K entries and raises tau. At the end
+// the same select + stable compaction writes the rows in ascending position.
+// The full L/g x L score matrix never exists in memory.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pivot_kernels.h"
+
+namespace pivot {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ lane helpers
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int mbcnt(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ord_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float widen(T x);
+template <> __device__ __forceinline__ float widen<float>(float x) { return x; }
+template <> __device__ __forceinline__ float widen<uint16_t>(uint16_t x) { return bf16_bits_to_float(x); }
+
+// Workgroup-scope fence: orders this wave's global and LDS accesses so that
+// other lanes of the wave observe them (buffers are wave-private).
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
+// ------------------------------------------------------ group geometry
+struct Geo {
+    int64_t B, G, Lq, Lk;
+    int g;
+    __device__ __forceinline__ int64_t first_row(int64_t m) const { return m * g; }
+    __device__ __forceinline__ int64_t end_row(int64_t m) const { return (m + 1) * g < Lq ? (m + 1) * g : Lq; }
+    __device__ __forceinline__ int64_t t_last(int64_t m) const { return Lk - Lq + end_row(m) - 1; }
+};
+
+// ------------------------------------------------------------ wave select
+// Result of selecting the best K of n entries by (score desc, position asc),
+// with entries stored in ascending position: every entry whose key is above
+// `kth`, plus the first `quota` entries whose key equals `kth`.
+struct Sel {
+    uint32_t kth;
+    int quota;
+    bool all;
+};
+
+// Radix select over 8-bit digits of ord_key(score), most significant first,
+// with a per-wave 256-bin histogram in LDS. sc may point to global memory.
+__device__ Sel wave_select(const float *sc, int n, int K, uint32_t *hist)
+{
+    Sel r;
+    if (n <= K) {
+        r.all = true;
+        r.kth = 0;
+        r.quota = 0;
+        return r;
+    }
+    r.all = false;
+    const int l = lane_id();
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t remaining = static_cast<uint32_t>(K);
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = l; i < 256; i += kWave) hist[i] = 0u;
+        wave_fence();
+        for (int j0 = 0; j0 < n; j0 += kWave) {
+            const int j = j0 + l;
+            const bool in = j < n;
+            const uint32_t key = in ? ord_key(sc[j]) : 0u;
+            const bool match = in && (key & pmask) == prefix;
+            const uint32_t digit = (key >> shift) & 0xFFu;
+            const uint64_t mm = ballot(match);
+            if (mm == 0) continue;
+            const int first = __ffsll(static_cast<long long>(mm)) - 1;
+            const uint32_t d0 = __shfl(digit, first);
+            const uint64_t same = ballot(match && digit == d0);
+            if (same == mm) {
+                if (l == first) atomicAdd(&hist[d0], static_cast<uint32_t>(popc(mm)));
+            } else if (match) {
+                atomicAdd(&hist[digit], 1u);
+            }
+        }
+        wave_fence();
+        const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+        const uint32_t tot = c0 + c1 + c2 + c3;
+        uint32_t suf = tot; // inclusive suffix sum over lanes (higher lanes hold higher bins)
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t t = __shfl_down(suf, o);
+            if (l + o < kWave) suf += t;
+        }
+        const uint32_t above = suf - tot;
+        const bool here = above < remaining && remaining <= suf;
+        const uint64_t hm = ballot(here);
+        const int src = __ffsll(static_cast<long long>(hm)) - 1;
+        uint32_t dig = 0, abv = 0;
+        if (here) {
+            uint32_t cum = above;
+            if (cum + c3 >= remaining) {
+                dig = 4 * l + 3;
+            } else {
+                cum += c3;
+                if (cum + c2 >= remaining) {
+                    dig = 4 * l + 2;
+                } else {
+                    cum += c2;
+                    if (cum + c1 >= remaining) {
+                        dig = 4 * l + 1;
+                    } else {
+                        cum += c1;
+                        dig = 4 * l;
+                    }
+                }
+            }
+            abv = cum;
+        }
+        dig = __shfl(dig, src);
+        abv = __shfl(abv, src);
+        remaining -= abv;
+        prefix |= dig << shift;
+        pmask |= 0xFFu << shift;
+        wave_fence();
+    }
+    r.kth = prefix;
+    r.quota = static_cast<int>(remaining);
+    return r;
+}
+
+// Walk sc[0..n) in order and call emit(slot, j, score) for every selected
+// entry; slots are dense and ascending. Returns the number selected.
+template <class F> __device__ int wave_emit(const float *sc, int n, Sel s, F &&emit)
+{
+    const int l = lane_id();
+    int eq_seen = 0, out = 0;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + l;
+        const bool in = j < n;
+        const float v = in ? sc[j] : 0.0f;
+        bool take;
+        if (s.all) {
+            take = in;
+        } else {
+            const uint32_t key = ord_key(v);
+            const bool gt = in && key > s.kth;
+            const bool eq = in && key == s.kth;
+            const uint64_t em = ballot(eq);
+            const int er = eq_seen + mbcnt(em);
+            eq_seen += popc(em);
+            take = gt || (eq && er < s.quota);
+        }
+        const uint64_t tm = ballot(take);
+        if (take) emit(out + mbcnt(tm), j, v);
+        out += popc(tm);
+    }
+    return out;
+}
+
+// ------------------------------------------------- per-group filter state
+struct Filter {
+    float *bs;    // buffered scores (wave-private, ascending position)
+    int32_t *bi;  // buffered positions
+    int cap;      // buffer capacity (>= K + 64)
+    int K;        // entries to keep
+    int cnt;      // buffered entries (wave-uniform)
+    float tau;    // admission threshold (wave-uniform): keep score > tau
+    uint32_t *hist;
+
+    // One 64-key step: lane holds (score, position) or !valid.
+    __device__ __forceinline__ void push(bool valid, float score, int32_t pos)
+    {
+        bool pass = valid && score > tau;
+        uint64_t pm = ballot(pass);
+        if (pm == 0) return;
+        int n = popc(pm);
+        if (cnt + n > cap) {
+            compact();
+            pass = valid && score > tau;
+            pm = ballot(pass);
+            n = popc(pm);
+        }
+        if (pass) {
+            const int slot = cnt + mbcnt(pm);
+            bs[slot] = score;
+            bi[slot] = pos;
+        }
+        cnt += n;
+    }
+
+    // Keep exactly the best K buffered entries, in order; tau := K-th score.
+    __device__ void compact()
+    {
+        wave_fence();
+        const Sel s = wave_select(bs, cnt, K, hist);
+        float *bsl = bs;
+        int32_t *bil = bi;
+        const int kept = wave_emit(bs, cnt, s, [&](int slot, int j, float v) {
+            const int32_t p = bil[j];
+            bsl[slot] = v;
+            bil[slot] = p;
+        });
+        wave_fence();
+        cnt = kept;
+        tau = s.all ? tau : key_float(s.kth);
+    }
+};
+
+// Final selection of a group's buffer into its outputs.
+struct SelectionOut {
+    int32_t *idx;    // rows [B, Lq, stride] or candidates [B, G, stride]
+    float *sc;       // rows only (may be null)
+    int32_t *count;  // candidates only (may be null)
+    int stride;      // topk (rows) or c (candidates)
+    int to_candidates;
+};
+
+__device__ void finish_group(const Geo &geo, const SelectionOut &o, int64_t b, int64_t m, Filter &f)
+{
+    wave_fence();
+    const Sel s = wave_select(f.bs, f.cnt, f.K, f.hist);
+    const int l = lane_id();
+    const int32_t *bi = f.bi;
+    if (o.to_candidates) {
+        int32_t *ci = o.idx + (b * geo.G + m) * o.stride;
+        const int n = wave_emit(f.bs, f.cnt, s, [&](int slot, int j, float) { ci[slot] = bi[j]; });
+        for (int t = n + l; t < o.stride; t += kWave) ci[t] = -1;
+        if (o.count && l == 0) o.count[b * geo.G + m] = n;
+        return;
+    }
+    const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+    const int64_t stride = o.stride;
+    int32_t *idx = o.idx;
+    float *scr = o.sc;
+    const int n = wave_emit(f.bs, f.cnt, s, [&](int slot, int j, float v) {
+        const int32_t p = bi[j];
+        for (int64_t r = r0; r < r1; ++r) {
+            const int64_t off = (b * geo.Lq + r) * stride + slot;
+            idx[off] = p;
+            if (scr) scr[off] = v;
+        }
+    });
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int t = n + l; t < o.stride; t += kWave) {
+            const int64_t off = (b * geo.Lq + r) * stride + t;
+            idx[off] = -1;
+            if (scr) scr[off] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- pool
+// eq. (4): thread per (b, m, head, VEC-element chunk). fp32 sum over members
+// in order, one IEEE division by the member count, RNE to the q dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const float *__restrict__ w,
+                                              T *__restrict__ qbar, float *__restrict__ wbar, Geo geo, int H,
+                                              int D)
+{
+    constexpr int VEC = 16 / sizeof(T);
+    const int chunks = D / VEC;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = geo.B * geo.G * H * chunks;
+    if (tid >= total) return;
+    const int ch = static_cast<int>(tid % chunks);
+    const int64_t t2 = tid / chunks;
+    const int h = static_cast<int>(t2 % H);
+    const int64_t bm = t2 / H;
+    const int64_t b = bm / geo.G, m = bm % geo.G;
+    const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+    const float gm = static_cast<float>(r1 - r0);
+
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+        const T *src = q + ((b * geo.Lq + r) * H + h) * D + ch * VEC;
+        union {
+            uint4 v;
+            T e[VEC];
+        } u;
+        u.v = *reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + widen<T>(u.e[e]);
+    }
+    union {
+        uint4 v;
+        T e[VEC];
+    } o;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const float mean = acc[e] / gm;  // IEEE division (HIP default)
+        if constexpr (sizeof(T) == 2) {
+            o.e[e] = float_to_bf16_rne(mean);
+        } else {
+            o.e[e] = mean;
+        }
+    }
+    *reinterpret_cast<uint4 *>(qbar + (bm * H + h) * D + ch * VEC) = o.v;
+    if (ch == 0) {
+        float s = 0.0f;
+        for (int64_t r = r0; r < r1; ++r) s = s + w[(b * geo.Lq + r) * H + h];
+        wbar[bm * H + h] = s / gm;
+    }
+}
+
+// -------------------------------------------------------- MFMA scan (bf16)
+// One workgroup = 4 waves = 4 consecutive groups of one sequence. The WG
+// streams 64-key tiles of k through LDS (double-buffered, XOR-swizzled
+// 16-byte chunks) and every wave multiplies its proxy (H x D, held in
+// registers as MFMA A fragments) by the tile:
+//   v_mfma_f32_16x16x32_bf16: A = 16 heads x 32 dims, B = 32 dims x 16 keys.
+// Output lane l holds key (l % 16) and heads 4*(l/16) + v, v = 0..3, so the
+// ReLU and w-weighted sum over the lane's heads is in registers; a 3-step
+// exchange across the four 16-lane quarters leaves lane l with the full score
+// of key l of the tile.
+enum ScanMode { kFilter = 0, kRows = 1 };
+
+struct ScanArgs {
+    const void *qsrc;   // [B, G, H, D] proxies (the queries themselves when g == 1)
+    const float *wsrc;  // [B, G, H]
+    const void *k;      // [B, Lk, D]
+    Geo geo;
+    int H, D;
+    // kFilter
+    int K, cap;
+    float *buf_s;
+    int32_t *buf_i;
+    SelectionOut out;
+    // kRows
+    float *rows;  // [B, G, Lk]
+};
+
+constexpr int kTileKeys = 64;
+
+template <int H, int D, int Mode>
+__global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
+{
+    static_assert(H % 16 == 0 && D == 128, "tile swizzle assumes 16 chunks of 8 bf16 per key row");
+    constexpr int RB = H / 16;      // 16-head row blocks
+    constexpr int KB = D / 32;      // 32-dim contraction blocks
+    constexpr int CH = D / 8;       // 16-byte chunks per key row
+    constexpr int NT = kTileKeys;
+    constexpr int LOADS = NT * CH / 256;
+
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][NT * D];
+    __shared__ uint32_t hist[4][256];
+
+    const Geo &geo = a.geo;
+    const int wv = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int Q = l >> 4;
+    const int64_t nblk = (geo.G + 3) >> 2;
+    const int64_t b = blockIdx.x % geo.B;
+    const int64_t blk = nblk - 1 - blockIdx.x / geo.B;  // longest prefixes first
+    const int64_t m = blk * 4 + wv;
+    const bool active = m < geo.G;
+    const int64_t m_hi = (blk * 4 + 3 < geo.G - 1) ? blk * 4 + 3 : geo.G - 1;
+    const int64_t wg_tlast = geo.t_last(m_hi);
+    const int64_t my_tlast = active ? geo.t_last(m) : -1;
+    const int ntiles = static_cast<int>(wg_tlast / NT) + 1;
+    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    const int64_t gid = b * geo.G + (active ? m : blk * 4);
+
+    // A fragments (proxy) and the lane's head weights
+    bf16x8 afr[RB][KB];
+    float wr[RB][4];
+    {
+        const uint16_t *qg = static_cast<const uint16_t *>(a.qsrc) + gid * H * D;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(qg + (16 * rb + (l & 15)) * D + 32 * kb + 8 * Q);
+                afr[rb][kb] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) wr[rb][v] = a.wsrc[gid * H + 16 * rb + 4 * Q + v];
+        }
+    }
+
+    Filter f;
+    f.K = a.K;
+    f.cap = a.cap;
+    f.cnt = 0;
+    f.tau = -INFINITY;
+    f.hist = hist[wv];
+    if (Mode == kFilter) {
+        f.bs = a.buf_s + gid * a.cap;
+        f.bi = a.buf_i + gid * a.cap;
+    }
+    float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
+
+    uint4 stage[LOADS];
+    auto load_tile = [&](int64_t base) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = threadIdx.x + 256 * i;
+            const int r = id / CH, ch = id % CH;
+            const int64_t s = base + r;
+            stage[i] = (s < geo.Lk) ? *reinterpret_cast<const uint4 *>(kseq + s * D + ch * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int id = threadIdx.x + 256 * i;
+            const int r = id / CH, ch = id % CH;
+            *reinterpret_cast<uint4 *>(&tile[buf][r * D + ((ch ^ (r & 15)) * 8)]) = stage[i];
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
+        const int64_t base = static_cast<int64_t>(it) * NT;
+        if (it + 1 < ntiles) load_tile(base + NT);
+
+        float p[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            f32x4 acc[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int krow = 16 * cb + (l & 15);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(&tile[cur][krow * D + (((4 * kb + Q) ^ (l & 15)) * 8)]);
+                const bf16x8 bfr = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr, acc[rb], 0, 0, 0);
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s = fmaf(wr[rb][v], fmaxf(acc[rb][v], 0.0f), s);
+            }
+            p[cb] = s;
+        }
+        // quarters Q and Q^2 exchange column blocks, then Q and Q^1
+        const bool lo = Q < 2;
+        const float x0 = (lo ? p[0] : p[2]) + __shfl_xor(lo ? p[2] : p[0], 32);
+        const float x1 = (lo ? p[1] : p[3]) + __shfl_xor(lo ? p[3] : p[1], 32);
+        const bool odd = Q & 1;
+        float score = (odd ? x1 : x0) + __shfl_xor(odd ? x0 : x1, 16);
+        score = score + 0.0f;  // one zero: +0
+
+        const int64_t s = base + l;
+        const bool valid = s <= my_tlast;
+        if (Mode == kFilter) {
+            if (active) f.push(valid, score, static_cast<int32_t>(s));
+        } else {
+            if (active && s < geo.Lk) row[s] = valid ? score : -INFINITY;
+        }
+
+        if (it + 1 < ntiles) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    if (!active) return;
+    if (Mode == kFilter) {
+        finish_group(geo, a.out, b, m, f);
+    } else {
+        for (int64_t s = static_cast<int64_t>(ntiles) * NT + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
+    }
+}
+
+// ------------------------------------------------- exact-order scan (any)
+// One wave per group; lane l scores key base + l with the definition's exact
+// fp32 order: for each head, dot = sum_i q_i k_i (one rounding per product
+// and per sum, dims ascending); term = w * max(dot, 0); acc += term.
+template <typename T>
+__device__ __forceinline__ float exact_score(const T *__restrict__ qv, const float *__restrict__ wv,
+                                             const T *__restrict__ key, int H, int D)
+{
+#pragma clang fp contract(off)  // one rounding per product and per sum: no fused multiply-add
+    float acc = 0.0f;
+    for (int j = 0; j < H; ++j) {
+        float dot = 0.0f;
+        for (int i = 0; i < D; ++i) {
+            const float prod = widen<T>(qv[j * D + i]) * widen<T>(key[i]);
+            dot = dot + prod;
+        }
+        const float relu = dot > 0.0f ? dot : 0.0f;
+        const float term = wv[j] * relu;
+        acc = acc + term;
+    }
+    if (acc == 0.0f) acc = 0.0f;
+    return acc;
+}
+
+template <typename T, int Mode>
+__global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
+{
+    __shared__ uint32_t hist[4][256];
+    const Geo &geo = a.geo;
+    const int wv = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int64_t nblk = (geo.G + 3) >> 2;
+    const int64_t b = blockIdx.x % geo.B;
+    const int64_t blk = nblk - 1 - blockIdx.x / geo.B;
+    const int64_t m = blk * 4 + wv;
+    if (m >= geo.G) return;  // no workgroup barriers below
+    const int64_t tl = geo.t_last(m);
+    const int64_t gid = b * geo.G + m;
+    const T *qv = static_cast<const T *>(a.qsrc) + gid * a.H * a.D;
+    const float *wv_ = a.wsrc + gid * a.H;
+    const T *kseq = static_cast<const T *>(a.k) + b * geo.Lk * a.D;
+
+    Filter f;
+    f.K = a.K;
+    f.cap = a.cap;
+    f.cnt = 0;
+    f.tau = -INFINITY;
+    f.hist = hist[wv];
+    if (Mode == kFilter) {
+        f.bs = a.buf_s + gid * a.cap;
+        f.bi = a.buf_i + gid * a.cap;
+    }
+    float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
+
+    for (int64_t base = 0; base <= tl; base += kWave) {
+        const int64_t s = base + l;
+        const bool valid = s <= tl;
+        const float score = valid ? exact_score<T>(qv, wv_, kseq + s * a.D, a.H, a.D) : 0.0f;
+        if (Mode == kFilter) {
+            f.push(valid, score, static_cast<int32_t>(s));
+        } else if (valid) {
+            row[s] = score;
+        }
+    }
+    if (Mode == kFilter) {
+        finish_group(geo, a.out, b, m, f);
+    } else {
+        for (int64_t s = tl + 1 + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
+    }
+}
+
+// --------------------------------------------------------------- refine
+struct RefineArgs {
+    const void *q;   // [B, Lq, H, D]
+    const float *w;  // [B, Lq, H]
+    const void *k;   // [B, Lk, D]
+    Geo geo;
+    int H, D;
+    int topk, c;
+    const int32_t *cand;    // [B*G, c], ascending, -1 pad
+    const int32_t *cand_n;  // [B*G]
+    float *scratch;         // [B*G, g, c]
+    int32_t *out_idx;       // [B, Lq, topk]
+    float *out_sc;          // nullable
+};
+
+// Member selection from its scratch row; candidates s <= t are exactly the
+// first nvalid entries of C (C is ascending).
+__device__ void finish_member(const RefineArgs &a, int64_t b, int64_t r, const int32_t *C, const float *srow,
+                              int nvalid, uint32_t *hist)
+{
+    wave_fence();
+    const Sel s = wave_select(srow, nvalid, a.topk, hist);
+    const int l = lane_id();
+    int32_t *oi = a.out_idx + (b * a.geo.Lq + r) * a.topk;
+    float *os = a.out_sc ? a.out_sc + (b * a.geo.Lq + r) * a.topk : nullptr;
+    const int n = wave_emit(srow, nvalid, s, [&](int slot, int j, float v) {
+        oi[slot] = C[j];
+        if (os) os[slot] = v;
+    });
+    for (int t = n + l; t < a.topk; t += kWave) {
+        oi[t] = -1;
+        if (os) os[t] = -INFINITY;
+    }
+}
+
+// One workgroup (4..8 waves) per group; wave w re-scores member
+// (round * nwaves + w).
+// The candidate keys of each 64-candidate tile are gathered once into LDS and
+// shared by every member wave.
+template <int H, int D>
+__global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
+{
+    static_assert(H % 16 == 0 && D == 128, "tile swizzle assumes 16 chunks of 8 bf16 per key row");
+    constexpr int RB = H / 16, KB = D / 32, CH = D / 8, NT = kTileKeys;
+    constexpr int MAXLOADS = NT * CH / 256;  // blockDim >= 256
+
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][NT * D];
+    __shared__ uint32_t hist[8][256];
+
+    const Geo &geo = a.geo;
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
+    const int wv = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int Q = l >> 4;
+    const int64_t gid = blockIdx.x;
+    const int64_t b = gid / geo.G, m = gid % geo.G;
+    const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+    const int gm = static_cast<int>(r1 - r0);
+    const int nc = a.cand_n[gid];
+    const int32_t *C = a.cand + gid * a.c;
+    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    const int ntiles = (nc + NT - 1) / NT;
+    const int loads = (NT * CH + nthreads - 1) / nthreads;
+
+    uint4 stage[MAXLOADS];
+    auto load_tile = [&](int jb) {
+#pragma unroll
+        for (int i = 0; i < MAXLOADS; ++i) {
+            const int id = threadIdx.x + nthreads * i;
+            if (i < loads && id < NT * CH) {
+                const int r = id / CH, ch = id % CH;
+                const int j = jb + r;
+                const int32_t s = (j < nc) ? C[j] : -1;
+                stage[i] = (s >= 0) ? *reinterpret_cast<const uint4 *>(kseq + static_cast<int64_t>(s) * D + ch * 8)
+                                    : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < MAXLOADS; ++i) {
+            const int id = threadIdx.x + nthreads * i;
+            if (i < loads && id < NT * CH) {
+                const int r = id / CH, ch = id % CH;
+                *reinterpret_cast<uint4 *>(&tile[buf][r * D + ((ch ^ (r & 15)) * 8)]) = stage[i];
+            }
+        }
+    };
+
+    for (int round = 0; round * nwaves < gm; ++round) {
+        const int mi = round * nwaves + wv;
+        const bool active = mi < gm;
+        const int64_t r = r0 + (active ? mi : 0);
+        const int64_t t = geo.Lk - geo.Lq + r;
+        float *srow = a.scratch + (gid * geo.g + (active ? mi : 0)) * a.c;
+
+        bf16x8 afr[RB][KB];
+        float wr[RB][4];
+        {
+            const uint16_t *qr = static_cast<const uint16_t *>(a.q) + (b * geo.Lq + r) * H * D;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(qr + (16 * rb + (l & 15)) * D + 32 * kb + 8 * Q);
+                    afr[rb][kb] = __builtin_bit_cast(bf16x8, v);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) wr[rb][v] = a.w[(b * geo.Lq + r) * H + 16 * rb + 4 * Q + v];
+            }
+        }
+
+        int nvalid = 0;
+        if (ntiles > 0) {
+            load_tile(0);
+            store_tile(0);
+        }
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int cur = it & 1;
+            const int jb = it * NT;
+            if (it + 1 < ntiles) load_tile(jb + NT);
+
+            float p[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                f32x4 acc[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                const int krow = 16 * cb + (l & 15);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const uint4 v =
+                        *reinterpret_cast<const uint4 *>(&tile[cur][krow * D + (((4 * kb + Q) ^ (l & 15)) * 8)]);
+                    const bf16x8 bfr = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr, acc[rb], 0, 0, 0);
+                }
+                float s = 0.0f;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s = fmaf(wr[rb][v], fmaxf(acc[rb][v], 0.0f), s);
+                }
+                p[cb] = s;
+            }
+            const bool lo = Q < 2;
+            const float x0 = (lo ? p[0] : p[2]) + __shfl_xor(lo ? p[2] : p[0], 32);
+            const float x1 = (lo ? p[1] : p[3]) + __shfl_xor(lo ? p[3] : p[1], 32);
+            const bool odd = Q & 1;
+            float score = (odd ? x1 : x0) + __shfl_xor(odd ? x0 : x1, 16);
+            score = score + 0.0f;
+
+            const int j = jb + l;
+            if (active) {
+                const bool in = j < nc;
+                const int32_t pos = in ? C[j] : 0;
+                nvalid += popc(ballot(in && pos <= t));
+                if (in) srow[j] = score;
+            }
+            if (it + 1 < ntiles) store_tile(cur ^ 1);
+            __syncthreads();
+        }
+        if (active) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+    }
+}
+
+// Exact-order refine: one workgroup of 4 waves per group; lane l scores
+// candidate tile*64 + l for the wave's member.
+template <typename T>
+__global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
+{
+    __shared__ uint32_t hist[4][256];
+    const Geo &geo = a.geo;
+    const int wv = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int64_t gid = blockIdx.x;
+    const int64_t b = gid / geo.G, m = gid % geo.G;
+    const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+    const int gm = static_cast<int>(r1 - r0);
+    const int nc = a.cand_n[gid];
+    const int32_t *C = a.cand + gid * a.c;
+    const T *kseq = static_cast<const T *>(a.k) + b * geo.Lk * a.D;
+    for (int mi = wv; mi < gm; mi += 4) {
+        const int64_t r = r0 + mi;
+        const int64_t t = geo.Lk - geo.Lq + r;
+        const T *qv = static_cast<const T *>(a.q) + (b * geo.Lq + r) * a.H * a.D;
+        const float *wv_ = a.w + (b * geo.Lq + r) * a.H;
+        float *srow = a.scratch + (gid * geo.g + mi) * a.c;
+        int nvalid = 0;
+        for (int jb = 0; jb < nc; jb += kWave) {
+            const int j = jb + l;
+            const bool in = j < nc;
+            const int32_t pos = in ? C[j] : 0;
+            if (in) srow[j] = exact_score<T>(qv, wv_, kseq + static_cast<int64_t>(pos) * a.D, a.H, a.D);
+            nvalid += popc(ballot(in && pos <= t));
+        }
+        finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+    }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- launchers
+hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
+                       float *wbar, hipStream_t st)
+{
+    Geo geo{sh.B, G, sh.Lq, sh.Lk, g};
+    const int vec = sh.bf16 ? 8 : 4;
+    const int64_t total = sh.B * G * sh.H * (sh.D / vec);
+    const int64_t blocks = (total + 255) / 256;
+    if (sh.bf16) {
+        hipLaunchKernelGGL(k_pool<uint16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(q), w, static_cast<uint16_t *>(qbar), wbar, geo, sh.H, sh.D);
+    } else {
+        hipLaunchKernelGGL(k_pool<float>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                           static_cast<const float *>(q), w, static_cast<float *>(qbar), wbar, geo, sh.H, sh.D);
+    }
+    return hipGetLastError();
+}
+
+bool mfma_shape(const LaunchShape &sh) { return sh.bf16 && sh.H == 64 && sh.D == 128; }
+
+hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st)
+{
+    ScanArgs a{};
+    a.qsrc = L.qsrc;
+    a.wsrc = L.wsrc;
+    a.k = L.k;
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.H = sh.H;
+    a.D = sh.D;
+    a.K = L.K;
+    a.cap = L.cap;
+    a.buf_s = L.buf_s;
+    a.buf_i = L.buf_i;
+    a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
+    a.rows = L.rows;
+    const int64_t blocks = sh.B * ((L.G + 3) / 4);
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+    const bool rows = L.rows != nullptr;
+    if (mfma_shape(sh)) {
+        if (rows)
+            hipLaunchKernelGGL((k_scan_mfma<64, 128, kRows>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_scan_mfma<64, 128, kFilter>), grid, block, 0, st, a);
+    } else if (sh.bf16) {
+        if (rows)
+            hipLaunchKernelGGL((k_scan_exact<uint16_t, kRows>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_scan_exact<uint16_t, kFilter>), grid, block, 0, st, a);
+    } else {
+        if (rows)
+            hipLaunchKernelGGL((k_scan_exact<float, kRows>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_scan_exact<float, kFilter>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st)
+{
+    RefineArgs a{};
+    a.q = L.q;
+    a.w = L.w;
+    a.k = L.k;
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.H = sh.H;
+    a.D = sh.D;
+    a.topk = L.topk;
+    a.c = L.c;
+    a.cand = L.cand;
+    a.cand_n = L.cand_n;
+    a.scratch = L.scratch;
+    a.out_idx = L.out_idx;
+    a.out_sc = L.out_sc;
+    const dim3 grid(static_cast<uint32_t>(sh.B * L.G));
+    if (mfma_shape(sh)) {
+        int nw = L.g < 8 ? L.g : 8;  // 4..8 member waves; more members loop
+        if (nw < 4) nw = 4;
+        hipLaunchKernelGGL((k_refine_mfma<64, 128>), grid, dim3(64 * nw), 0, st, a);
+    } else if (sh.bf16) {
+        hipLaunchKernelGGL(k_refine_exact<uint16_t>, grid, dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(k_refine_exact<float>, grid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pivot

@@ -17,3 +17,13 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+@pytest.fixture(scope="session")
+def pivot_lib():
+    """libpivot.so, built in-tree first if nothing is built yet."""
+    import sparse_attention_indexer_proxy_amd as pv
+    if not os.path.exists(pv.library_path()):
+        from sparse_attention_indexer_proxy_amd import build
+        build.build()
+    return pv.load_library()

@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before anything reaches HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_proxy_amd as pv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pivot.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pivot_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("pivot_index_dense", "pivot_index_reuse", "pivot_index_refine", "pivot_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(pivot_lib):
+    missing = [n for n in _declared() if not hasattr(pivot_lib, n)]
+    assert not missing, f"not exported: {missing}"
+    assert set(_declared()) == set(pv.EXPORTED)
+
+
+def test_abi_version_matches_header(pivot_lib):
+    m = re.search(r"#define PIVOT_ABI_VERSION (\d+)", open(HEADER).read())
+    assert pivot_lib.pivot_abi_version() == int(m.group(1))
+
+
+def _prob(B=1, Lq=64, Lk=64, H=64, D=128, dt=1):
+    return pv.Problem(B, Lq, Lk, H, D, dt)
+
+
+def _ws(pivot_lib, prob, variant, g, topk, c):
+    out = ctypes.c_size_t(0)
+    st = pivot_lib.pivot_workspace_size(ctypes.byref(prob), variant, g, topk, c, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,variant,g,topk,c,expect", [
+    (dict(Lq=65, Lk=64), pv.REUSE, 8, 16, 0, 1),      # lq > lk
+    (dict(B=0), pv.DENSE, 1, 16, 0, 1),               # empty batch
+    (dict(), pv.REUSE, 0, 16, 0, 1),                  # g < 1
+    (dict(), pv.DENSE, 1, 0, 0, 1),                   # topk < 1
+    (dict(), pv.REFINE, 8, 16, 8, 1),                 # c < topk
+    (dict(dt=7), pv.DENSE, 1, 16, 0, 1),              # unknown dtype
+    (dict(D=12), pv.DENSE, 1, 16, 0, 2),              # bf16 dim not a multiple of 8
+    (dict(H=0), pv.DENSE, 1, 16, 0, 1),
+    (dict(Lk=2 ** 31, Lq=4), pv.DENSE, 1, 16, 0, 1),  # positions must fit int32
+    (dict(), 9, 1, 16, 0, 1),                         # unknown variant
+])
+def test_workspace_size_rejects_bad_arguments(pivot_lib, kw, variant, g, topk, c, expect):
+    st, _ = _ws(pivot_lib, _prob(**kw), variant, g, topk, c)
+    assert st == expect
+    assert pivot_lib.pivot_last_error().decode()
+
+
+def test_workspace_size_grows_with_the_problem(pivot_lib):
+    sizes = [_ws(pivot_lib, _prob(Lq=L, Lk=L), pv.REFINE, 8, 64, 128)[1] for L in (64, 512, 4096)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    st, dense = _ws(pivot_lib, _prob(Lq=512, Lk=512), pv.DENSE, 1, 64, 0)
+    assert st == 0 and dense > 0
+
+
+def test_index_calls_validate_before_launch(pivot_lib):
+    prob = _prob()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    idx = ctypes.c_void_p(1 << 21)
+    # null q
+    assert pivot_lib.pivot_index_dense(ctypes.byref(prob), None, fake, fake, 16, idx, None, fake, 1 << 30,
+                                       None) == 1
+    # workspace too small
+    assert pivot_lib.pivot_index_reuse(ctypes.byref(prob), fake, fake, fake, 8, 16, idx, None, fake, 16,
+                                       None) == 3
+    assert "workspace" in pivot_lib.pivot_last_error().decode()
+    # c < topk
+    assert pivot_lib.pivot_index_refine(ctypes.byref(prob), fake, fake, fake, 8, 16, 4, idx, None, None, None,
+                                        fake, 1 << 30, None) == 1
+    # null problem
+    assert pivot_lib.pivot_index_dense(None, fake, fake, fake, 16, idx, None, fake, 1 << 30, None) == 1
+    assert pivot_lib.pivot_pool(ctypes.byref(prob), 0, fake, fake, fake, fake, None) == 1
+    assert pivot_lib.pivot_proxy_scores(ctypes.byref(prob), 8, None, fake, fake, fake, None) == 1
+
+
+def test_status_strings(pivot_lib):
+    for s in range(5):
+        assert pivot_lib.pivot_status_str(s).decode()
+    assert pivot_lib.pivot_status_str(99).decode() == "unknown status"
+
+
+def test_python_binding_raises_on_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 8, 2, 8)
+    w = torch.zeros(1, 8, 2)
+    k = torch.zeros(1, 8, 8)
+    with pytest.raises(ValueError):
+        pv.index_dense(q, w, k, 4)          # host tensors are refused
+    with pytest.raises(ValueError):
+        pv.index_dense(q, w[:, :4], k, 4)   # shape mismatch
