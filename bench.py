@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the PIVOT indexer on one MI355X.
+
+One step = one full indexer call over the workload (Refine: pool -> fused
+proxy scan with top-c selection -> per-member re-score and top-k), inputs
+resident in HBM. Prints one JSON line:
+
+  value        query positions per second (B * Lq / step time)
+  roofline     the fused proxy-scan kernel against the bf16 MFMA peak:
+               algorithmic FLOPs per launch (2 d H sum_groups (t_last + 1))
+               over its average launch time from hipEvents on its stream
+  cpu_baseline the CPU oracle on a stratified sample of the same groups
+
+    python bench.py [--steps K] [--warmup W] [--variant refine|reuse|dense] [--g G]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import ALL, LONG_128K  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+METRIC = "indexer query-positions/sec (Refine g=8, L=128K) + % of bf16 MFMA peak"
+SCAN_SRC = os.path.join(ROOT, "sparse_attention_indexer_proxy_amd", "csrc", "pivot_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def group_last_positions(Lq, Lk, g):
+    G = -(-Lq // g)
+    return Lk - Lq + np.minimum((np.arange(G) + 1) * g, Lq) - 1
+
+
+def scan_flops(W, g):
+    tl = group_last_positions(W.Lq, W.Lk, g)
+    return 2.0 * W.d * W.H * W.B * float((tl + 1).sum())
+
+
+def refine_flops(W, g, c):
+    tl = group_last_positions(W.Lq, W.Lk, g)
+    G = len(tl)
+    gm = np.minimum((np.arange(G) + 1) * g, W.Lq) - np.arange(G) * g
+    return 2.0 * W.d * W.H * W.B * float((gm * np.minimum(c, tl + 1)).sum())
+
+
+def kernel_source_hash():
+    with open(SCAN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload_name, variant, g):
+    """HBM bytes per scan launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{workload_name}/{variant}/g{g}"
+    ent = rec.get(key)
+    if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, w, k, W, variant, g, budget_s):
+    """The oracle on a stratified sample of groups (rows for dense), sized to
+    about budget_s seconds; returns the metric-unit rate."""
+    import oracle
+    threads = oracle.num_threads()
+    per_seq = W.Lq if variant == "dense" else -(-W.Lq // g)
+    rows_per_unit = 1 if variant == "dense" else g
+    run = {"dense": lambda u: oracle.dense(q, w, k, W.topk, rows=u, want_scores=False),
+           "reuse": lambda u: oracle.reuse(q, w, k, g, W.topk, groups=u, want_scores=False),
+           "refine": lambda u: oracle.refine(q, w, k, g, W.topk, W.c, groups=u, want_scores=False,
+                                             want_cand=False)}[variant]
+    # probe: one thread-batch of mid-sequence units gives the time per unit
+    probe = np.linspace(per_seq // 2, per_seq // 2 + threads - 1, threads).astype(np.int64) % per_seq
+    t0 = time.perf_counter()
+    run(probe)
+    per_unit = max((time.perf_counter() - t0) / len(probe), 1e-6)
+    n = int(max(threads, min(per_seq * W.B, budget_s / per_unit)))
+    n = max(threads, n // threads * threads)
+    units = np.unique(np.linspace(0, per_seq * W.B - 1, n).astype(np.int64))
+    t0 = time.perf_counter()
+    run(units)
+    dt = time.perf_counter() - t0
+    return {"value": len(units) * rows_per_unit / dt, "unit": "query positions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{len(units)} of {per_seq * W.B} {'rows' if variant == 'dense' else 'groups'} "
+                       f"evenly spaced over the sequence (same mean prefix as the full workload), "
+                       f"{dt:.1f} s on {threads} threads")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=LONG_128K.name, choices=sorted(ALL))
+    ap.add_argument("--variant", default="refine", choices=["refine", "reuse", "dense"])
+    ap.add_argument("--g", type=int, default=None, help="group size (default: the workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the indexer's groups "
+              "would be split across GPUs; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_indexer_proxy_amd as pv
+
+    W = ALL[args.workload]
+    g = 1 if args.variant == "dense" else (args.g or W.g)
+    t0 = time.perf_counter()
+    from workloads import generate, to_device
+    q, w, k = generate(W)
+    log(f"[bench] generated {W.name} in {time.perf_counter() - t0:.1f} s")
+    tq, tw, tk = to_device(q, w, k)
+    dev = tq.device
+    variant_id = {"dense": pv.DENSE, "reuse": pv.REUSE, "refine": pv.REFINE}[args.variant]
+    ws = torch.empty(pv.workspace_size(variant_id, W.B, W.Lq, W.Lk, W.H, W.d, tq.dtype, g, W.topk, W.c),
+                     dtype=torch.uint8, device=dev)
+    log(f"[bench] workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def step():
+        if args.variant == "refine":
+            return pv.index_refine(tq, tw, tk, g, W.topk, W.c, workspace=ws)
+        if args.variant == "reuse":
+            return pv.index_reuse(tq, tw, tk, g, W.topk, workspace=ws)
+        return pv.index_dense(tq, tw, tk, W.topk, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    pv.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = pv.timing_read()
+    pv.timing_enable(False)
+    del out
+
+    ms_per_step = 1e3 * wall / args.steps
+    qpos = W.B * W.Lq
+    value = qpos / (wall / args.steps)
+    scan_ms, scan_n = stages["scan"]
+    scan_avg_s = scan_ms / max(scan_n, 1) / 1e3
+    sflops = scan_flops(W, g)
+    achieved = sflops / scan_avg_s / 1e12
+    total_flops = sflops + (refine_flops(W, g, W.c) if args.variant == "refine" else 0.0)
+    kernels = {name: round(ms / max(n, 1), 4) for name, (ms, n) in stages.items() if n}
+    log(f"[bench] {args.variant} g={g}: {ms_per_step:.3f} ms/step, kernels (ms/launch) {kernels}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, w, k, W, args.variant, g, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if W.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{W.name} PIVOT-{args.variant}", "batch": W.B, "seq_len": W.Lk,
+                   "query_rows": W.Lq, "heads": W.H, "dim": W.d, "g": g, "topk": W.topk,
+                   "c": W.c if args.variant == "refine" else None, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(W.name, args.variant, g),
+                     "kernel": "proxy scan + top-K selection (k_scan_mfma)",
+                     "flops_per_launch": sflops},
+        "cpu_baseline": cpu,
+        "kernels_ms_per_launch": kernels,
+        "whole_call_mfma_frac": total_flops / (wall / args.steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,6 +117,17 @@ pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const 
 pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *qbar, const float *wbar,
                                 const void *k, float *out, void *stream);
 
+/* Optional per-kernel timing (instrumentation for benchmarks). While enabled
+ * on the calling thread, every kernel a pivot_* call enqueues is bracketed by
+ * a pair of hipEvents on the same stream. pivot_timing_read waits for the
+ * recorded events, adds the elapsed milliseconds of each stage into ms[s] and
+ * the number of launches into launches[s] (arrays of PIVOT_STAGES entries;
+ * either may be NULL), then forgets the records. Disabling also forgets them. */
+#define PIVOT_STAGES 4
+typedef enum { PIVOT_STAGE_POOL = 0, PIVOT_STAGE_SCAN = 1, PIVOT_STAGE_SELECT = 2, PIVOT_STAGE_REFINE = 3 } pivot_stage;
+pivot_status pivot_timing_enable(int32_t on);
+pivot_status pivot_timing_read(double *ms, int64_t *launches);
+
 const char *pivot_status_str(pivot_status s);
 const char *pivot_last_error(void);
 int32_t pivot_abi_version(void);

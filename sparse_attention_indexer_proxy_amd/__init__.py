@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "pool", "proxy_scores",
-           "workspace_size", "library_path", "load_library", "DENSE", "REUSE", "REFINE"]
+           "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
+           "DENSE", "REUSE", "REFINE", "STAGES"]
 
 DENSE, REUSE, REFINE = 0, 1, 2
 _F32, _BF16 = 0, 1
@@ -29,8 +30,9 @@ _LIB_PATH = os.path.join(_PKG, "libpivot.so")
 _lib = None
 
 EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
-            "pivot_pool", "pivot_proxy_scores", "pivot_status_str", "pivot_last_error",
-            "pivot_abi_version")
+            "pivot_pool", "pivot_proxy_scores", "pivot_timing_enable", "pivot_timing_read",
+            "pivot_status_str", "pivot_last_error", "pivot_abi_version")
+STAGES = ("pool", "scan", "select", "refine")
 
 
 class PivotError(RuntimeError):
@@ -68,6 +70,10 @@ def load_library(path: str | None = None):
     for name in ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
                  "pivot_pool", "pivot_proxy_scores"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.pivot_timing_enable.argtypes = [i32]
+    lib.pivot_timing_enable.restype = ctypes.c_int
+    lib.pivot_timing_read.argtypes = [vp, vp]
+    lib.pivot_timing_read.restype = ctypes.c_int
     lib.pivot_status_str.argtypes = [ctypes.c_int]
     lib.pivot_status_str.restype = ctypes.c_char_p
     lib.pivot_last_error.restype = ctypes.c_char_p
@@ -224,3 +230,18 @@ def proxy_scores(qbar, wbar, k, g: int, lq: int, stream=None):
     _check(load_library().pivot_proxy_scores(ctypes.byref(prob), g, _ptr(qbar), _ptr(wbar), _ptr(k), _ptr(out),
                                              _stream_ptr(stream, qbar.device)))
     return out
+
+
+def timing_enable(on: bool = True):
+    """Bracket every kernel launched by this thread's calls with hipEvents."""
+    _check(load_library().pivot_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """Wait for the recorded events; return {stage: (total_ms, launches)} and
+    forget the records."""
+    import numpy as np
+    ms = np.zeros(len(STAGES), dtype=np.float64)
+    n = np.zeros(len(STAGES), dtype=np.int64)
+    _check(load_library().pivot_timing_read(ms.ctypes.data_as(ctypes.c_void_p), n.ctypes.data_as(ctypes.c_void_p)))
+    return {name: (float(ms[i]), int(n[i])) for i, name in enumerate(STAGES)}

@@ -12,9 +12,56 @@
 #include "pivot.h"
 #include "pivot_kernels.h"
 
+#include <vector>
+
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// ---------------------------------------------------------------- timing
+struct TimedLaunch {
+    int stage;
+    hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_timed;
+
+void forget_timing()
+{
+    for (auto &t : g_timed) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    g_timed.clear();
+}
+
+// Brackets one kernel launch with events when timing is enabled.
+struct StageTimer {
+    TimedLaunch rec{};
+    bool armed = false;
+    hipStream_t stream;
+    StageTimer(int stage, hipStream_t s) : stream(s)
+    {
+        if (!g_timing) return;
+        rec.stage = stage;
+        if (hipEventCreate(&rec.start) != hipSuccess) return;
+        if (hipEventCreate(&rec.stop) != hipSuccess) {
+            (void)hipEventDestroy(rec.start);
+            return;
+        }
+        armed = hipEventRecord(rec.start, stream) == hipSuccess;
+    }
+    ~StageTimer()
+    {
+        if (!armed) return;
+        if (hipEventRecord(rec.stop, stream) == hipSuccess) {
+            g_timed.push_back(rec);
+        } else {
+            (void)hipEventDestroy(rec.start);
+            (void)hipEventDestroy(rec.stop);
+        }
+    }
+};
 
 pivot_status fail(pivot_status s, const char *fmt, ...)
 {
@@ -134,7 +181,10 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     if (L.pool) {
         void *qbar = base + L.qbar;
         float *wbar = reinterpret_cast<float *>(base + L.wbar);
-        st = hip_status(pivot::launch_pool(sh, L.g, L.G, q, w, qbar, wbar, s), "pool launch");
+        {
+            StageTimer tm(PIVOT_STAGE_POOL, s);
+            st = hip_status(pivot::launch_pool(sh, L.g, L.G, q, w, qbar, wbar, s), "pool launch");
+        }
         if (st != PIVOT_OK) return st;
         qsrc = qbar;
         wsrc = wbar;
@@ -167,7 +217,10 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
         sl.to_candidates = 0;
     }
     sl.rows = nullptr;
-    st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
+    {
+        StageTimer tm(PIVOT_STAGE_SCAN, s);
+        st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
+    }
     if (st != PIVOT_OK || variant != PIVOT_REFINE) return st;
 
     pivot::RefineLaunch rl{};
@@ -183,6 +236,7 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     rl.scratch = reinterpret_cast<float *>(base + L.scratch);
     rl.out_idx = indices;
     rl.out_sc = scores;
+    StageTimer tm(PIVOT_STAGE_REFINE, s);
     return hip_status(pivot::launch_refine(sh, rl, s), "refine launch");
 }
 
@@ -255,6 +309,31 @@ pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *q
     sl.g = g;
     sl.rows = out;
     return hip_status(pivot::launch_scan(shape_of(p), sl, static_cast<hipStream_t>(stream)), "scan launch");
+}
+
+pivot_status pivot_timing_enable(int32_t on)
+{
+    g_timing = on != 0;
+    if (!g_timing) forget_timing();
+    return PIVOT_OK;
+}
+
+pivot_status pivot_timing_read(double *ms, int64_t *launches)
+{
+    pivot_status st = PIVOT_OK;
+    for (auto &t : g_timed) {
+        float e = 0.0f;
+        hipError_t err = hipEventSynchronize(t.stop);
+        if (err == hipSuccess) err = hipEventElapsedTime(&e, t.start, t.stop);
+        if (err != hipSuccess) {
+            st = hip_status(err, "timing event");
+            continue;
+        }
+        if (ms) ms[t.stage] += e;
+        if (launches) launches[t.stage] += 1;
+    }
+    forget_timing();
+    return st;
 }
 
 const char *pivot_status_str(pivot_status s)

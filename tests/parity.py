@@ -12,20 +12,10 @@ from __future__ import annotations
 
 import numpy as np
 
+from workloads import to_device  # noqa: F401  (re-exported for the tests)
+
 RTOL = 1e-3
 ATOL_FRAC = 1e-6
-
-
-def to_device(q, w, k, device="cuda"):
-    import torch
-    if q.dtype == np.uint16:
-        tq = torch.from_numpy(q.view(np.int16)).to(device).view(torch.bfloat16)
-        tk = torch.from_numpy(k.view(np.int16)).to(device).view(torch.bfloat16)
-    else:
-        tq = torch.from_numpy(q).to(device)
-        tk = torch.from_numpy(k).to(device)
-    tw = torch.from_numpy(np.ascontiguousarray(w)).to(device)
-    return tq, tw, tk
 
 
 def bf16_tensor_bits(t) -> np.ndarray:

@@ -247,3 +247,16 @@ def gauss_random(rng_seed: int, B: int, Lq: int, Lk: int, H: int, d: int, dtype:
     k = r.standard_normal((B, Lk, d))
     ww = r.random((B, Lq, H))
     return to_storage(q, dtype), f64_to_f32(ww), to_storage(k, dtype)
+
+
+def to_device(q, w, k, device="cuda"):
+    """Copy generated arrays to torch device tensors (bf16 bits -> bfloat16)."""
+    import torch
+    if q.dtype == np.uint16:
+        tq = torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to(device).view(torch.bfloat16)
+        tk = torch.from_numpy(np.ascontiguousarray(k).view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        tq = torch.from_numpy(np.ascontiguousarray(q)).to(device)
+        tk = torch.from_numpy(np.ascontiguousarray(k)).to(device)
+    tw = torch.from_numpy(np.ascontiguousarray(w)).to(device)
+    return tq, tw, tk
