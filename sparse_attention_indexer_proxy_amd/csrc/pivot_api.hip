@@ -102,7 +102,7 @@ struct Layout {
     int64_t G;
     int g, K, cap;
     bool pool;
-    size_t qbar, wbar, buf_s, buf_i, cand, cand_n, scratch, total;
+    size_t qbar, wbar, buf, cand, cand_n, scratch, total;
 };
 
 pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, int32_t c, Layout *L)
@@ -139,8 +139,7 @@ pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, 
     };
     l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
-    l.buf_s = take(groups * cap * sizeof(float));
-    l.buf_i = take(groups * cap * sizeof(int32_t));
+    l.buf = take(groups * 2 * cap * sizeof(float));
     if (variant == PIVOT_REFINE) {
         l.cand = take(groups * static_cast<size_t>(c) * sizeof(int32_t));
         l.cand_n = take(groups * sizeof(int32_t));
@@ -201,8 +200,7 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     sl.g = L.g;
     sl.K = L.K;
     sl.cap = L.cap;
-    sl.buf_s = reinterpret_cast<float *>(base + L.buf_s);
-    sl.buf_i = reinterpret_cast<int32_t *>(base + L.buf_i);
+    sl.buf = reinterpret_cast<float *>(base + L.buf);
     if (variant == PIVOT_REFINE) {
         sl.out_idx = cand;
         sl.out_sc = nullptr;

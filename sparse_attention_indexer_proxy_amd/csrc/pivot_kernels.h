@@ -22,8 +22,7 @@ struct ScanLaunch {
     int64_t G;
     int g;
     int K, cap;         // selection size and per-group buffer capacity
-    float *buf_s;       // [B*G, cap]
-    int32_t *buf_i;     // [B*G, cap]
+    float *buf;         // [B*G, 2*cap]: cap scores then cap int32 positions per group
     int32_t *out_idx;   // rows [B, Lq, stride] or candidates [B, G, stride]
     float *out_sc;      // rows only, nullable
     int32_t *out_count; // candidates only, nullable

@@ -105,8 +105,41 @@ struct Sel {
     bool all;
 };
 
+constexpr int kVec = 4;                // entries per lane per step
+constexpr int kStep = kWave * kVec;    // 256 entries per step; lane l owns j0 + 4l .. j0 + 4l + 3
+
+// Exclusive prefix over lanes of a per-lane count c in [0, 7]; *total = sum.
+__device__ __forceinline__ int lane_prefix(int c, int *total)
+{
+    const uint64_t b0 = ballot(c & 1), b1 = ballot(c & 2), b2 = ballot(c & 4);
+    *total = popc(b0) + 2 * popc(b1) + 4 * popc(b2);
+    return mbcnt(b0) + 2 * mbcnt(b1) + 4 * mbcnt(b2);
+}
+
+// Count one entry per lane into the 256-bin histogram of digit `shift` of
+// its key, if its key matches the selected prefix. When every matching lane
+// has the same digit (the common case for the leading digits), one lane adds
+// the whole count.
+__device__ __forceinline__ void hist_add(bool in, uint32_t key, uint32_t prefix, uint32_t pmask, int shift,
+                                         uint32_t *hist, int l)
+{
+    const bool match = in && (key & pmask) == prefix;
+    const uint32_t digit = (key >> shift) & 0xFFu;
+    const uint64_t mm = ballot(match);
+    if (mm == 0) return;
+    const int first = __ffsll(static_cast<long long>(mm)) - 1;
+    const uint32_t d0 = __shfl(digit, first);
+    const uint64_t same = ballot(match && digit == d0);
+    if (same == mm) {
+        if (l == first) atomicAdd(&hist[d0], static_cast<uint32_t>(popc(mm)));
+    } else if (match) {
+        atomicAdd(&hist[digit], 1u);
+    }
+}
+
 // Radix select over 8-bit digits of ord_key(score), most significant first,
-// with a per-wave 256-bin histogram in LDS. sc may point to global memory.
+// with a per-wave 256-bin histogram in LDS. sc may point to global memory;
+// each lane keeps 8 loads in flight.
 __device__ Sel wave_select(const float *sc, int n, int K, uint32_t *hist)
 {
     Sel r;
@@ -123,27 +156,22 @@ __device__ Sel wave_select(const float *sc, int n, int K, uint32_t *hist)
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = l; i < 256; i += kWave) hist[i] = 0u;
         wave_fence();
-        for (int j0 = 0; j0 < n; j0 += kWave) {
-            const int j = j0 + l;
-            const bool in = j < n;
-            const uint32_t key = in ? ord_key(sc[j]) : 0u;
-            const bool match = in && (key & pmask) == prefix;
-            const uint32_t digit = (key >> shift) & 0xFFu;
-            const uint64_t mm = ballot(match);
-            if (mm == 0) continue;
-            const int first = __ffsll(static_cast<long long>(mm)) - 1;
-            const uint32_t d0 = __shfl(digit, first);
-            const uint64_t same = ballot(match && digit == d0);
-            if (same == mm) {
-                if (l == first) atomicAdd(&hist[d0], static_cast<uint32_t>(popc(mm)));
-            } else if (match) {
-                atomicAdd(&hist[digit], 1u);
+        for (int j0 = 0; j0 < n; j0 += 2 * kStep) {
+            float v[2 * kVec];
+            bool in[2 * kVec];
+#pragma unroll
+            for (int e = 0; e < 2 * kVec; ++e) {
+                const int j = j0 + (e / kVec) * kStep + kVec * l + (e % kVec);
+                in[e] = j < n;
+                v[e] = in[e] ? sc[j] : 0.0f;
             }
+#pragma unroll
+            for (int e = 0; e < 2 * kVec; ++e) hist_add(in[e], ord_key(v[e]), prefix, pmask, shift, hist, l);
         }
         wave_fence();
         const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
         const uint32_t tot = c0 + c1 + c2 + c3;
-        uint32_t suf = tot; // inclusive suffix sum over lanes (higher lanes hold higher bins)
+        uint32_t suf = tot;  // inclusive suffix sum over lanes (higher lanes hold higher bins)
         for (int o = 1; o < kWave; o <<= 1) {
             const uint32_t t = __shfl_down(suf, o);
             if (l + o < kWave) suf += t;
@@ -185,31 +213,56 @@ __device__ Sel wave_select(const float *sc, int n, int K, uint32_t *hist)
     return r;
 }
 
-// Walk sc[0..n) in order and call emit(slot, j, score) for every selected
-// entry; slots are dense and ascending. Returns the number selected.
-template <class F> __device__ int wave_emit(const float *sc, int n, Sel s, F &&emit)
+// Walk sc[0..n) in order and call emit(slot, position, score) for every
+// selected entry, where position is pos[j] (or j when pos is null); slots are
+// dense and ascending. Every entry of a step is loaded before any emit, so
+// emit may write back into sc/pos (in-place compaction: slot <= j).
+template <class F> __device__ int wave_emit(const float *sc, const int32_t *pos, int n, Sel s, F &&emit)
 {
     const int l = lane_id();
     int eq_seen = 0, out = 0;
-    for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + l;
-        const bool in = j < n;
-        const float v = in ? sc[j] : 0.0f;
-        bool take;
-        if (s.all) {
-            take = in;
-        } else {
-            const uint32_t key = ord_key(v);
-            const bool gt = in && key > s.kth;
-            const bool eq = in && key == s.kth;
-            const uint64_t em = ballot(eq);
-            const int er = eq_seen + mbcnt(em);
-            eq_seen += popc(em);
-            take = gt || (eq && er < s.quota);
+    for (int j0 = 0; j0 < n; j0 += kStep) {
+        float v[kVec];
+        int32_t p[kVec];
+        bool take[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int j = j0 + kVec * l + e;
+            take[e] = j < n;
+            v[e] = take[e] ? sc[j] : 0.0f;
+            p[e] = take[e] ? (pos ? pos[j] : j) : 0;
         }
-        const uint64_t tm = ballot(take);
-        if (take) emit(out + mbcnt(tm), j, v);
-        out += popc(tm);
+        if (!s.all) {
+            bool eq[kVec];
+            int neq = 0;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const uint32_t key = ord_key(v[e]);
+                eq[e] = take[e] && key == s.kth;
+                take[e] = take[e] && key > s.kth;
+                neq += eq[e];
+            }
+            int eq_tot;
+            int rank = eq_seen + lane_prefix(neq, &eq_tot);
+            eq_seen += eq_tot;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                if (eq[e]) {
+                    take[e] = rank < s.quota;
+                    ++rank;
+                }
+            }
+        }
+        int nt = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) nt += take[e];
+        int t_tot;
+        int slot = out + lane_prefix(nt, &t_tot);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            if (take[e]) emit(slot++, p[e], v[e]);
+        }
+        out += t_tot;
     }
     return out;
 }
@@ -224,7 +277,8 @@ struct Filter {
     float tau;    // admission threshold (wave-uniform): keep score > tau
     uint32_t *hist;
 
-    // One 64-key step: lane holds (score, position) or !valid.
+    // One 64-key step: lane holds (score, position) or !valid. The branch
+    // conditions are wave-uniform (ballots, readfirstlane'd counters).
     __device__ __forceinline__ void push(bool valid, float score, int32_t pos)
     {
         bool pass = valid && score > tau;
@@ -242,7 +296,7 @@ struct Filter {
             bs[slot] = score;
             bi[slot] = pos;
         }
-        cnt += n;
+        cnt = __builtin_amdgcn_readfirstlane(cnt + n);
     }
 
     // Keep exactly the best K buffered entries, in order; tau := K-th score.
@@ -252,14 +306,13 @@ struct Filter {
         const Sel s = wave_select(bs, cnt, K, hist);
         float *bsl = bs;
         int32_t *bil = bi;
-        const int kept = wave_emit(bs, cnt, s, [&](int slot, int j, float v) {
-            const int32_t p = bil[j];
+        const int kept = wave_emit(bs, bi, cnt, s, [&](int slot, int32_t p, float v) {
             bsl[slot] = v;
             bil[slot] = p;
         });
         wave_fence();
-        cnt = kept;
-        tau = s.all ? tau : key_float(s.kth);
+        cnt = __builtin_amdgcn_readfirstlane(kept);
+        tau = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(s.all ? tau : key_float(s.kth))));
     }
 };
 
@@ -277,10 +330,9 @@ __device__ void finish_group(const Geo &geo, const SelectionOut &o, int64_t b, i
     wave_fence();
     const Sel s = wave_select(f.bs, f.cnt, f.K, f.hist);
     const int l = lane_id();
-    const int32_t *bi = f.bi;
     if (o.to_candidates) {
         int32_t *ci = o.idx + (b * geo.G + m) * o.stride;
-        const int n = wave_emit(f.bs, f.cnt, s, [&](int slot, int j, float) { ci[slot] = bi[j]; });
+        const int n = wave_emit(f.bs, f.bi, f.cnt, s, [&](int slot, int32_t p, float) { ci[slot] = p; });
         for (int t = n + l; t < o.stride; t += kWave) ci[t] = -1;
         if (o.count && l == 0) o.count[b * geo.G + m] = n;
         return;
@@ -289,8 +341,7 @@ __device__ void finish_group(const Geo &geo, const SelectionOut &o, int64_t b, i
     const int64_t stride = o.stride;
     int32_t *idx = o.idx;
     float *scr = o.sc;
-    const int n = wave_emit(f.bs, f.cnt, s, [&](int slot, int j, float v) {
-        const int32_t p = bi[j];
+    const int n = wave_emit(f.bs, f.bi, f.cnt, s, [&](int slot, int32_t p, float v) {
         for (int64_t r = r0; r < r1; ++r) {
             const int64_t off = (b * geo.Lq + r) * stride + slot;
             idx[off] = p;
@@ -363,14 +414,15 @@ __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const flo
 
 // -------------------------------------------------------- MFMA scan (bf16)
 // One workgroup = 4 waves = 4 consecutive groups of one sequence. The WG
-// streams 64-key tiles of k through LDS (double-buffered, XOR-swizzled
-// 16-byte chunks) and every wave multiplies its proxy (H x D, held in
-// registers as MFMA A fragments) by the tile:
+// streams 64-key tiles of k into LDS (double-buffered; global_load_lds puts
+// each 16-byte chunk straight into LDS at an XOR-swizzled slot, so the MFMA
+// operand reads are bank-conflict free) and every wave multiplies its proxy
+// (H x D, held in registers as MFMA A fragments) by the tile:
 //   v_mfma_f32_16x16x32_bf16: A = 16 heads x 32 dims, B = 32 dims x 16 keys.
 // Output lane l holds key (l % 16) and heads 4*(l/16) + v, v = 0..3, so the
-// ReLU and w-weighted sum over the lane's heads is in registers; a 3-step
-// exchange across the four 16-lane quarters leaves lane l with the full score
-// of key l of the tile.
+// ReLU and w-weighted sum over the lane's heads stays in registers; two
+// permlane swaps across the 16-lane quarters then leave lane l with the full
+// score of key l of the tile.
 enum ScanMode { kFilter = 0, kRows = 1 };
 
 struct ScanArgs {
@@ -381,8 +433,7 @@ struct ScanArgs {
     int H, D;
     // kFilter
     int K, cap;
-    float *buf_s;
-    int32_t *buf_i;
+    float *buf_s;  // [B*G][2*cap]: cap scores, then cap positions (int32)
     SelectionOut out;
     // kRows
     float *rows;  // [B, G, Lk]
@@ -390,23 +441,136 @@ struct ScanArgs {
 
 constexpr int kTileKeys = 64;
 
+typedef __attribute__((address_space(1))) const void *global_cptr;
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// Lane l of the wave's 1 KiB slice `slice` (0..15) of a 64 x 128 bf16 tile:
+// the tile row it fills and the element offset of its 16-byte chunk within
+// the key row, so that LDS slot (row, l % 16) holds logical chunk
+// (l % 16) ^ (row % 16).
+__device__ __forceinline__ int slice_row(int slice, int l) { return slice * 4 + (l >> 4); }
+__device__ __forceinline__ int slice_col(int slice, int l) { return (((l & 15) ^ (slice_row(slice, l) & 15)) * 8); }
+
+// B fragment for key block cb (16 keys), dim block kb (32 dims): lane l reads
+// key 16*cb + l%16, dims 32*kb + 8*(l/16) .. +8, from the swizzled tile.
+__device__ __forceinline__ bf16x8 b_frag(const uint16_t *tile, int cb, int kb, int l)
+{
+    const int row = 16 * cb + (l & 15);
+    const int chunk = (4 * kb + (l >> 4)) ^ (l & 15);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(tile + row * 128 + chunk * 8));
+}
+
+template <int RB>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&afr)[RB][4], const uint16_t *tile, int cb, int l,
+                                           f32x4 (&acc)[RB])
+{
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 bfr = b_frag(tile, cb, kb, l);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr, acc[rb], 0, 0, 0);
+    }
+}
+
+template <int RB>
+__device__ __forceinline__ float relu_weighted(const f32x4 (&acc)[RB], const float (&wr)[RB][4])
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            // ReLU on the bit pattern: negative floats (and -0) are negative
+            // int32, so max(bits, 0) gives +0 for them and keeps the rest.
+            const float relu = __int_as_float(max(__float_as_int(acc[rb][v]), 0));
+            s = fmaf(wr[rb][v], relu, s);
+        }
+    }
+    return s;
+}
+
+// Sum p[cb] over the four 16-lane quarters so lane l ends with key l's total.
+__device__ __forceinline__ float quarter_transpose_sum(const float (&p)[4])
+{
+    // halves: lanes 0-31 collect key blocks 0 and 1, lanes 32-63 blocks 2 and 3
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+    const float x0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+    const float x1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+    // rows: quarter 0 keeps block 0, 1 block 1, 2 block 2, 3 block 3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+    return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;  // + 0: one zero, +0
+}
+
+// Score of key l of the tile for the wave's A (RB row blocks of 16 heads).
+// Two accumulator sets let the MFMAs of block cb+1 overlap the weighted
+// ReLU reduction of block cb.
+template <int RB>
+__device__ __forceinline__ float tile_scores(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4],
+                                             const uint16_t *tile, int l)
+{
+    f32x4 acc0[RB], acc1[RB];
+    float p[4];
+    mfma_block<RB>(afr, tile, 0, l, acc0);
+    mfma_block<RB>(afr, tile, 1, l, acc1);
+    p[0] = relu_weighted<RB>(acc0, wr);
+    mfma_block<RB>(afr, tile, 2, l, acc0);
+    p[1] = relu_weighted<RB>(acc1, wr);
+    mfma_block<RB>(afr, tile, 3, l, acc1);
+    p[2] = relu_weighted<RB>(acc0, wr);
+    p[3] = relu_weighted<RB>(acc1, wr);
+    return quarter_transpose_sum(p);
+}
+
+template <int H>
+__device__ __forceinline__ void load_a(const uint16_t *src, int l, bf16x8 (&afr)[H / 16][4])
+{
+#pragma unroll
+    for (int rb = 0; rb < H / 16; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            afr[rb][kb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(src + (16 * rb + (l & 15)) * 128 + 32 * kb + 8 * (l >> 4)));
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 16][4])
+{
+#pragma unroll
+    for (int rb = 0; rb < H / 16; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wr[rb][v] = src[16 * rb + 4 * (l >> 4) + v];
+    }
+}
+
+// Sampled admission threshold (filter mode). Before the full pass the WG
+// scores every `stride`-th tile; each wave sets tau a few standard deviations
+// below its sample's estimate of the K-th best score, so the full pass admits
+// about 1.5 K survivors instead of c (1 + ln(n / c)). If a group still ends
+// with fewer than K survivors the WG repeats the pass for it with tau = -inf,
+// so the selection is exact whatever the sample shows.
+constexpr int kSampleStride = 16;     // tiles between sampled tiles (>= this)
+constexpr float kSampleSigmas = 6.0f;
+
 template <int H, int D, int Mode>
 __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
 {
-    static_assert(H % 16 == 0 && D == 128, "tile swizzle assumes 16 chunks of 8 bf16 per key row");
-    constexpr int RB = H / 16;      // 16-head row blocks
-    constexpr int KB = D / 32;      // 32-dim contraction blocks
-    constexpr int CH = D / 8;       // 16-byte chunks per key row
+    static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
+    constexpr int RB = H / 16;
     constexpr int NT = kTileKeys;
-    constexpr int LOADS = NT * CH / 256;
 
-    __shared__ __attribute__((aligned(16))) uint16_t tile[2][NT * D];
+    // two distinct LDS objects, so the compiler can tell that the tile being
+    // read is not the one the in-flight global_load_lds is filling
+    __shared__ __attribute__((aligned(1024))) uint16_t tile0[NT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t tile1[NT * D];
     __shared__ uint32_t hist[4][256];
 
     const Geo &geo = a.geo;
     const int wv = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
-    const int Q = l >> 4;
     const int64_t nblk = (geo.G + 3) >> 2;
     const int64_t b = blockIdx.x % geo.B;
     const int64_t blk = nblk - 1 - blockIdx.x / geo.B;  // longest prefixes first
@@ -419,22 +583,10 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
     const int64_t gid = b * geo.G + (active ? m : blk * 4);
 
-    // A fragments (proxy) and the lane's head weights
-    bf16x8 afr[RB][KB];
+    bf16x8 afr[RB][4];
     float wr[RB][4];
-    {
-        const uint16_t *qg = static_cast<const uint16_t *>(a.qsrc) + gid * H * D;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(qg + (16 * rb + (l & 15)) * D + 32 * kb + 8 * Q);
-                afr[rb][kb] = __builtin_bit_cast(bf16x8, v);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) wr[rb][v] = a.wsrc[gid * H + 16 * rb + 4 * Q + v];
-        }
-    }
+    load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
+    load_w<H>(a.wsrc + gid * H, l, wr);
 
     Filter f;
     f.K = a.K;
@@ -443,88 +595,104 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     f.tau = -INFINITY;
     f.hist = hist[wv];
     if (Mode == kFilter) {
-        f.bs = a.buf_s + gid * a.cap;
-        f.bi = a.buf_i + gid * a.cap;
+        f.bs = a.buf_s + gid * 2 * static_cast<int64_t>(a.cap);  // [cap scores | cap positions]
+        f.bi = reinterpret_cast<int32_t *>(f.bs + a.cap);
     }
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
-    uint4 stage[LOADS];
-    auto load_tile = [&](int64_t base) {
+    // This lane's part of every tile load: 4 slices of 1 KiB per wave.
+    auto issue_tile = [&](int buf, int64_t base) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = threadIdx.x + 256 * i;
-            const int r = id / CH, ch = id % CH;
-            const int64_t s = base + r;
-            stage[i] = (s < geo.Lk) ? *reinterpret_cast<const uint4 *>(kseq + s * D + ch * 8) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+            const int slice = wv * 4 + j;
+            int64_t s = base + slice_row(slice, l);
+            s = s < geo.Lk ? s : geo.Lk - 1;  // past the end: any valid row (its scores are masked)
+            const uint16_t *src = kseq + s * D + slice_col(slice, l);
+            uint16_t *dst = buf ? tile1 : tile0;
+            __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int id = threadIdx.x + 256 * i;
-            const int r = id / CH, ch = id % CH;
-            *reinterpret_cast<uint4 *>(&tile[buf][r * D + ((ch ^ (r & 15)) * 8)]) = stage[i];
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int it = 0; it < ntiles; ++it) {
-        const int cur = it & 1;
-        const int64_t base = static_cast<int64_t>(it) * NT;
-        if (it + 1 < ntiles) load_tile(base + NT);
-
-        float p[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            f32x4 acc[RB];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const int krow = 16 * cb + (l & 15);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(&tile[cur][krow * D + (((4 * kb + Q) ^ (l & 15)) * 8)]);
-                const bf16x8 bfr = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr, acc[rb], 0, 0, 0);
-            }
-            float s = 0.0f;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s = fmaf(wr[rb][v], fmaxf(acc[rb][v], 0.0f), s);
-            }
-            p[cb] = s;
-        }
-        // quarters Q and Q^2 exchange column blocks, then Q and Q^1
-        const bool lo = Q < 2;
-        const float x0 = (lo ? p[0] : p[2]) + __shfl_xor(lo ? p[2] : p[0], 32);
-        const float x1 = (lo ? p[1] : p[3]) + __shfl_xor(lo ? p[3] : p[1], 32);
-        const bool odd = Q & 1;
-        float score = (odd ? x1 : x0) + __shfl_xor(odd ? x0 : x1, 16);
-        score = score + 0.0f;  // one zero: +0
-
-        const int64_t s = base + l;
-        const bool valid = s <= my_tlast;
-        if (Mode == kFilter) {
-            if (active) f.push(valid, score, static_cast<int32_t>(s));
-        } else {
-            if (active && s < geo.Lk) row[s] = valid ? score : -INFINITY;
-        }
-
-        if (it + 1 < ntiles) store_tile(cur ^ 1);
+    // One pass over tiles t0, t0 + step, ... < ntiles; fn(tile index, base
+    // position, lane's score) after each tile's scores.
+    auto pass = [&](int t0, int step, auto &&fn) {
+        if (t0 >= ntiles) return;
+        issue_tile(0, static_cast<int64_t>(t0) * NT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        int cur = 0;
+        for (int it = t0; it < ntiles; it += step) {
+            const int64_t base = static_cast<int64_t>(it) * NT;
+            if (it + step < ntiles) issue_tile(cur ^ 1, base + static_cast<int64_t>(step) * NT);
+            const float score = cur ? tile_scores<RB>(afr, wr, tile1, l) : tile_scores<RB>(afr, wr, tile0, l);
+            fn(it, base, score);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed in LDS
+            __syncthreads();
+            cur ^= 1;
+        }
+    };
+
+    if (Mode == kRows) {
+        pass(0, 1, [&](int, int64_t base, float score) {
+            const int64_t s = base + l;
+            if (active && s < geo.Lk) row[s] = s <= my_tlast ? score : -INFINITY;
+        });
+        if (!active) return;
+        for (int64_t s = static_cast<int64_t>(ntiles) * NT + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
+        return;
+    }
+
+    // ---- phase A: sampled threshold (the buffer is empty, use it as scratch)
+    const int64_t n_valid = my_tlast + 1;
+    const int sample_cap_tiles = (2 * a.cap) / NT;
+    int stride = kSampleStride;
+    if ((ntiles + stride - 1) / stride > sample_cap_tiles) stride = (ntiles + sample_cap_tiles - 1) / sample_cap_tiles;
+    const bool sample = ntiles * NT > 4 * a.K && sample_cap_tiles > 0;  // short prefixes: plain streaming
+    if (sample) {
+        float *smp = f.bs;
+        int nsv = 0;  // valid sampled keys (wave-uniform)
+        pass(0, stride, [&](int it, int64_t base, float score) {
+            const int64_t s = base + l;
+            const bool valid = s <= my_tlast;
+            if (active) smp[(it / stride) * NT + l] = valid ? score : -INFINITY;
+            nsv += popc(ballot(valid));
+        });
+        if (active) {
+            const int nslots = ((ntiles - 1) / stride + 1) * NT;
+            const float expect = static_cast<float>(a.K) * static_cast<float>(nsv) / static_cast<float>(n_valid);
+            const int r = static_cast<int>(ceilf(expect + kSampleSigmas * sqrtf(expect) + 8.0f));
+            if (n_valid > 2 * static_cast<int64_t>(a.K) && r < nsv) {
+                wave_fence();
+                const Sel sel = wave_select(smp, nslots, r, f.hist);
+                f.tau = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(key_float(sel.kth))));
+            }
+        }
+    }
+
+    // ---- phase B: the full pass with the streaming filter
+    auto filter_fn = [&](int, int64_t base, float score) {
+        const int64_t s = base + l;
+        if (active) f.push(s <= my_tlast, score, static_cast<int32_t>(s));
+    };
+    pass(0, 1, filter_fn);
+
+    // exactness guard: a group with fewer than min(K, n_valid) survivors had
+    // its sampled tau set too high; the WG repeats the pass for it from -inf
+    const int64_t need = n_valid < a.K ? n_valid : a.K;
+    const bool failed = active && f.cnt < need;
+    if (__syncthreads_or(failed)) {
+        const bool redo = failed;
+        if (redo) {
+            f.cnt = 0;
+            f.tau = -INFINITY;
+        }
+        pass(0, 1, [&](int, int64_t base, float score) {
+            const int64_t s = base + l;
+            if (redo) f.push(s <= my_tlast, score, static_cast<int32_t>(s));
+        });
     }
 
     if (!active) return;
-    if (Mode == kFilter) {
-        finish_group(geo, a.out, b, m, f);
-    } else {
-        for (int64_t s = static_cast<int64_t>(ntiles) * NT + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
-    }
+    finish_group(geo, a.out, b, m, f);
 }
 
 // ------------------------------------------------- exact-order scan (any)
@@ -576,8 +744,8 @@ __global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
     f.tau = -INFINITY;
     f.hist = hist[wv];
     if (Mode == kFilter) {
-        f.bs = a.buf_s + gid * a.cap;
-        f.bi = a.buf_i + gid * a.cap;
+        f.bs = a.buf_s + gid * 2 * static_cast<int64_t>(a.cap);  // [cap scores | cap positions]
+        f.bi = reinterpret_cast<int32_t *>(f.bs + a.cap);
     }
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
@@ -623,8 +791,8 @@ __device__ void finish_member(const RefineArgs &a, int64_t b, int64_t r, const i
     const int l = lane_id();
     int32_t *oi = a.out_idx + (b * a.geo.Lq + r) * a.topk;
     float *os = a.out_sc ? a.out_sc + (b * a.geo.Lq + r) * a.topk : nullptr;
-    const int n = wave_emit(srow, nvalid, s, [&](int slot, int j, float v) {
-        oi[slot] = C[j];
+    const int n = wave_emit(srow, C, nvalid, s, [&](int slot, int32_t p, float v) {
+        oi[slot] = p;
         if (os) os[slot] = v;
     });
     for (int t = n + l; t < a.topk; t += kWave) {
@@ -634,25 +802,24 @@ __device__ void finish_member(const RefineArgs &a, int64_t b, int64_t r, const i
 }
 
 // One workgroup (4..8 waves) per group; wave w re-scores member
-// (round * nwaves + w).
-// The candidate keys of each 64-candidate tile are gathered once into LDS and
-// shared by every member wave.
+// (round * nwaves + w). Each 64-candidate tile of keys is gathered once into
+// LDS (global_load_lds, same swizzle as the scan) and shared by every member
+// wave; candidate positions are prefetched one tile ahead.
 template <int H, int D>
 __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
 {
-    static_assert(H % 16 == 0 && D == 128, "tile swizzle assumes 16 chunks of 8 bf16 per key row");
-    constexpr int RB = H / 16, KB = D / 32, CH = D / 8, NT = kTileKeys;
-    constexpr int MAXLOADS = NT * CH / 256;  // blockDim >= 256
+    static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
+    constexpr int RB = H / 16, NT = kTileKeys;
+    constexpr int kSlices = 16;  // 1 KiB slices per tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t tile[2][NT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t tile0[NT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t tile1[NT * D];
     __shared__ uint32_t hist[8][256];
 
     const Geo &geo = a.geo;
-    const int nthreads = blockDim.x;
-    const int nwaves = nthreads >> 6;
+    const int nwaves = blockDim.x >> 6;
     const int wv = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
-    const int Q = l >> 4;
     const int64_t gid = blockIdx.x;
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
@@ -661,29 +828,24 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
     const int32_t *C = a.cand + gid * a.c;
     const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
     const int ntiles = (nc + NT - 1) / NT;
-    const int loads = (NT * CH + nthreads - 1) / nthreads;
 
-    uint4 stage[MAXLOADS];
-    auto load_tile = [&](int jb) {
+    // positions of the rows this lane gathers for a tile (slices wv, wv+nwaves, ...)
+    auto load_pos = [&](int tile_idx, int32_t (&pos)[4]) {
 #pragma unroll
-        for (int i = 0; i < MAXLOADS; ++i) {
-            const int id = threadIdx.x + nthreads * i;
-            if (i < loads && id < NT * CH) {
-                const int r = id / CH, ch = id % CH;
-                const int j = jb + r;
-                const int32_t s = (j < nc) ? C[j] : -1;
-                stage[i] = (s >= 0) ? *reinterpret_cast<const uint4 *>(kseq + static_cast<int64_t>(s) * D + ch * 8)
-                                    : make_uint4(0, 0, 0, 0);
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int slice = wv + nwaves * j;
+            const int cj = tile_idx * NT + slice_row(slice, l);
+            pos[j] = (slice < kSlices && cj < nc) ? C[cj] : 0;  // row 0: any valid key row
         }
     };
-    auto store_tile = [&](int buf) {
+    auto issue_tile = [&](int buf, const int32_t (&pos)[4]) {
 #pragma unroll
-        for (int i = 0; i < MAXLOADS; ++i) {
-            const int id = threadIdx.x + nthreads * i;
-            if (i < loads && id < NT * CH) {
-                const int r = id / CH, ch = id % CH;
-                *reinterpret_cast<uint4 *>(&tile[buf][r * D + ((ch ^ (r & 15)) * 8)]) = stage[i];
+        for (int j = 0; j < 4; ++j) {
+            const int slice = wv + nwaves * j;
+            if (slice < kSlices) {
+                const uint16_t *src = kseq + static_cast<int64_t>(pos[j]) * D + slice_col(slice, l);
+                uint16_t *dst = buf ? tile1 : tile0;
+                __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
             }
         }
     };
@@ -695,72 +857,38 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
         const int64_t t = geo.Lk - geo.Lq + r;
         float *srow = a.scratch + (gid * geo.g + (active ? mi : 0)) * a.c;
 
-        bf16x8 afr[RB][KB];
+        bf16x8 afr[RB][4];
         float wr[RB][4];
-        {
-            const uint16_t *qr = static_cast<const uint16_t *>(a.q) + (b * geo.Lq + r) * H * D;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(qr + (16 * rb + (l & 15)) * D + 32 * kb + 8 * Q);
-                    afr[rb][kb] = __builtin_bit_cast(bf16x8, v);
-                }
-#pragma unroll
-                for (int v = 0; v < 4; ++v) wr[rb][v] = a.w[(b * geo.Lq + r) * H + 16 * rb + 4 * Q + v];
-            }
-        }
+        load_a<H>(static_cast<const uint16_t *>(a.q) + (b * geo.Lq + r) * H * D, l, afr);
+        load_w<H>(a.w + (b * geo.Lq + r) * H, l, wr);
 
-        int nvalid = 0;
+        int32_t pos[4], pos_next[4];
         if (ntiles > 0) {
-            load_tile(0);
-            store_tile(0);
+            load_pos(0, pos);
+            issue_tile(0, pos);
         }
+        if (ntiles > 1) load_pos(1, pos_next);
+        int32_t cpos = l < nc ? C[l] : 0;
+        int nvalid = 0;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+
         for (int it = 0; it < ntiles; ++it) {
             const int cur = it & 1;
-            const int jb = it * NT;
-            if (it + 1 < ntiles) load_tile(jb + NT);
-
-            float p[4];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                f32x4 acc[RB];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                const int krow = 16 * cb + (l & 15);
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const uint4 v =
-                        *reinterpret_cast<const uint4 *>(&tile[cur][krow * D + (((4 * kb + Q) ^ (l & 15)) * 8)]);
-                    const bf16x8 bfr = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr, acc[rb], 0, 0, 0);
-                }
-                float s = 0.0f;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) s = fmaf(wr[rb][v], fmaxf(acc[rb][v], 0.0f), s);
-                }
-                p[cb] = s;
+            const int j = it * NT + l;
+            const int32_t cpos_here = cpos;
+            if (it + 1 < ntiles) {
+                issue_tile(cur ^ 1, pos_next);
+                if (it + 2 < ntiles) load_pos(it + 2, pos_next);
+                cpos = (j + NT < nc) ? C[j + NT] : 0;
             }
-            const bool lo = Q < 2;
-            const float x0 = (lo ? p[0] : p[2]) + __shfl_xor(lo ? p[2] : p[0], 32);
-            const float x1 = (lo ? p[1] : p[3]) + __shfl_xor(lo ? p[3] : p[1], 32);
-            const bool odd = Q & 1;
-            float score = (odd ? x1 : x0) + __shfl_xor(odd ? x0 : x1, 16);
-            score = score + 0.0f;
-
-            const int j = jb + l;
+            const float score = cur ? tile_scores<RB>(afr, wr, tile1, l) : tile_scores<RB>(afr, wr, tile0, l);
             if (active) {
                 const bool in = j < nc;
-                const int32_t pos = in ? C[j] : 0;
-                nvalid += popc(ballot(in && pos <= t));
+                nvalid += popc(ballot(in && cpos_here <= t));
                 if (in) srow[j] = score;
             }
-            if (it + 1 < ntiles) store_tile(cur ^ 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile in LDS
             __syncthreads();
         }
         if (active) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
@@ -834,8 +962,7 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     a.D = sh.D;
     a.K = L.K;
     a.cap = L.cap;
-    a.buf_s = L.buf_s;
-    a.buf_i = L.buf_i;
+    a.buf_s = L.buf;
     a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
     a.rows = L.rows;
     const int64_t blocks = sh.B * ((L.G + 3) / 4);

@@ -209,3 +209,50 @@ def test_side_stream_and_preallocated_workspace():
     assert torch.equal(idx, ref)
     with pytest.raises(pv.PivotError):
         pv.index_refine(tq, tw, tk, 8, 16, 32, workspace=ws[:need // 2])
+
+
+def _striped_keys(L, seed, hot_sampled):
+    """Exact keys where the 64-key tiles at multiples of 16 (the tiles the
+    scan samples for its threshold) are all "hot" (hot_sampled=True) or all
+    "cold" (False) relative to the rest. With positive queries, hot keys score
+    far above cold ones."""
+    r = np.random.default_rng([seed, 7])
+    cold = r.integers(-3, 4, size=(1, L, 128)).astype(np.float64) / 4.0
+    hot = r.integers(2, 4, size=(1, L, 128)).astype(np.float64) / 4.0
+    tile = np.arange(L) // 64
+    sampled = (tile % 16) == 0
+    use_hot = sampled if hot_sampled else ~sampled
+    k = np.where(use_hot[None, :, None], hot, cold)
+    from workloads import to_storage
+    return to_storage(k, BF16)
+
+
+@pytest.mark.parametrize("hot_sampled", [True, False], ids=["sample_too_high", "sample_too_low"])
+def test_mfma_sampled_threshold_stays_exact(hot_sampled):
+    """The scan sets its admission threshold from every 16th tile. Keys that
+    make the sample unrepresentative must still give the exact top-K: a too
+    high sample forces the exact re-run, a too low one forces compactions."""
+    L, g, topk, c = 4096, 8, 128, 256
+    r = np.random.default_rng(11)
+    q = r.integers(1, 4, size=(1, L, 64, 128)).astype(np.float64) / 4.0
+    from workloads import to_storage
+    q = to_storage(q, BF16)
+    w = np.ldexp(1.0, r.integers(-3, 1, size=(1, L, 64))).astype(np.float32)
+    k = _striped_keys(L, 3, hot_sampled)
+    tq, tw, tk = to_device(q, w, k)
+    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True)
+    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True)
+    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True)
+    torch.cuda.synchronize()
+    ref = oracle.refine(q, w, k, g, topk, c)
+    np.testing.assert_array_equal(f_n.cpu().numpy(), ref["cand_n"])
+    np.testing.assert_array_equal(f_c.cpu().numpy(), ref["cand"])
+    np.testing.assert_array_equal(f_i.cpu().numpy(), ref["indices"])
+    np.testing.assert_array_equal(f_s.cpu().numpy(), ref["scores"])
+    ref = oracle.reuse(q, w, k, g, topk)
+    np.testing.assert_array_equal(r_i.cpu().numpy(), ref["indices"])
+    np.testing.assert_array_equal(r_s.cpu().numpy(), ref["scores"])
+    rows = np.r_[0:64, 1000:1010, 2047:2050, 4000:4096]
+    ref = oracle.dense(q, w, k, topk, rows=rows)
+    np.testing.assert_array_equal(d_i.cpu().numpy()[0, rows], ref["indices"][0, rows])
+    np.testing.assert_array_equal(d_s.cpu().numpy()[0, rows], ref["scores"][0, rows])
