@@ -73,3 +73,93 @@ def check_candidates(gpu_C, ref_C, proxy_row, what=""):
     far = np.abs(ds - boundary) > t
     assert not far.any(), f"{what}: candidates {diff[far][:5]} differ away from the boundary {boundary}"
     return len(diff)
+
+
+# ----------------------------------------------------------- group checks
+def _f64(a):
+    from workloads import bf16_bits_to_f32
+    return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def member_scores(q, w, k, b, r, positions):
+    """Float64 eq. (1) scores of query row r of sequence b over ``positions``."""
+    qv = _f64(q[b, r])                                   # [H, d]
+    kv = _f64(k[b, positions])                           # [P, d]
+    return (w[b, r].astype(np.float64)[:, None] * np.maximum(qv @ kv.T, 0.0)).sum(axis=0)
+
+
+def check_refine_groups(q, w, k, g, topk, c, gpu_idx, gpu_sc, gpu_C, gpu_n, groups):
+    """Float rule on sampled Refine groups: candidate sets against the oracle's
+    proxy scores, member rows against the oracle's member step run on the
+    GPU's own candidate sets. Returns the total symmetric-difference size."""
+    import oracle
+    B, Lq = q.shape[:2]
+    Lk = k.shape[1]
+    G = -(-Lq // g)
+    ref = oracle.refine(q, w, k, g, topk, c, groups=groups)
+    given = oracle.refine(q, w, k, g, topk, c, groups=groups, cand_in=gpu_C, cand_in_n=gpu_n)
+    diffs = 0
+    for u in groups:
+        b, m = divmod(int(u), G)
+        prow = oracle.proxy_row(q, w, k, g, b, m)
+        n = gpu_n[b, m]
+        diffs += check_candidates(gpu_C[b, m, :n], ref["cand"][b, m, :ref["cand_n"][b, m]], prow,
+                                  f"C of group {b}/{m}")
+        for r in range(m * g, min((m + 1) * g, Lq)):
+            diffs += compare_row(gpu_idx[b, r], None if gpu_sc is None else gpu_sc[b, r],
+                                 given["indices"][b, r], given["scores"][b, r],
+                                 lambda p, b=b, r=r: member_scores(q, w, k, b, r, p), f"refine row {b}/{r}")
+    return diffs
+
+
+def check_reuse_groups(q, w, k, g, topk, gpu_idx, gpu_sc, groups):
+    import oracle
+    B, Lq = q.shape[:2]
+    G = -(-Lq // g)
+    ref = oracle.reuse(q, w, k, g, topk, groups=groups)
+    diffs = 0
+    for u in groups:
+        b, m = divmod(int(u), G)
+        prow = oracle.proxy_row(q, w, k, g, b, m).astype(np.float64)
+        r0 = m * g
+        diffs += compare_row(gpu_idx[b, r0], None if gpu_sc is None else gpu_sc[b, r0], ref["indices"][b, r0],
+                             ref["scores"][b, r0], lambda p: prow[p], f"reuse group {b}/{m}")
+        rows = gpu_idx[b, r0:min(r0 + g, Lq)]
+        assert np.all(rows == rows[0]), f"reuse group {b}/{m}: member rows differ"
+    return diffs
+
+
+def check_dense_rows(q, w, k, topk, gpu_idx, gpu_sc, rows):
+    import oracle
+    B, Lq = q.shape[:2]
+    Lk = k.shape[1]
+    ref = oracle.dense(q, w, k, topk, rows=rows)
+    diffs = 0
+    for u in rows:
+        b, r = divmod(int(u), Lq)
+        t = Lk - Lq + r
+        diffs += compare_row(gpu_idx[b, r], None if gpu_sc is None else gpu_sc[b, r], ref["indices"][b, r],
+                             ref["scores"][b, r], lambda p, b=b, r=r: member_scores(q, w, k, b, r, p),
+                             f"dense row {b}/{r}")
+    return diffs
+
+
+def structure_all_rows(idx, Lq, Lk, topk, g=None, counts=None):
+    """Vectorised structural checks over every row: -1 only in the tail,
+    strictly ascending valid entries, each <= its bound (t, or t_last for
+    Reuse), and the valid count where it has a closed form."""
+    B, _, K = idx.shape
+    valid = idx >= 0
+    n = valid.sum(axis=-1)
+    ar = np.arange(K)
+    assert np.array_equal(valid, ar[None, None, :] < n[..., None]), "-1 entries not confined to the tail"
+    d = np.diff(idx, axis=-1)
+    both = valid[..., 1:]
+    assert np.all(d[both] > 0), "valid entries not strictly ascending"
+    pos = np.arange(Lq) + (Lk - Lq)
+    if g is not None:
+        pos = np.minimum((pos - (Lk - Lq)) // g * g + g, Lq) - 1 + (Lk - Lq)
+    last = np.take_along_axis(idx, np.maximum(n - 1, 0)[..., None], axis=-1)[..., 0]
+    assert np.all((n == 0) | (last <= pos[None, :])), "index beyond its causal bound"
+    if counts is not None:
+        assert np.array_equal(n, counts), "valid counts differ from the closed form"
