@@ -152,13 +152,20 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
-    pv.timing_enable(True)
+    # timed region: plain calls, as a caller would make them
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         out = step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del out
+    # per-kernel durations: the same steps again with every launch bracketed
+    # by hipEvents on its stream
+    pv.timing_enable(True)
+    for _ in range(args.steps):
+        out = step()
+    torch.cuda.synchronize()
     stages = pv.timing_read()
     pv.timing_enable(False)
     del out

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "pivot.h"
@@ -102,8 +103,21 @@ struct Layout {
     int64_t G;
     int g, K, cap;
     bool pool;
-    size_t qbar, wbar, buf, cand, cand_n, scratch, total;
+    bool few;               // few groups: split scan into score rows + block selects
+    int scan_splits, refine_splits;
+    size_t qbar, wbar, buf, rows, cand, cand_n, scratch, total;
 };
+
+// Below this many groups the per-group fused scan cannot fill 256 CUs; the
+// key axis is split over workgroups instead (decode shapes). The environment
+// variable PIVOT_FEW_GROUPS overrides the threshold (0 disables the split
+// path, a huge value forces it); tests use it to cover both paths.
+int64_t few_groups_threshold()
+{
+    const char *v = getenv("PIVOT_FEW_GROUPS");
+    if (v && *v) return strtoll(v, nullptr, 10);
+    return 256;
+}
 
 pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, int32_t c, Layout *L)
 {
@@ -139,7 +153,19 @@ pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, 
     };
     l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
-    l.buf = take(groups * 2 * cap * sizeof(float));
+    l.few = pivot::mfma_shape(sh) && static_cast<int64_t>(groups) < few_groups_threshold();
+    if (l.few) {
+        const int64_t tiles = (p->lk + 63) / 64;
+        int64_t ss = (2048 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
+        l.scan_splits = static_cast<int>(ss < tiles ? ss : tiles);
+        const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 63) / 64;
+        int64_t rs = (512 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
+        l.refine_splits = static_cast<int>(rs < ctiles ? rs : ctiles);
+        l.rows = take(groups * static_cast<size_t>(p->lk) * sizeof(float));
+    } else {
+        l.scan_splits = l.refine_splits = 1;
+        l.buf = take(groups * 2 * cap * sizeof(float));
+    }
     if (variant == PIVOT_REFINE) {
         l.cand = take(groups * static_cast<size_t>(c) * sizeof(int32_t));
         l.cand_n = take(groups * sizeof(int32_t));
@@ -200,7 +226,7 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     sl.g = L.g;
     sl.K = L.K;
     sl.cap = L.cap;
-    sl.buf = reinterpret_cast<float *>(base + L.buf);
+    sl.buf = L.few ? nullptr : reinterpret_cast<float *>(base + L.buf);
     if (variant == PIVOT_REFINE) {
         sl.out_idx = cand;
         sl.out_sc = nullptr;
@@ -215,7 +241,27 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
         sl.to_candidates = 0;
     }
     sl.rows = nullptr;
-    {
+    if (L.few) {
+        sl.rows = reinterpret_cast<float *>(base + L.rows);
+        {
+            StageTimer tm(PIVOT_STAGE_SCAN, s);
+            st = hip_status(pivot::launch_scan_split(sh, sl, L.scan_splits, s), "split scan launch");
+        }
+        if (st != PIVOT_OK) return st;
+        pivot::RowSelectLaunch rs{};
+        rs.G = L.G;
+        rs.g = L.g;
+        rs.kind = 0;
+        rs.rows = sl.rows;
+        rs.K = L.K;
+        rs.to_candidates = sl.to_candidates;
+        rs.out_idx = sl.out_idx;
+        rs.out_sc = sl.out_sc;
+        rs.out_count = sl.out_count;
+        rs.out_stride = sl.out_stride;
+        StageTimer tm(PIVOT_STAGE_SELECT, s);
+        st = hip_status(pivot::launch_select_rows(sh, rs, s), "select launch");
+    } else {
         StageTimer tm(PIVOT_STAGE_SCAN, s);
         st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
     }
@@ -234,8 +280,26 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     rl.scratch = reinterpret_cast<float *>(base + L.scratch);
     rl.out_idx = indices;
     rl.out_sc = scores;
-    StageTimer tm(PIVOT_STAGE_REFINE, s);
-    return hip_status(pivot::launch_refine(sh, rl, s), "refine launch");
+    rl.splits = L.refine_splits;
+    {
+        StageTimer tm(PIVOT_STAGE_REFINE, s);
+        st = hip_status(pivot::launch_refine(sh, rl, s), "refine launch");
+    }
+    if (st != PIVOT_OK || rl.splits <= 1) return st;
+    pivot::RowSelectLaunch ms{};
+    ms.G = L.G;
+    ms.g = L.g;
+    ms.kind = 1;
+    ms.rows = rl.scratch;
+    ms.K = topk;
+    ms.out_idx = indices;
+    ms.out_sc = scores;
+    ms.out_stride = topk;
+    ms.cand = cand;
+    ms.cand_n = cand_n;
+    ms.c = c;
+    StageTimer tm(PIVOT_STAGE_SELECT, s);
+    return hip_status(pivot::launch_select_rows(sh, ms, s), "member select launch");
 }
 
 }  // namespace

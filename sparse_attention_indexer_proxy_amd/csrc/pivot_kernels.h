@@ -43,6 +43,24 @@ struct RefineLaunch {
     float *scratch;     // [B*G, g, c]
     int32_t *out_idx;
     float *out_sc;
+    int splits;         // > 1: split C over workgroups, member selection left to launch_select_rows
+};
+
+// Block-wide selection of rows held in memory (few-groups path).
+struct RowSelectLaunch {
+    int64_t G;
+    int g;
+    int kind;           // 0: group score rows [B*G, Lk]; 1: member rows of the split refine
+    const float *rows;
+    int K;
+    int to_candidates;
+    int32_t *out_idx;
+    float *out_sc;
+    int32_t *out_count;
+    int out_stride;
+    const int32_t *cand;
+    const int32_t *cand_n;
+    int c;
 };
 
 bool mfma_shape(const LaunchShape &sh);
@@ -50,5 +68,8 @@ hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, c
                        float *wbar, hipStream_t st);
 hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st);
 hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st);
+// Proxy score rows with the key axis split over `splits` workgroups per group.
+hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int splits, hipStream_t st);
+hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, hipStream_t st);
 
 }  // namespace pivot

@@ -695,6 +695,393 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     finish_group(geo, a.out, b, m, f);
 }
 
+// ---------------------------------------------- split scan (few groups)
+// When there are too few groups to fill the GPU (decode: one group per
+// sequence), the key axis of each group is split over many workgroups and
+// the proxy scores are written to a row buffer [B*G, Lk] for k_select_rows.
+// The four waves of a workgroup share each 64-key tile and take one 16-key
+// block each; the scan is HBM-bound here (each key meets only H rows).
+template <int H, int D>
+__global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
+{
+    static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
+    constexpr int RB = H / 16;
+    constexpr int NT = kTileKeys;
+    __shared__ __attribute__((aligned(1024))) uint16_t tile0[NT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t tile1[NT * D];
+
+    const Geo &geo = a.geo;
+    const int wv = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const int64_t gid = blockIdx.x / splits;
+    const int split = blockIdx.x % splits;
+    const int64_t b = gid / geo.G, m = gid % geo.G;
+    const int64_t tl = geo.t_last(m);
+    const int ntiles_all = static_cast<int>(tl / NT) + 1;
+    const int per = (ntiles_all + splits - 1) / splits;
+    const int t0 = split * per;
+    const int t1 = t0 + per < ntiles_all ? t0 + per : ntiles_all;
+    if (t0 >= t1) return;  // uniform over the workgroup
+    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    float *row = a.rows + gid * geo.Lk;
+
+    bf16x8 afr[RB][4];
+    float wr[RB][4];
+    load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
+    load_w<H>(a.wsrc + gid * H, l, wr);
+
+    auto issue_tile = [&](int buf, int64_t base) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int slice = wv * 4 + j;
+            int64_t s = base + slice_row(slice, l);
+            s = s < geo.Lk ? s : geo.Lk - 1;
+            const uint16_t *src = kseq + s * D + slice_col(slice, l);
+            uint16_t *dst = buf ? tile1 : tile0;
+            __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
+        }
+    };
+
+    issue_tile(0, static_cast<int64_t>(t0) * NT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    int cur = 0;
+    for (int it = t0; it < t1; ++it) {
+        const int64_t base = static_cast<int64_t>(it) * NT;
+        if (it + 1 < t1) issue_tile(cur ^ 1, base + NT);
+        f32x4 acc[RB];
+        mfma_block<RB>(afr, cur ? tile1 : tile0, wv, l, acc);
+        const float p = relu_weighted<RB>(acc, wr);
+        // sum over the four 16-lane quarters: every lane ends with key l % 16
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+        const float x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        const float score = (__uint_as_float(q[0]) + __uint_as_float(q[1])) + 0.0f;
+        const int64_t s = base + 16 * wv + l;
+        if (l < 16 && s <= tl) row[s] = score;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        cur ^= 1;
+    }
+}
+
+// --------------------------------------------------- block-wide select
+// Selection of one row by a whole workgroup (1024 threads), for rows too
+// long for one wave: the proxy rows of the split scan and the member rows of
+// the split refine. Same radix select and stable emission as the wave
+// versions, with the lane prefix extended across waves through LDS.
+struct RowSelectArgs {
+    Geo geo;
+    int kind;              // 0: group rows (decode scan); 1: member rows (split refine)
+    const float *rows;     // kind 0: [B*G, Lk]; kind 1: scratch [B*G, g, c]
+    int K;                 // kind 0: c (to candidates) or topk (to member rows); kind 1: topk
+    int to_candidates;     // kind 0 only
+    int32_t *out_idx;      // rows [B, Lq, topk] or candidates [B, G, c]
+    float *out_sc;         // rows only, nullable
+    int32_t *out_count;    // candidates only, nullable
+    int out_stride;
+    const int32_t *cand;   // kind 1: [B*G, c]
+    const int32_t *cand_n; // kind 1: [B*G]
+    int c;                 // kind 1
+};
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+struct BlockShared {
+    uint32_t hist[kSelWaves][256];  // one histogram per wave (no inter-wave atomic contention)
+    int wave_sum[2][kSelWaves];
+    uint32_t bcast[4];
+};
+
+// Exclusive prefix over the block's threads of per-thread counts c0, c1 in
+// [0, 7]; returns them and the block totals.
+__device__ __forceinline__ void block_prefix2(int c0, int c1, int *p0, int *p1, int *t0, int *t1, BlockShared &sh)
+{
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    int w0, w1;
+    const int e0 = lane_prefix(c0, &w0);
+    const int e1 = lane_prefix(c1, &w1);
+    if (l == 0) {
+        sh.wave_sum[0][wv] = w0;
+        sh.wave_sum[1][wv] = w1;
+    }
+    __syncthreads();
+    int b0 = 0, b1 = 0, s0 = 0, s1 = 0;
+    for (int i = 0; i < kSelWaves; ++i) {
+        const int x0 = sh.wave_sum[0][i], x1 = sh.wave_sum[1][i];
+        if (i < wv) {
+            b0 += x0;
+            b1 += x1;
+        }
+        s0 += x0;
+        s1 += x1;
+    }
+    __syncthreads();
+    *p0 = b0 + e0;
+    *p1 = b1 + e1;
+    *t0 = s0;
+    *t1 = s1;
+}
+
+__device__ Sel block_select(const float *sc, int n, int K, BlockShared &sh)
+{
+    Sel r;
+    if (n <= K) {
+        r.all = true;
+        r.kth = 0;
+        r.quota = 0;
+        return r;
+    }
+    r.all = false;
+    const int tid = threadIdx.x, l = tid & 63;
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t remaining = static_cast<uint32_t>(K);
+    const int wv = tid >> 6;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+        __syncthreads();
+        float vn[kVec];
+        auto fetch = [&](int j0) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const int j = j0 + kVec * tid + e;
+                vn[e] = j < n ? sc[j] : 0.0f;
+            }
+        };
+        fetch(0);
+        for (int j0 = 0; j0 < n; j0 += kVec * kSelThreads) {
+            float v[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) v[e] = vn[e];
+            if (j0 + kVec * kSelThreads < n) fetch(j0 + kVec * kSelThreads);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                hist_add(j0 + kVec * tid + e < n, ord_key(v[e]), prefix, pmask, shift, sh.hist[wv], l);
+        }
+        __syncthreads();
+        if (tid < 256) {  // fold the wave histograms into wave 0's
+            uint32_t t = 0;
+            for (int i = 0; i < kSelWaves; ++i) t += sh.hist[i][tid];
+            sh.hist[0][tid] = t;
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            const uint32_t c0 = sh.hist[0][4 * l], c1 = sh.hist[0][4 * l + 1], c2 = sh.hist[0][4 * l + 2],
+                           c3 = sh.hist[0][4 * l + 3];
+            const uint32_t tot = c0 + c1 + c2 + c3;
+            uint32_t suf = tot;
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t t = __shfl_down(suf, o);
+                if (l + o < kWave) suf += t;
+            }
+            const uint32_t above = suf - tot;
+            if (above < remaining && remaining <= suf) {
+                uint32_t cum = above, dig;
+                if (cum + c3 >= remaining) {
+                    dig = 4 * l + 3;
+                } else {
+                    cum += c3;
+                    if (cum + c2 >= remaining) {
+                        dig = 4 * l + 2;
+                    } else {
+                        cum += c2;
+                        if (cum + c1 >= remaining) {
+                            dig = 4 * l + 1;
+                        } else {
+                            cum += c1;
+                            dig = 4 * l;
+                        }
+                    }
+                }
+                sh.bcast[0] = dig;
+                sh.bcast[1] = cum;
+            }
+        }
+        __syncthreads();
+        const uint32_t dig = sh.bcast[0], abv = sh.bcast[1];
+        remaining -= abv;
+        prefix |= dig << shift;
+        pmask |= 0xFFu << shift;
+        __syncthreads();
+    }
+    r.kth = prefix;
+    r.quota = static_cast<int>(remaining);
+    return r;
+}
+
+template <class F> __device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, BlockShared &sh, F &&emit)
+{
+    const int tid = threadIdx.x;
+    int eq_seen = 0, out = 0;
+    // the next chunk's loads are issued before the current chunk is processed
+    float vn[kVec];
+    int32_t pn[kVec];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int j = j0 + kVec * tid + e;
+            vn[e] = j < n ? sc[j] : 0.0f;
+            pn[e] = j < n ? (pos ? pos[j] : j) : 0;
+        }
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < n; j0 += kVec * kSelThreads) {
+        float v[kVec];
+        int32_t p[kVec];
+        bool take[kVec], eq[kVec];
+        int neq = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            v[e] = vn[e];
+            p[e] = pn[e];
+        }
+        if (j0 + kVec * kSelThreads < n) fetch(j0 + kVec * kSelThreads);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int j = j0 + kVec * tid + e;
+            const bool in = j < n;
+            const uint32_t key = ord_key(v[e]);
+            eq[e] = in && !s.all && key == s.kth;
+            take[e] = in && (s.all || key > s.kth);
+            neq += eq[e];
+        }
+        // ranks among equal keys, in position order
+        int rank, dummy, eq_tot, dummy_t;
+        block_prefix2(neq, 0, &rank, &dummy, &eq_tot, &dummy_t, sh);
+        rank += eq_seen;
+        eq_seen += eq_tot;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            if (eq[e]) {
+                take[e] = rank < s.quota;
+                ++rank;
+            }
+        }
+        int nt = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) nt += take[e];
+        int slot, d2, t_tot, d3;
+        block_prefix2(nt, 0, &slot, &d2, &t_tot, &d3, sh);
+        slot += out;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            if (take[e]) emit(slot++, p[e], v[e]);
+        }
+        out += t_tot;
+    }
+    return out;
+}
+
+constexpr int kSurvivors = 12288;  // LDS capacity of the prefilter (entries)
+constexpr int kSampleMax = 8192;   // sampled scores held in LDS
+
+__global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
+{
+    __shared__ BlockShared sh;
+    __shared__ float sel_scores[kSurvivors];
+    __shared__ int32_t sel_pos[kSurvivors];
+    const Geo &geo = a.geo;
+    const int tid = threadIdx.x;
+    if (a.kind == 0) {
+        const int64_t gid = blockIdx.x;
+        const int64_t b = gid / geo.G, m = gid % geo.G;
+        int n = static_cast<int>(geo.t_last(m) + 1);
+        const float *sc = a.rows + gid * geo.Lk;
+        const int32_t *pos = nullptr;
+
+        // Sampled prefilter: tau from every stride-th score, then a stable
+        // compaction of the scores > tau into LDS, where the exact select
+        // runs. Falls back to the full row when the survivors overflow LDS
+        // or are fewer than K (a sample that overshoots).
+        if (n > 4 * a.K && 3 * a.K <= kSurvivors) {
+            const int stride = n / kSampleMax + 1 > 16 ? n / kSampleMax + 1 : 16;
+            const int ns = (n + stride - 1) / stride;
+            float *smp = sel_scores;
+            for (int i = tid; i < ns; i += kSelThreads) smp[i] = sc[static_cast<int64_t>(i) * stride];
+            __syncthreads();
+            const float expect = static_cast<float>(a.K) * static_cast<float>(ns) / static_cast<float>(n);
+            const int r = static_cast<int>(ceilf(expect + kSampleSigmas * sqrtf(expect) + 8.0f));
+            if (r < ns) {
+                const Sel ts = block_select(smp, ns, r, sh);
+                Sel above;
+                above.all = false;
+                above.kth = ts.kth;  // keep keys strictly above the r-th sampled key
+                above.quota = 0;
+                __syncthreads();
+                const int kept = block_emit(sc, nullptr, n, above, sh, [&](int slot, int32_t p, float v) {
+                    if (slot < kSurvivors) {
+                        sel_scores[slot] = v;
+                        sel_pos[slot] = p;
+                    }
+                });
+                __syncthreads();
+                if (kept >= a.K && kept <= kSurvivors) {
+                    n = kept;
+                    sc = sel_scores;
+                    pos = sel_pos;
+                }
+            }
+        }
+        const Sel s = block_select(sc, n, a.K, sh);
+        if (a.to_candidates) {
+            int32_t *ci = a.out_idx + gid * a.out_stride;
+            const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float) { ci[slot] = p; });
+            for (int t = got + tid; t < a.out_stride; t += kSelThreads) ci[t] = -1;
+            if (a.out_count && tid == 0) a.out_count[gid] = got;
+            return;
+        }
+        const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+        const int64_t stride = a.out_stride;
+        const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float v) {
+            for (int64_t r = r0; r < r1; ++r) {
+                a.out_idx[(b * geo.Lq + r) * stride + slot] = p;
+                if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + slot] = v;
+            }
+        });
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
+                a.out_idx[(b * geo.Lq + r) * stride + t] = -1;
+                if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + t] = -INFINITY;
+            }
+        }
+        return;
+    }
+    // kind 1: member row = blockIdx.x over flat query rows
+    const int64_t row = blockIdx.x;
+    const int64_t b = row / geo.Lq, r = row % geo.Lq;
+    const int64_t m = r / geo.g;
+    const int64_t gid = b * geo.G + m;
+    const int mi = static_cast<int>(r - geo.first_row(m));
+    const int64_t t = geo.Lk - geo.Lq + r;
+    const int nc = a.cand_n[gid];
+    const int32_t *C = a.cand + gid * a.c;
+    // candidates s <= t are a prefix of C (ascending): count them
+    int cnt_le = 0;
+    for (int j0 = 0; j0 < nc; j0 += kSelThreads) {
+        const int j = j0 + tid;
+        cnt_le += (j < nc && C[j] <= t) ? 1 : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) cnt_le += __shfl_xor(cnt_le, o);
+    if ((tid & 63) == 0) sh.wave_sum[0][tid >> 6] = cnt_le;
+    __syncthreads();
+    int nvalid = 0;
+    for (int i = 0; i < kSelWaves; ++i) nvalid += sh.wave_sum[0][i];
+    __syncthreads();
+    const float *sc = a.rows + (gid * geo.g + mi) * static_cast<int64_t>(a.c);
+    const Sel s = block_select(sc, nvalid, a.K, sh);
+    int32_t *oi = a.out_idx + row * a.out_stride;
+    float *os = a.out_sc ? a.out_sc + row * a.out_stride : nullptr;
+    const int got = block_emit(sc, C, nvalid, s, sh, [&](int slot, int32_t p, float v) {
+        oi[slot] = p;
+        if (os) os[slot] = v;
+    });
+    for (int x = got + tid; x < a.out_stride; x += kSelThreads) {
+        oi[x] = -1;
+        if (os) os[x] = -INFINITY;
+    }
+}
+
 // ------------------------------------------------- exact-order scan (any)
 // One wave per group; lane l scores key base + l with the definition's exact
 // fp32 order: for each head, dot = sum_i q_i k_i (one rounding per product
@@ -779,6 +1166,8 @@ struct RefineArgs {
     float *scratch;         // [B*G, g, c]
     int32_t *out_idx;       // [B, Lq, topk]
     float *out_sc;          // nullable
+    int splits;             // > 1: workgroup (gid, split) scores one slice of C and leaves the
+                            // member selection to k_select_rows
 };
 
 // Member selection from its scratch row; candidates s <= t are exactly the
@@ -820,14 +1209,21 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
     const int nwaves = blockDim.x >> 6;
     const int wv = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
-    const int64_t gid = blockIdx.x;
+    const int64_t gid = blockIdx.x / a.splits;
+    const int split = blockIdx.x % a.splits;
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
     const int gm = static_cast<int>(r1 - r0);
     const int nc = a.cand_n[gid];
     const int32_t *C = a.cand + gid * a.c;
     const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
-    const int ntiles = (nc + NT - 1) / NT;
+    // this workgroup's tiles of C: [tile_lo, tile_hi)
+    const int ntiles_all = (nc + NT - 1) / NT;
+    const int per_split = (ntiles_all + a.splits - 1) / a.splits;
+    const int tile_lo = split * per_split;
+    const int tile_hi = tile_lo + per_split < ntiles_all ? tile_lo + per_split : ntiles_all;
+    if (tile_lo >= tile_hi) return;  // uniform over the workgroup
+    const int ntiles = tile_hi - tile_lo;
 
     // positions of the rows this lane gathers for a tile (slices wv, wv+nwaves, ...)
     auto load_pos = [&](int tile_idx, int32_t (&pos)[4]) {
@@ -863,23 +1259,21 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
         load_w<H>(a.w + (b * geo.Lq + r) * H, l, wr);
 
         int32_t pos[4], pos_next[4];
-        if (ntiles > 0) {
-            load_pos(0, pos);
-            issue_tile(0, pos);
-        }
-        if (ntiles > 1) load_pos(1, pos_next);
-        int32_t cpos = l < nc ? C[l] : 0;
+        load_pos(tile_lo, pos);
+        issue_tile(0, pos);
+        if (ntiles > 1) load_pos(tile_lo + 1, pos_next);
+        int32_t cpos = tile_lo * NT + l < nc ? C[tile_lo * NT + l] : 0;
         int nvalid = 0;
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
 
         for (int it = 0; it < ntiles; ++it) {
             const int cur = it & 1;
-            const int j = it * NT + l;
+            const int j = (tile_lo + it) * NT + l;
             const int32_t cpos_here = cpos;
             if (it + 1 < ntiles) {
                 issue_tile(cur ^ 1, pos_next);
-                if (it + 2 < ntiles) load_pos(it + 2, pos_next);
+                if (it + 2 < ntiles) load_pos(tile_lo + it + 2, pos_next);
                 cpos = (j + NT < nc) ? C[j + NT] : 0;
             }
             const float score = cur ? tile_scores<RB>(afr, wr, tile1, l) : tile_scores<RB>(afr, wr, tile0, l);
@@ -891,7 +1285,7 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile in LDS
             __syncthreads();
         }
-        if (active) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+        if (active && a.splits == 1) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
     }
 }
 
@@ -1003,7 +1397,8 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     a.scratch = L.scratch;
     a.out_idx = L.out_idx;
     a.out_sc = L.out_sc;
-    const dim3 grid(static_cast<uint32_t>(sh.B * L.G));
+    a.splits = L.splits > 1 ? L.splits : 1;
+    const dim3 grid(static_cast<uint32_t>(sh.B * L.G * a.splits));
     if (mfma_shape(sh)) {
         int nw = L.g < 8 ? L.g : 8;  // 4..8 member waves; more members loop
         if (nw < 4) nw = 4;
@@ -1013,6 +1408,46 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     } else {
         hipLaunchKernelGGL(k_refine_exact<float>, grid, dim3(256), 0, st, a);
     }
+    return hipGetLastError();
+}
+
+}  // namespace pivot
+
+namespace pivot {
+
+hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int splits, hipStream_t st)
+{
+    if (!mfma_shape(sh) || !L.rows || splits < 1) return hipErrorInvalidValue;
+    ScanArgs a{};
+    a.qsrc = L.qsrc;
+    a.wsrc = L.wsrc;
+    a.k = L.k;
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.H = sh.H;
+    a.D = sh.D;
+    a.rows = L.rows;
+    const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
+    hipLaunchKernelGGL((k_scan_split<64, 128>), grid, dim3(256), 0, st, a, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, hipStream_t st)
+{
+    RowSelectArgs a{};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.kind = L.kind;
+    a.rows = L.rows;
+    a.K = L.K;
+    a.to_candidates = L.to_candidates;
+    a.out_idx = L.out_idx;
+    a.out_sc = L.out_sc;
+    a.out_count = L.out_count;
+    a.out_stride = L.out_stride;
+    a.cand = L.cand;
+    a.cand_n = L.cand_n;
+    a.c = L.c;
+    const int64_t jobs = L.kind == 0 ? sh.B * L.G : sh.B * sh.Lq;
+    hipLaunchKernelGGL(k_select_rows, dim3(static_cast<uint32_t>(jobs)), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -98,14 +98,22 @@ MFMA_EXACT_CASES = [
 ]
 
 
+@pytest.fixture(params=["fused", "split"])
+def scan_path(request, monkeypatch):
+    """Run a test on the fused per-group scan ("fused") and on the split-key
+    scan + block selects used for few groups ("split")."""
+    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if request.param == "fused" else str(1 << 40))
+    return request.param
+
+
 @pytest.mark.parametrize("case", MFMA_EXACT_CASES, ids=[c[0] for c in MFMA_EXACT_CASES])
-def test_mfma_kernels_bitwise_on_exact_inputs(case):
+def test_mfma_kernels_bitwise_on_exact_inputs(case, scan_path):
     name, B, Lq, Lk, g, topk, c, wl = case
     q, w, k = exact_random(zlib.crc32(name.encode()) % 1000, B, Lq, Lk, 64, 128, BF16, w_levels=wl)
     _assert_bitwise(_gpu_all(q, w, k, g, topk, c), _oracle_all(q, w, k, g, topk, c))
 
 
-def test_mfma_all_equal_keys_fall_back_to_position():
+def test_mfma_all_equal_keys_fall_back_to_position(scan_path):
     L, g, topk, c = 200, 8, 16, 32
     q, w, _ = exact_random(5, 1, L, L, 64, 128, BF16)
     k = np.tile(exact_random(6, 1, 1, 1, 1, 128, BF16)[2], (1, L, 1))
@@ -119,7 +127,7 @@ def test_mfma_all_equal_keys_fall_back_to_position():
 
 
 @pytest.mark.parametrize("seed", [1, 2])
-def test_mfma_kernels_float_rule_on_gaussian_inputs(seed):
+def test_mfma_kernels_float_rule_on_gaussian_inputs(seed, scan_path):
     B, L, g, topk, c = 1, 600, 8, 24, 48
     q, w, k = gauss_random(seed, B, L, L, 64, 128, BF16)
     gpu = _gpu_all(q, w, k, g, topk, c)
@@ -211,24 +219,26 @@ def test_side_stream_and_preallocated_workspace():
         pv.index_refine(tq, tw, tk, 8, 16, 32, workspace=ws[:need // 2])
 
 
-def _striped_keys(L, seed, hot_sampled):
-    """Exact keys where the 64-key tiles at multiples of 16 (the tiles the
-    scan samples for its threshold) are all "hot" (hot_sampled=True) or all
-    "cold" (False) relative to the rest. With positive queries, hot keys score
-    far above cold ones."""
+def _striped_keys(L, seed, hot_sampled, stripe="tile"):
+    """Exact keys where the positions a threshold sample looks at are all
+    "hot" (hot_sampled=True) or all "cold" (False) relative to the rest: the
+    64-key tiles at multiples of 16 (the fused scan's sample, stripe="tile")
+    or every 16th position (the block select's sample, stripe="pos"). With
+    positive queries, hot keys score far above cold ones."""
     r = np.random.default_rng([seed, 7])
     cold = r.integers(-3, 4, size=(1, L, 128)).astype(np.float64) / 4.0
     hot = r.integers(2, 4, size=(1, L, 128)).astype(np.float64) / 4.0
-    tile = np.arange(L) // 64
-    sampled = (tile % 16) == 0
+    unit = np.arange(L) // 64 if stripe == "tile" else np.arange(L)
+    sampled = (unit % 16) == 0
     use_hot = sampled if hot_sampled else ~sampled
     k = np.where(use_hot[None, :, None], hot, cold)
     from workloads import to_storage
     return to_storage(k, BF16)
 
 
+@pytest.mark.parametrize("stripe", ["tile", "pos"])
 @pytest.mark.parametrize("hot_sampled", [True, False], ids=["sample_too_high", "sample_too_low"])
-def test_mfma_sampled_threshold_stays_exact(hot_sampled):
+def test_mfma_sampled_threshold_stays_exact(hot_sampled, stripe, scan_path):
     """The scan sets its admission threshold from every 16th tile. Keys that
     make the sample unrepresentative must still give the exact top-K: a too
     high sample forces the exact re-run, a too low one forces compactions."""
@@ -238,7 +248,7 @@ def test_mfma_sampled_threshold_stays_exact(hot_sampled):
     from workloads import to_storage
     q = to_storage(q, BF16)
     w = np.ldexp(1.0, r.integers(-3, 1, size=(1, L, 64))).astype(np.float32)
-    k = _striped_keys(L, 3, hot_sampled)
+    k = _striped_keys(L, 3, hot_sampled, stripe)
     tq, tw, tk = to_device(q, w, k)
     f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True)
     r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True)
