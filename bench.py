@@ -106,6 +106,20 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
                        f"{dt:.1f} s on {threads} threads")}
 
 
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch against mib MiB gives the factor that
+    turns those counters into HBM bytes."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +130,8 @@ def main():
     ap.add_argument("--g", type=int, default=None, help="group size (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (scales HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,6 +141,8 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        return copy_calibration(torch, args.copy_calibration)
     import sparse_attention_indexer_proxy_amd as pv
 
     W = ALL[args.workload]

@@ -105,7 +105,7 @@ struct Layout {
     bool pool;
     bool few;               // few groups: split scan into score rows + block selects
     int scan_splits, refine_splits;
-    size_t qbar, wbar, buf, rows, cand, cand_n, scratch, total;
+    size_t qbar, wbar, buf, rows, cand, cand_n, scratch, nvalid, total;
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
@@ -170,6 +170,7 @@ pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, 
         l.cand = take(groups * static_cast<size_t>(c) * sizeof(int32_t));
         l.cand_n = take(groups * sizeof(int32_t));
         l.scratch = take(groups * static_cast<size_t>(g) * static_cast<size_t>(c) * sizeof(float));
+        l.nvalid = take(static_cast<size_t>(p->batch) * static_cast<size_t>(p->lq) * sizeof(int32_t));
     }
     l.total = off;
     *L = l;
@@ -281,11 +282,33 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     rl.out_idx = indices;
     rl.out_sc = scores;
     rl.splits = L.refine_splits;
+    // MFMA refine over many groups with c <= 4096: the member selection
+    // runs as its own kernel (one wave per row), so the refine kernel's
+    // matrix work is never idle behind it. With few groups (few rows) the
+    // block-wide row select is faster: it spreads each row over 1024 lanes.
+    const bool member_kernel = pivot::mfma_shape(sh) && !L.few && pivot::member_select_slabs(c) > 0;
+    rl.finish = !member_kernel;
+    rl.row_nvalid = member_kernel ? reinterpret_cast<int32_t *>(base + L.nvalid) : nullptr;
     {
         StageTimer tm(PIVOT_STAGE_REFINE, s);
         st = hip_status(pivot::launch_refine(sh, rl, s), "refine launch");
     }
-    if (st != PIVOT_OK || rl.splits <= 1) return st;
+    if (st != PIVOT_OK) return st;
+    if (member_kernel) {
+        pivot::MemberSelectLaunch ml{};
+        ml.G = L.G;
+        ml.g = L.g;
+        ml.topk = topk;
+        ml.c = c;
+        ml.cand = cand;
+        ml.row_nvalid = rl.row_nvalid;
+        ml.scores = rl.scratch;
+        ml.out_idx = indices;
+        ml.out_sc = scores;
+        StageTimer tm(PIVOT_STAGE_SELECT, s);
+        return hip_status(pivot::launch_select_members(sh, ml, s), "member select launch");
+    }
+    if (rl.splits <= 1) return st;
     pivot::RowSelectLaunch ms{};
     ms.G = L.G;
     ms.g = L.g;

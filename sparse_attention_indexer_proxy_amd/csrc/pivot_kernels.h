@@ -43,7 +43,22 @@ struct RefineLaunch {
     float *scratch;     // [B*G, g, c]
     int32_t *out_idx;
     float *out_sc;
-    int splits;         // > 1: split C over workgroups, member selection left to launch_select_rows
+    int splits;         // > 1: split C over workgroups
+    int finish;         // splits == 1: select each member's top-k inside the refine kernel;
+                        // otherwise launch_select_members / launch_select_rows does it
+    int32_t *row_nvalid;  // [B, Lq], nullable, splits == 1: #{j : C[j] <= t} per row
+};
+
+// Per-member top-k over the re-scored candidate rows (MFMA refine, c <= 4096).
+struct MemberSelectLaunch {
+    int64_t G;
+    int g;
+    int topk, c;
+    const int32_t *cand;
+    const int32_t *row_nvalid;  // [B, Lq] from the refine launch
+    const float *scores;  // [B*G, g, c]
+    int32_t *out_idx;
+    float *out_sc;
 };
 
 // Block-wide selection of rows held in memory (few-groups path).
@@ -71,5 +86,8 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
 // Proxy score rows with the key axis split over `splits` workgroups per group.
 hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int splits, hipStream_t st);
 hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, hipStream_t st);
+// Register-resident member selection needs c <= 4096; returns its slab count or 0.
+int member_select_slabs(int c);
+hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch &L, hipStream_t st);
 
 }  // namespace pivot

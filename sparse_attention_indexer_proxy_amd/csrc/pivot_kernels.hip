@@ -56,6 +56,15 @@ __device__ __forceinline__ int mbcnt(uint64_t m)
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
+// Sum over the wave of a per-lane count in [0, 127].
+__device__ __forceinline__ int wave_total(uint32_t c)
+{
+    int t = 0;
+#pragma unroll
+    for (int bit = 0; bit < 7; ++bit) t += popc(ballot((c >> bit) & 1u)) << bit;
+    return t;
+}
+
 // Order-preserving map of a float to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t ord_key(float f)
 {
@@ -524,6 +533,66 @@ __device__ __forceinline__ float tile_scores(const bf16x8 (&afr)[RB][4], const f
     return quarter_transpose_sum(p);
 }
 
+// B fragments of one 16-key block (all four 32-dim slices).
+__device__ __forceinline__ void load_b(const uint16_t *tile, int cb, int l, bf16x8 (&bfr)[4])
+{
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) bfr[kb] = b_frag(tile, cb, kb, l);
+}
+
+template <int RB>
+__device__ __forceinline__ void mfma_regs(const bf16x8 (&afr)[RB][4], const bf16x8 (&bfr)[4], f32x4 (&acc)[RB])
+{
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr[kb], acc[rb], 0, 0, 0);
+    }
+}
+
+// Scores of keys l and 64 + l of a 128-key tile. Software-pipelined over
+// the eight 16-key blocks: block cb+2's B fragments are read from LDS while
+// block cb's MFMAs run, and block cb-1's ReLU-weighted reduction overlaps
+// them; the first half's transpose overlaps the second half's MFMAs.
+template <int RB>
+__device__ __forceinline__ void tile_scores_128(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4],
+                                                const uint16_t *tile, int l, float (&score)[2])
+{
+    f32x4 acc0[RB], acc1[RB];
+    bf16x8 b0[4], b1[4];
+    float p[8];
+    load_b(tile, 0, l, b0);
+    load_b(tile, 1, l, b1);
+    mfma_regs<RB>(afr, b0, acc0);
+    load_b(tile, 2, l, b0);
+    mfma_regs<RB>(afr, b1, acc1);
+    load_b(tile, 3, l, b1);
+    p[0] = relu_weighted<RB>(acc0, wr);
+    mfma_regs<RB>(afr, b0, acc0);
+    load_b(tile, 4, l, b0);
+    p[1] = relu_weighted<RB>(acc1, wr);
+    mfma_regs<RB>(afr, b1, acc1);
+    load_b(tile, 5, l, b1);
+    p[2] = relu_weighted<RB>(acc0, wr);
+    mfma_regs<RB>(afr, b0, acc0);
+    load_b(tile, 6, l, b0);
+    p[3] = relu_weighted<RB>(acc1, wr);
+    mfma_regs<RB>(afr, b1, acc1);
+    load_b(tile, 7, l, b1);
+    p[4] = relu_weighted<RB>(acc0, wr);
+    mfma_regs<RB>(afr, b0, acc0);
+    p[5] = relu_weighted<RB>(acc1, wr);
+    mfma_regs<RB>(afr, b1, acc1);
+    p[6] = relu_weighted<RB>(acc0, wr);
+    p[7] = relu_weighted<RB>(acc1, wr);
+    const float lo[4] = {p[0], p[1], p[2], p[3]};
+    const float hi[4] = {p[4], p[5], p[6], p[7]};
+    score[0] = quarter_transpose_sum(lo);
+    score[1] = quarter_transpose_sum(hi);
+}
+
 template <int H>
 __device__ __forceinline__ void load_a(const uint16_t *src, int l, bf16x8 (&afr)[H / 16][4])
 {
@@ -555,33 +624,69 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
 constexpr int kSampleStride = 16;     // tiles between sampled tiles (>= this)
 constexpr float kSampleSigmas = 6.0f;
 
+// Fused-scan workgroup shape: kScanWaves groups (one per wave) share each
+// 128-key tile; kScanBufs tiles are in LDS or in flight at once. The kernel
+// needs about 240 VGPRs, so a CU holds eight of its waves: one workgroup of
+// eight waves with two buffers measured faster than two workgroups of four
+// (each key tile is fetched once per eight groups instead of four) and than
+// a third buffer (L=128K, g=8: 16.4 ms vs 20.8 and 16.8).
+#ifndef PIVOT_SCAN_WAVES
+#define PIVOT_SCAN_WAVES 8
+#endif
+#ifndef PIVOT_SCAN_BUFS
+#define PIVOT_SCAN_BUFS 2
+#endif
+constexpr int kScanWaves = PIVOT_SCAN_WAVES;
+constexpr int kScanBufs = PIVOT_SCAN_BUFS;
+static_assert(kScanBufs == 2 || kScanBufs == 3, "two or three tile buffers");
+
+// Workgroup barrier without a memory fence. LDS tiles are written only by
+// global_load_lds, whose completion each wave establishes with an explicit
+// vmcnt wait before the barrier, and every wave has consumed its own LDS
+// reads of a tile before it arrives; the signal fences keep the compiler
+// from moving memory operations across the barrier.
+__device__ __forceinline__ void tile_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int H, int D, int Mode>
-__global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
+__global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
     constexpr int RB = H / 16;
-    constexpr int NT = kTileKeys;
+    constexpr int NT = 2 * kTileKeys;                     // 128 keys per tile
+    constexpr int SLICES = NT * D * 2 / 1024;             // 1 KiB slices per tile (32)
+    constexpr int SLICES_PER_WAVE = SLICES / kScanWaves;  // DMA instructions per lane per tile (4)
+    static_assert(SLICES % kScanWaves == 0, "each wave issues the same number of slices");
+    constexpr int NB = kScanBufs;
+    constexpr int AHEAD = (NB - 2) * SLICES_PER_WAVE;     // vmcnt that leaves the newer tiles in flight
 
-    // two distinct LDS objects, so the compiler can tell that the tile being
-    // read is not the one the in-flight global_load_lds is filling
+    // NB tile buffers, each its own LDS object so the compiler can tell that
+    // the tile being read is not one the in-flight DMAs are filling. Tile i
+    // of a pass lives in buffer i % NB; the DMA for tile i + NB - 1 is issued
+    // while tile i is scored.
     __shared__ __attribute__((aligned(1024))) uint16_t tile0[NT * D];
     __shared__ __attribute__((aligned(1024))) uint16_t tile1[NT * D];
-    __shared__ uint32_t hist[4][256];
+    __shared__ __attribute__((aligned(1024))) uint16_t tile2[NB == 3 ? NT * D : 8];
+    __shared__ uint32_t hist[kScanWaves][256];
 
     const Geo &geo = a.geo;
     const int wv = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
-    const int64_t nblk = (geo.G + 3) >> 2;
+    const int64_t nblk = (geo.G + kScanWaves - 1) / kScanWaves;
     const int64_t b = blockIdx.x % geo.B;
     const int64_t blk = nblk - 1 - blockIdx.x / geo.B;  // longest prefixes first
-    const int64_t m = blk * 4 + wv;
+    const int64_t m = blk * kScanWaves + wv;
     const bool active = m < geo.G;
-    const int64_t m_hi = (blk * 4 + 3 < geo.G - 1) ? blk * 4 + 3 : geo.G - 1;
+    const int64_t m_hi = (blk * kScanWaves + kScanWaves - 1 < geo.G - 1) ? blk * kScanWaves + kScanWaves - 1 : geo.G - 1;
     const int64_t wg_tlast = geo.t_last(m_hi);
     const int64_t my_tlast = active ? geo.t_last(m) : -1;
     const int ntiles = static_cast<int>(wg_tlast / NT) + 1;
     const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
-    const int64_t gid = b * geo.G + (active ? m : blk * 4);
+    const int64_t gid = b * geo.G + (active ? m : blk * kScanWaves);
 
     bf16x8 afr[RB][4];
     float wr[RB][4];
@@ -600,42 +705,89 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     }
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
-    // This lane's part of every tile load: 4 slices of 1 KiB per wave.
-    auto issue_tile = [&](int buf, int64_t base) {
+    // This lane's DMA rows for a tile: slices wv * SLICES_PER_WAVE + j.
+    int slice_off[SLICES_PER_WAVE], slice_rowi[SLICES_PER_WAVE];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int slice = wv * 4 + j;
-            int64_t s = base + slice_row(slice, l);
+    for (int j = 0; j < SLICES_PER_WAVE; ++j) {
+        const int slice = wv * SLICES_PER_WAVE + j;
+        slice_rowi[j] = slice_row(slice, l);
+        slice_off[j] = slice_col(slice, l);
+    }
+    auto issue_tile = [&](int buf, int64_t base) {
+        uint16_t *dst = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
+#pragma unroll
+        for (int j = 0; j < SLICES_PER_WAVE; ++j) {
+            int64_t s = base + slice_rowi[j];
             s = s < geo.Lk ? s : geo.Lk - 1;  // past the end: any valid row (its scores are masked)
-            const uint16_t *src = kseq + s * D + slice_col(slice, l);
-            uint16_t *dst = buf ? tile1 : tile0;
-            __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
+            const uint16_t *src = kseq + s * D + slice_off[j];
+            __builtin_amdgcn_global_load_lds((global_cptr)src,
+                                             (lds_ptr)(dst + (wv * SLICES_PER_WAVE + j) * 512), 16, 0, 0);
         }
     };
-    // One pass over tiles t0, t0 + step, ... < ntiles; fn(tile index, base
-    // position, lane's score) after each tile's scores.
-    auto pass = [&](int t0, int step, auto &&fn) {
-        if (t0 >= ntiles) return;
-        issue_tile(0, static_cast<int64_t>(t0) * NT);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        int cur = 0;
-        for (int it = t0; it < ntiles; it += step) {
+
+    // Phases of a pass over the tiles; the per-score work is chosen at run
+    // time so the tile pipeline below is compiled once.
+    enum { kPhaseRows = 0, kPhaseSample = 1, kPhaseFilter = 2, kPhaseRedo = 3 };
+    int stride = 1;
+    int nsv = 0;          // valid sampled keys (phase Sample)
+    bool redo = false;    // phase Redo: this wave repeats its selection
+    float *smp = f.bs;    // sample slots (phase Sample; the buffer is empty then)
+    auto on_score = [&](int phase, int it, int half, int64_t base, float score) {
+        const int64_t s = base + l;
+        const bool valid = s <= my_tlast;
+        if (phase == kPhaseRows) {
+            if (active && s < geo.Lk) row[s] = valid ? score : -INFINITY;
+        } else if (phase == kPhaseSample) {
+            if (active) smp[(it / stride) * NT + half * (NT / 2) + l] = valid ? score : -INFINITY;
+            nsv += popc(ballot(valid));
+        } else if (phase == kPhaseFilter) {
+            if (active) f.push(valid, score, static_cast<int32_t>(s));
+        } else {
+            if (redo) f.push(valid, score, static_cast<int32_t>(s));
+        }
+    };
+    auto pass = [&](int phase, int step) {
+        const int nt = (ntiles - 1) / step + 1;  // tiles 0, step, 2 step, ...
+        const int64_t tstep = static_cast<int64_t>(step) * NT;
+        issue_tile(0, 0);
+        if (NB == 3 && nt > 1) {
+            issue_tile(1, tstep);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | SLICES_PER_WAVE);  // tile 0 has landed, tile 1 may not
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        tile_barrier();
+        int buf = 0;
+        for (int i = 0; i < nt; ++i) {
+            const int it = i * step;
             const int64_t base = static_cast<int64_t>(it) * NT;
-            if (it + step < ntiles) issue_tile(cur ^ 1, base + static_cast<int64_t>(step) * NT);
-            const float score = cur ? tile_scores<RB>(afr, wr, tile1, l) : tile_scores<RB>(afr, wr, tile0, l);
-            fn(it, base, score);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed in LDS
-            __syncthreads();
-            cur ^= 1;
+            // the buffer of tile i + NB - 1 held tile i - 1, which every wave
+            // finished reading before the last barrier
+            const bool ahead = i + NB - 1 < nt;
+            if (ahead) issue_tile(buf == 0 ? NB - 1 : buf - 1, base + (NB - 1) * tstep);
+            float sc2[2];
+            if (buf == 0)
+                tile_scores_128<RB>(afr, wr, tile0, l, sc2);
+            else if (NB == 2 || buf == 1)
+                tile_scores_128<RB>(afr, wr, tile1, l, sc2);
+            else
+                tile_scores_128<RB>(afr, wr, tile2, l, sc2);
+            on_score(phase, it, 0, base, sc2[0]);
+            on_score(phase, it, 1, base + NT / 2, sc2[1]);
+            // tile i + 1 must be in LDS; with three buffers tile i + 2's DMAs
+            // may stay in flight (vector memory counts complete in issue
+            // order, so stores issued after them only make this wait longer)
+            if (NB == 3 && ahead)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | AHEAD);
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            tile_barrier();
+            buf = buf == NB - 1 ? 0 : buf + 1;
         }
     };
 
     if (Mode == kRows) {
-        pass(0, 1, [&](int, int64_t base, float score) {
-            const int64_t s = base + l;
-            if (active && s < geo.Lk) row[s] = s <= my_tlast ? score : -INFINITY;
-        });
+        pass(kPhaseRows, 1);
         if (!active) return;
         for (int64_t s = static_cast<int64_t>(ntiles) * NT + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
         return;
@@ -644,18 +796,11 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     // ---- phase A: sampled threshold (the buffer is empty, use it as scratch)
     const int64_t n_valid = my_tlast + 1;
     const int sample_cap_tiles = (2 * a.cap) / NT;
-    int stride = kSampleStride;
+    stride = kSampleStride;
     if ((ntiles + stride - 1) / stride > sample_cap_tiles) stride = (ntiles + sample_cap_tiles - 1) / sample_cap_tiles;
     const bool sample = ntiles * NT > 4 * a.K && sample_cap_tiles > 0;  // short prefixes: plain streaming
     if (sample) {
-        float *smp = f.bs;
-        int nsv = 0;  // valid sampled keys (wave-uniform)
-        pass(0, stride, [&](int it, int64_t base, float score) {
-            const int64_t s = base + l;
-            const bool valid = s <= my_tlast;
-            if (active) smp[(it / stride) * NT + l] = valid ? score : -INFINITY;
-            nsv += popc(ballot(valid));
-        });
+        pass(kPhaseSample, stride);
         if (active) {
             const int nslots = ((ntiles - 1) / stride + 1) * NT;
             const float expect = static_cast<float>(a.K) * static_cast<float>(nsv) / static_cast<float>(n_valid);
@@ -669,26 +814,19 @@ __global__ __launch_bounds__(256) void k_scan_mfma(ScanArgs a)
     }
 
     // ---- phase B: the full pass with the streaming filter
-    auto filter_fn = [&](int, int64_t base, float score) {
-        const int64_t s = base + l;
-        if (active) f.push(s <= my_tlast, score, static_cast<int32_t>(s));
-    };
-    pass(0, 1, filter_fn);
+    pass(kPhaseFilter, 1);
 
     // exactness guard: a group with fewer than min(K, n_valid) survivors had
     // its sampled tau set too high; the WG repeats the pass for it from -inf
     const int64_t need = n_valid < a.K ? n_valid : a.K;
     const bool failed = active && f.cnt < need;
     if (__syncthreads_or(failed)) {
-        const bool redo = failed;
+        redo = failed;
         if (redo) {
             f.cnt = 0;
             f.tau = -INFINITY;
         }
-        pass(0, 1, [&](int, int64_t base, float score) {
-            const int64_t s = base + l;
-            if (redo) f.push(s <= my_tlast, score, static_cast<int32_t>(s));
-        });
+        pass(kPhaseRedo, 1);
     }
 
     if (!active) return;
@@ -1082,6 +1220,211 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
     }
 }
 
+// ------------------------------------------------ member select (registers)
+// Eq. (9) for the rows of the MFMA refine: one wave per query row. The
+// member's re-scored candidates (at most 64 * NV of them) are held in
+// registers, entry j = 64 i + lane in kv[i] (kv = ord_key of the score).
+// The K-th largest key kth is found by bisection over the key bits: after
+// each bit the bracket [T, T + 2^bit) that holds kth is known together with
+// the number of keys inside it; once that number fits a small LDS buffer
+// those keys are compacted there and the remaining bits are resolved over
+// them alone, so the full register array is swept only for the leading
+// bits. The chosen entries are written in ascending candidate order, which
+// is ascending position because C is ascending.
+struct MemberSelectArgs {
+    Geo geo;
+    int topk, c;
+    const int32_t *cand;        // [B*G, c], ascending, -1 pad
+    const int32_t *row_nvalid;  // [B, Lq]: entries of C at or before the row's position
+    const float *scores;        // [B*G, g, c] member scores over C
+    int32_t *out_idx;           // [B, Lq, topk]
+    float *out_sc;              // nullable
+};
+
+// Raw buffer descriptor over n 32-bit entries at p (gfx9 family: fourth
+// word 0x00020000 = 32-bit data format, no swizzle); loads past the end
+// return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *p, int n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n * 4, 0x00020000);
+}
+
+constexpr int kMsWaves = 4;     // rows (one per wave) per workgroup
+constexpr int kMsMid = 1024;    // LDS keys per wave for the final bits
+constexpr int kMsChunk = 16;    // slabs of positions loaded at a time
+
+// Number of keys in kv[] that are >= x (a wave-uniform count).
+template <int N>
+__device__ __forceinline__ int count_ge(const uint32_t (&kv)[N], uint32_t x)
+{
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) n += popc(ballot(kv[i] >= x));
+    return n;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = __shfl_xor(v, o);
+        v = x > v ? x : v;
+    }
+    return v;
+}
+
+template <int NV>
+__global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelectArgs a)
+{
+    static_assert(NV >= 1 && NV <= kWave, "slab count");
+    constexpr int CH = NV < kMsChunk ? NV : kMsChunk;
+    static_assert(NV % CH == 0, "whole chunks");
+    __shared__ uint32_t mid_all[kMsWaves][kMsMid];
+    const Geo &geo = a.geo;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row addressing
+    const int l = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kMsWaves + wv;
+    if (row >= geo.B * geo.Lq) return;  // wave-uniform; the waves never synchronise
+    const int64_t b = row / geo.Lq, r = row - b * geo.Lq;
+    const int64_t m = r / geo.g;
+    const int64_t gid = b * geo.G + m;
+    const int mi = static_cast<int>(r - geo.first_row(m));
+    const int32_t *C = a.cand + gid * a.c;
+    const float *sc = a.scores + (gid * geo.g + mi) * static_cast<int64_t>(a.c);
+
+    // The score loads depend only on the row; entries past the valid
+    // prefix are masked once nvalid has arrived. Keys: 0 marks an empty
+    // slot (every float maps to a key >= 0x007FFFFF).
+    // Raw buffer loads over the row (c entries): one lane offset plus an
+    // immediate per slab, and entries past the row read as 0 without a
+    // branch, so nothing per entry outlives the loads.
+    const int nvalid = a.row_nvalid[row];
+    const __amdgpu_buffer_rsrc_t rs = row_buffer(sc, a.c);
+    const __amdgpu_buffer_rsrc_t rc = row_buffer(C, a.c);
+    uint32_t kv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) kv[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (kWave * i + l) * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) kv[i] = l < nvalid - kWave * i ? ord_key(__uint_as_float(kv[i])) : 0u;
+
+    const int K = a.topk;
+    // selected: key > kth, plus the first `quota` keys equal to kth;
+    // ties_all: every key equal to kth is selected
+    uint32_t kth = 1u;
+    int quota = 0;
+    bool ties_all = true;
+    if (nvalid > K) {
+        // invariant: kth in [T, T + 2^bit); n_lo = #{key >= T} >= K,
+        // n_hi = #{key >= T + 2^bit} < K
+        uint32_t T = 0;
+        int n_lo = nvalid, n_hi = 0;
+        int bit = 32;
+        while (bit > 0 && n_lo - n_hi > kMsMid) {
+            --bit;
+            const uint32_t x = T | (1u << bit);
+            const int n = count_ge(kv, x);
+            if (n >= K) {
+                T = x;
+                n_lo = n;
+            } else {
+                n_hi = n;
+            }
+            if ((bit & 7) == 0 && bit > 0 && n_lo - n_hi > kMsMid) {
+                // a bracket that stays crowded may hold one repeated key
+                // (e.g. many exact zeros): if its largest key has every
+                // bracket key at or above it, that key is kth
+                uint32_t top = 0;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const bool in = kv[i] != 0u && (kv[i] >> bit) == (T >> bit);
+                    top = in && kv[i] > top ? kv[i] : top;
+                }
+                top = wave_max_u32(top);
+                if (count_ge(kv, top) == n_lo) {
+                    T = top;
+                    bit = 0;
+                }
+            }
+        }
+        if (bit > 0) {
+            // compact the keys of the bracket into LDS, then finish there
+            uint32_t *mid = mid_all[wv];
+            int nm = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const bool in = kv[i] != 0u && (bit == 32 || (kv[i] >> bit) == (T >> bit));
+                const uint64_t im = ballot(in);
+                if (in) mid[nm + mbcnt(im)] = kv[i];
+                nm += popc(im);
+            }
+            wave_fence();
+            uint32_t mv[kMsMid / kWave];
+#pragma unroll
+            for (int q = 0; q < kMsMid / kWave; ++q) {
+                const int j = kWave * q + l;
+                mv[q] = j < nm ? mid[j] : 0u;
+            }
+            // n_hi counts the keys above the compacted bracket
+            while (bit > 0) {
+                --bit;
+                const uint32_t x = T | (1u << bit);
+                if (n_hi + count_ge(mv, x) >= K) T = x;
+            }
+        }
+        kth = T;
+        const int n_gt = T == 0xFFFFFFFFu ? 0 : count_ge(kv, T + 1u);
+        const int n_eq = count_ge(kv, T) - n_gt;
+        quota = K - n_gt;
+        ties_all = quota == n_eq;
+    }
+
+    // ordered emission; the next chunk of positions is loaded while the
+    // current one is written
+    int32_t *oi = a.out_idx + row * a.topk;
+    float *os = a.out_sc ? a.out_sc + row * a.topk : nullptr;
+    int out = 0, eq_seen = 0;
+    int32_t cv[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) cv[e] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(rc, (kWave * e + l) * 4, 0, 0));
+#pragma unroll
+    for (int i0 = 0; i0 < NV; i0 += CH) {
+        if (kWave * i0 >= nvalid) break;
+        int32_t cn[CH];
+        if (i0 + CH < NV) {
+#pragma unroll
+            for (int e = 0; e < CH; ++e)
+                cn[e] = static_cast<int32_t>(
+                    __builtin_amdgcn_raw_buffer_load_b32(rc, (kWave * (i0 + CH + e) + l) * 4, 0, 0));
+        }
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const uint32_t key = kv[i0 + e];
+            bool take = key >= kth;  // kth >= 1, so empty slots never qualify
+            if (!ties_all) {
+                const bool eq = key == kth;
+                const uint64_t em = ballot(eq);
+                const int rank = eq_seen + mbcnt(em);
+                eq_seen += popc(em);
+                take = key > kth || (eq && rank < quota);
+            }
+            const uint64_t tm = ballot(take);
+            if (take) {
+                const int slot = out + mbcnt(tm);
+                oi[slot] = cv[e];
+                if (os) os[slot] = key_float(key);
+            }
+            out += popc(tm);
+        }
+        if (i0 + CH < NV) {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) cv[e] = cn[e];
+        }
+    }
+    for (int x = out + l; x < K; x += kWave) {
+        oi[x] = -1;
+        if (os) os[x] = -INFINITY;
+    }
+}
+
 // ------------------------------------------------- exact-order scan (any)
 // One wave per group; lane l scores key base + l with the definition's exact
 // fp32 order: for each head, dot = sum_i q_i k_i (one rounding per product
@@ -1166,8 +1509,10 @@ struct RefineArgs {
     float *scratch;         // [B*G, g, c]
     int32_t *out_idx;       // [B, Lq, topk]
     float *out_sc;          // nullable
-    int splits;             // > 1: workgroup (gid, split) scores one slice of C and leaves the
-                            // member selection to k_select_rows
+    int splits;             // > 1: workgroup (gid, split) scores one slice of C
+    int finish;             // select each member's top-k in this kernel (splits == 1 only);
+                            // otherwise k_select_members / k_select_rows does it
+    int32_t *row_nvalid;    // [B, Lq], nullable (splits == 1): #{j : C[j] <= t} per row
 };
 
 // Member selection from its scratch row; candidates s <= t are exactly the
@@ -1285,7 +1630,8 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile in LDS
             __syncthreads();
         }
-        if (active && a.splits == 1) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+        if (active && a.row_nvalid && l == 0) a.row_nvalid[b * geo.Lq + r] = nvalid;
+        if (active && a.finish) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
     }
 }
 
@@ -1363,10 +1709,12 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
     const bool rows = L.rows != nullptr;
     if (mfma_shape(sh)) {
+        const dim3 mgrid(static_cast<uint32_t>(sh.B * ((L.G + kScanWaves - 1) / kScanWaves)));
+        const dim3 mblock(kScanWaves * 64);
         if (rows)
-            hipLaunchKernelGGL((k_scan_mfma<64, 128, kRows>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((k_scan_mfma<64, 128, kRows>), mgrid, mblock, 0, st, a);
         else
-            hipLaunchKernelGGL((k_scan_mfma<64, 128, kFilter>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((k_scan_mfma<64, 128, kFilter>), mgrid, mblock, 0, st, a);
     } else if (sh.bf16) {
         if (rows)
             hipLaunchKernelGGL((k_scan_exact<uint16_t, kRows>), grid, block, 0, st, a);
@@ -1398,6 +1746,8 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     a.out_idx = L.out_idx;
     a.out_sc = L.out_sc;
     a.splits = L.splits > 1 ? L.splits : 1;
+    a.finish = a.splits == 1 && L.finish;
+    a.row_nvalid = a.splits == 1 ? L.row_nvalid : nullptr;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * a.splits));
     if (mfma_shape(sh)) {
         int nw = L.g < 8 ? L.g : 8;  // 4..8 member waves; more members loop
@@ -1428,6 +1778,36 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.rows = L.rows;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
     hipLaunchKernelGGL((k_scan_split<64, 128>), grid, dim3(256), 0, st, a, splits);
+    return hipGetLastError();
+}
+
+int member_select_slabs(int c)
+{
+    for (int nv : {8, 16, 32, 64})
+        if (c <= kWave * nv) return nv;
+    return 0;
+}
+
+hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch &L, hipStream_t st)
+{
+    MemberSelectArgs a{};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.topk = L.topk;
+    a.c = L.c;
+    a.cand = L.cand;
+    a.row_nvalid = L.row_nvalid;
+    a.scores = L.scores;
+    a.out_idx = L.out_idx;
+    a.out_sc = L.out_sc;
+    const int64_t rows = sh.B * sh.Lq;
+    const dim3 grid(static_cast<uint32_t>((rows + kMsWaves - 1) / kMsWaves)), block(kMsWaves * kWave);
+    switch (member_select_slabs(L.c)) {
+    case 8: hipLaunchKernelGGL(k_select_members<8>, grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL(k_select_members<16>, grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL(k_select_members<32>, grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_select_members<64>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
