@@ -77,6 +77,31 @@ def recorded_traffic(workload_name, variant, g):
     return ent.get("hbm_bytes_per_launch")
 
 
+def practical_peaks():
+    """Run the in-tree probe (dense bf16 MFMA loop with random and with zero
+    operands, and a 2 GiB device copy); None if it is not built."""
+    import subprocess
+    probe = os.path.join(ROOT, "sparse_attention_indexer_proxy_amd", "mfma_probe")
+    if not os.path.exists(probe):
+        return None
+    try:
+        res = subprocess.run([probe, "0.5"], capture_output=True, text=True, timeout=120)
+        return json.loads(res.stdout.strip().splitlines()[-1]) if res.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(q, w, k, W, variant, g, budget_s):
     """The oracle on a stratified sample of groups (rows for dense), sized to
     about budget_s seconds; returns the metric-unit rate."""
@@ -100,7 +125,7 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
     run(units)
     dt = time.perf_counter() - t0
     return {"value": len(units) * rows_per_unit / dt, "unit": "query positions/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": (f"{len(units)} of {per_seq * W.B} {'rows' if variant == 'dense' else 'groups'} "
                        f"evenly spaced over the sequence (same mean prefix as the full workload), "
                        f"{dt:.1f} s on {threads} threads")}
@@ -188,6 +213,19 @@ def main():
     pv.timing_enable(False)
     del out
 
+    # per-call durations from hipEvents around each ABI call on its stream
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        out = step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    median_call_ms = call_ms[len(call_ms) // 2]
+    del out
+    practical = practical_peaks()
+
     ms_per_step = 1e3 * wall / args.steps
     qpos = W.B * W.Lq
     value = qpos / (wall / args.steps)
@@ -226,6 +264,10 @@ def main():
                      "kernel": "proxy scan + top-K selection (k_scan_mfma)",
                      "flops_per_launch": sflops},
         "cpu_baseline": cpu,
+        "median_call_ms": median_call_ms,
+        "practical_peak": practical,
+        "scan_frac_of_practical_mfma": (achieved / practical["mfma_bf16_random_tflops"]
+                                        if practical and practical.get("mfma_bf16_random_tflops") else None),
         "kernels_ms_per_launch": kernels,
         "whole_call_mfma_frac": total_flops / (wall / args.steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
     }

@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pivot_kernels.hip"), os.path.join(CSRC, "pivot_api.hip")]
 LIB = os.path.join(PKG, "libpivot.so")
+PROBE_SRC = os.path.join(CSRC, "mfma_probe.hip")
+PROBE = os.path.join(PKG, "mfma_probe")  # practical MFMA / copy ceilings (measurement only)
 ARCH = os.environ.get("PIVOT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -33,9 +35,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpivot.so)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def _run_hipcc(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
@@ -43,7 +43,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build_probe(verbose: bool = False) -> str:
+    tmp = PROBE + ".tmp"
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    _run_hipcc([hipcc(), *flags, PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    tmp = LIB + ".tmp"
+    _run_hipcc([hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -621,7 +621,7 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
 // about 1.5 K survivors instead of c (1 + ln(n / c)). If a group still ends
 // with fewer than K survivors the WG repeats the pass for it with tau = -inf,
 // so the selection is exact whatever the sample shows.
-constexpr int kSampleStride = 16;     // tiles between sampled tiles (>= this)
+constexpr int kSampleStride = 32;     // tiles between sampled tiles (>= this)
 constexpr float kSampleSigmas = 6.0f;
 
 // Fused-scan workgroup shape: kScanWaves groups (one per wave) share each
