@@ -20,6 +20,7 @@ _SRC = os.path.join(_HERE, "pivot_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_pivot_oracle.so")
 
 DENSE, REUSE, REFINE = 0, 1, 2
+AGGREGATIONS = {"mean": 0, "first": 1, "last": 2}
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
@@ -54,10 +55,16 @@ def load(path: str | None = None):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.oracle_run.argtypes = [P, i32, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_run.restype = ctypes.c_int
+    lib.oracle_run2.argtypes = [P, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_run2.restype = ctypes.c_int
     lib.oracle_pool.argtypes = [P, i32, vp, vp, vp, vp]
     lib.oracle_pool.restype = ctypes.c_int
+    lib.oracle_pool2.argtypes = [P, i32, i32, vp, vp, vp, vp]
+    lib.oracle_pool2.restype = ctypes.c_int
     lib.oracle_proxy_row.argtypes = [P, i32, vp, vp, vp, i64, i64, vp]
     lib.oracle_proxy_row.restype = ctypes.c_int
+    lib.oracle_proxy_row2.argtypes = [P, i32, i32, vp, vp, vp, i64, i64, vp]
+    lib.oracle_proxy_row2.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -96,11 +103,19 @@ def groups_of(Lq: int, g: int) -> int:
     return -(-Lq // g)
 
 
+def _agg(agg) -> int:
+    if agg not in AGGREGATIONS:
+        raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}")
+    return AGGREGATIONS[agg]
+
+
 def run(variant: int, q, w, k, topk: int, g: int = 1, c: int = 0, units=None, cand_in=None,
-        cand_in_n=None, want_scores=True, want_cand=True, lib_path=None):
+        cand_in_n=None, want_scores=True, want_cand=True, lib_path=None, agg="mean", member_causal=False):
     """Run one variant. Returns a dict with 'indices', 'scores' (or None),
     'cand'/'cand_n' (Refine), 'counters' = (proxy, refine, dense) dot counts.
-    Rows outside the requested ``units`` stay at -2 (indices) / nan (scores)."""
+    Rows outside the requested ``units`` stay at -2 (indices) / nan (scores).
+    ``agg`` picks the proxy (mean of eq. (4), or the first / last member);
+    ``member_causal`` (Reuse) bounds each member's top-k by its own t."""
     q, w, k = _c(q), _c(w), _c(k)
     prob = _problem(q, w, k)
     B, Lq = prob.B, prob.Lq
@@ -121,9 +136,10 @@ def run(variant: int, q, w, k, topk: int, g: int = 1, c: int = 0, units=None, ca
         if cand_in.shape != (B, G, c) or cand_in_n.shape != (B, G):
             raise ValueError("cand_in must be [B, G, c] and cand_in_n [B, G]")
     counters = np.zeros(3, dtype=np.float64)
-    rc = load(lib_path).oracle_run(ctypes.byref(prob), variant, g, topk, c, _ptr(q), _ptr(w), _ptr(k),
-                                   _ptr(u), 0 if u is None else len(u), _ptr(idx), _ptr(sc), _ptr(cand),
-                                   _ptr(cand_n), _ptr(cand_in), _ptr(cand_in_n), _ptr(counters))
+    rc = load(lib_path).oracle_run2(ctypes.byref(prob), variant, g, topk, c, _agg(agg), int(bool(member_causal)),
+                                    _ptr(q), _ptr(w), _ptr(k), _ptr(u), 0 if u is None else len(u), _ptr(idx),
+                                    _ptr(sc), _ptr(cand), _ptr(cand_n), _ptr(cand_in), _ptr(cand_in_n),
+                                    _ptr(counters))
     if rc != 0:
         raise ValueError(f"oracle_run failed with code {rc}")
     return {"indices": idx, "scores": sc, "cand": cand, "cand_n": cand_n,
@@ -145,8 +161,9 @@ def refine(q, w, k, g, topk, c, groups=None, **kw):
     return run(REFINE, q, w, k, topk, g, c, units=groups, **kw)
 
 
-def pool(q, w, g, lib_path=None):
-    """eq. (4): (qbar [B,G,H,d] float32 holding q-dtype values, wbar [B,G,H])."""
+def pool(q, w, g, lib_path=None, agg="mean"):
+    """eq. (4): (qbar [B,G,H,d] float32 holding q-dtype values, wbar [B,G,H]).
+    ``agg`` = "first" / "last" takes that member's q and w instead."""
     q, w = _c(q), _c(w)
     B, Lq, H, d = q.shape
     k_stub = np.zeros((B, Lq, d), dtype=q.dtype)
@@ -154,20 +171,21 @@ def pool(q, w, g, lib_path=None):
     G = groups_of(Lq, g)
     qbar = np.empty((B, G, H, d), dtype=np.float32)
     wbar = np.empty((B, G, H), dtype=np.float32)
-    rc = load(lib_path).oracle_pool(ctypes.byref(prob), g, _ptr(q), _ptr(w), _ptr(qbar), _ptr(wbar))
+    rc = load(lib_path).oracle_pool2(ctypes.byref(prob), g, _agg(agg), _ptr(q), _ptr(w), _ptr(qbar), _ptr(wbar))
     if rc != 0:
         raise ValueError(f"oracle_pool failed with code {rc}")
     return qbar, wbar
 
 
-def proxy_row(q, w, k, g, b, m, lib_path=None):
+def proxy_row(q, w, k, g, b, m, lib_path=None, agg="mean"):
     """eq. (5): the proxy score row of group m of sequence b over s <= t_last."""
     q, w, k = _c(q), _c(w), _c(k)
     prob = _problem(q, w, k)
     last = min((m + 1) * g, prob.Lq) - 1
     t_last = prob.Lk - prob.Lq + last
     out = np.empty(t_last + 1, dtype=np.float32)
-    rc = load(lib_path).oracle_proxy_row(ctypes.byref(prob), g, _ptr(q), _ptr(w), _ptr(k), b, m, _ptr(out))
+    rc = load(lib_path).oracle_proxy_row2(ctypes.byref(prob), g, _agg(agg), _ptr(q), _ptr(w), _ptr(k), b, m,
+                                          _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_proxy_row failed with code {rc}")
     return out

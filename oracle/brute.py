@@ -8,7 +8,9 @@ with ``numpy.lexsort``, where the oracle loops in float32 and selects with
 
 Equations from the PIVOT paper summary page (picx.dev): eq. (1) indexer score,
 eq. (4) mean-pool proxy, eq. (5) proxy scan, eq. (6) Reuse, eq. (7) candidate
-set, eqs. (8)-(9) Refine.
+set, eqs. (8)-(9) Refine; section "Ablation Studies" for the first / last
+query proxies, and eq. (6) with each member's own bound for member-causal
+Reuse.
 """
 from __future__ import annotations
 
@@ -45,8 +47,9 @@ def _emit(out_i, out_s, row, chosen, sc, topk):
     out_s[row, n:] = -np.inf
 
 
-def proxy(q, w, g, dtype):
-    """eq. (4) per sequence: float64 mean, then rounded like the q storage."""
+def proxy(q, w, g, dtype, agg="mean"):
+    """eq. (4) per sequence: float64 mean, then rounded like the q storage;
+    agg "first" / "last" takes that member's q and w as they are."""
     B, Lq, H, d = q.shape
     G = -(-Lq // g)
     qf, wf = _f64(q, dtype), np.asarray(w, np.float64)
@@ -54,6 +57,11 @@ def proxy(q, w, g, dtype):
     wbar = np.empty((B, G, H))
     for m in range(G):
         sl = slice(m * g, min((m + 1) * g, Lq))
+        if agg in ("first", "last"):
+            r = sl.start if agg == "first" else sl.stop - 1
+            qbar[:, m] = qf[:, r]
+            wbar[:, m] = wf[:, r]
+            continue
         qm = qf[:, sl].sum(axis=1) / (sl.stop - sl.start)
         qm32 = qm.astype(np.float32)
         if dtype == BF16:
@@ -79,10 +87,10 @@ def dense(q, w, k, topk, dtype):
     return idx, sco
 
 
-def reuse(q, w, k, g, topk, dtype):
+def reuse(q, w, k, g, topk, dtype, agg="mean", member_causal=False):
     B, Lq, H, d = q.shape
     Lk = k.shape[1]
-    qbar, wbar = proxy(q, w, g, dtype)
+    qbar, wbar = proxy(q, w, g, dtype, agg)
     kf = _f64(k, dtype)
     idx = np.empty((B, Lq, topk), np.int64)
     sco = np.empty((B, Lq, topk))
@@ -94,15 +102,18 @@ def reuse(q, w, k, g, topk, dtype):
             t_last = Lk - Lq + rows[-1]
             ch, sc = select(Ibar[m, :t_last + 1], pos[:t_last + 1], topk)
             for r in rows:
+                if member_causal:
+                    t = Lk - Lq + r
+                    ch, sc = select(Ibar[m, :t + 1], pos[:t + 1], topk)
                 _emit(idx[b], sco[b], r, ch, sc, topk)
     return idx, sco
 
 
-def refine(q, w, k, g, topk, c, dtype):
+def refine(q, w, k, g, topk, c, dtype, agg="mean"):
     """Returns (indices, scores, candidate sets as a list of arrays)."""
     B, Lq, H, d = q.shape
     Lk = k.shape[1]
-    qbar, wbar = proxy(q, w, g, dtype)
+    qbar, wbar = proxy(q, w, g, dtype, agg)
     qf, wf, kf = _f64(q, dtype), np.asarray(w, np.float64), _f64(k, dtype)
     idx = np.empty((B, Lq, topk), np.int64)
     sco = np.empty((B, Lq, topk))

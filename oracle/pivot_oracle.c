@@ -30,6 +30,14 @@
  *     (scores: the matching values, then -inf);
  *   - |C| = min(c, t_last + 1), and a Refine row keeps min(k, |C with s<=t|).
  *
+ * Variant knobs (section "Ablation Studies", proxy aggregation, and the
+ * per-member reading of eq. (6)):
+ *   - aggregation: the proxy is the per-head mean of eq. (4) (default), or
+ *     the first or the last member's own q and w, unchanged;
+ *   - member-causal Reuse: every member at t keeps the proxy's top-k over
+ *     s <= t (eq. (6) with the member's own bound) instead of the group's
+ *     one row over s <= t_last.
+ *
  * Positions: query row r of a sequence sits at position Lk - Lq + r.
  */
 #include <math.h>
@@ -49,6 +57,7 @@ typedef struct {
 
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_NO_MEM = 2 };
 enum { VAR_DENSE = 0, VAR_REUSE = 1, VAR_REFINE = 2 };
+enum { AGG_MEAN = 0, AGG_FIRST = 1, AGG_LAST = 2 };
 
 /* ---------------------------------------------------------------- storage */
 static float widen(const void *base, int dtype, int64_t i)
@@ -184,23 +193,45 @@ static void pool_group(const oracle_problem *p, int g, const void *q, const floa
     }
 }
 
-int oracle_pool(const oracle_problem *p, int32_t g, const void *q, const float *w, float *qbar_out,
-                float *wbar_out)
+/* The proxy of group m under an aggregation: the mean of eq. (4), or one
+ * member's (first or last) q and w taken as they are. */
+static void proxy_of_group(const oracle_problem *p, int g, int agg, const void *q, const float *w, int64_t b,
+                           int64_t m, float *qbar, float *wbar)
+{
+    int64_t r0 = m * g, r1 = r0 + g < p->Lq ? r0 + g : p->Lq;
+    if (agg == AGG_FIRST)
+        widen_query_row(p, q, w, b, r0, qbar, wbar);
+    else if (agg == AGG_LAST)
+        widen_query_row(p, q, w, b, r1 - 1, qbar, wbar);
+    else
+        pool_group(p, g, q, w, b, m, qbar, wbar);
+}
+
+int oracle_pool2(const oracle_problem *p, int32_t g, int32_t agg, const void *q, const float *w,
+                 float *qbar_out, float *wbar_out)
 {
     if (!check_problem(p) || g < 1 || !q || !w || !qbar_out || !wbar_out) return OR_BAD_ARG;
+    if (agg < AGG_MEAN || agg > AGG_LAST) return OR_BAD_ARG;
     int64_t G = n_groups(p, g), hd = (int64_t)p->H * p->d;
     for (int64_t b = 0; b < p->B; ++b)
         for (int64_t m = 0; m < G; ++m)
-            pool_group(p, g, q, w, b, m, qbar_out + (b * G + m) * hd, wbar_out + (b * G + m) * p->H);
+            proxy_of_group(p, g, agg, q, w, b, m, qbar_out + (b * G + m) * hd, wbar_out + (b * G + m) * p->H);
     return OR_OK;
+}
+
+int oracle_pool(const oracle_problem *p, int32_t g, const void *q, const float *w, float *qbar_out,
+                float *wbar_out)
+{
+    return oracle_pool2(p, g, AGG_MEAN, q, w, qbar_out, wbar_out);
 }
 
 /* ------------------------------------------------------------ eq. (5) */
 /* Proxy score row of one group: out[s] for s in [0, t_last]. */
-int oracle_proxy_row(const oracle_problem *p, int32_t g, const void *q, const float *w, const void *k,
-                     int64_t b, int64_t m, float *out)
+int oracle_proxy_row2(const oracle_problem *p, int32_t g, int32_t agg, const void *q, const float *w,
+                      const void *k, int64_t b, int64_t m, float *out)
 {
     if (!check_problem(p) || g < 1 || b < 0 || b >= p->B || m < 0 || m >= n_groups(p, g)) return OR_BAD_ARG;
+    if (agg < AGG_MEAN || agg > AGG_LAST) return OR_BAD_ARG;
     int64_t hd = (int64_t)p->H * p->d;
     int64_t last = (m + 1) * g - 1 < p->Lq - 1 ? (m + 1) * g - 1 : p->Lq - 1;
     int64_t t_last = p->Lk - p->Lq + last;
@@ -210,13 +241,19 @@ int oracle_proxy_row(const oracle_problem *p, int32_t g, const void *q, const fl
     if (!kf || !qbar || !wbar) {
         rc = OR_NO_MEM;
     } else {
-        pool_group(p, g, q, w, b, m, qbar, wbar);
+        proxy_of_group(p, g, agg, q, w, b, m, qbar, wbar);
         for (int64_t s = 0; s <= t_last; ++s) out[s] = index_score(p->H, p->d, qbar, wbar, kf + s * p->d);
     }
     free(kf);
     free(qbar);
     free(wbar);
     return rc;
+}
+
+int oracle_proxy_row(const oracle_problem *p, int32_t g, const void *q, const float *w, const void *k,
+                     int64_t b, int64_t m, float *out)
+{
+    return oracle_proxy_row2(p, g, AGG_MEAN, q, w, k, b, m, out);
 }
 
 /* ------------------------------------------------------------ variants */
@@ -236,14 +273,20 @@ int oracle_proxy_row(const oracle_problem *p, int32_t g, const void *q, const fl
  *             (Refine only; same layout as cand / cand_n)
  *   counters  double[3] or NULL: proxy dot products (H per scored key of a
  *             proxy), member re-score dot products, dense dot products
+ *
+ * oracle_run2 adds the variant knobs: agg (0 mean, 1 first member, 2 last
+ * member) for the proxy of Reuse and Refine, and member_causal (Reuse only:
+ * each member keeps the proxy's top-k over s <= its own t).
  */
-int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk, int32_t c, const void *q,
-               const float *w, const void *k, const int64_t *units, int64_t n_units, int32_t *indices,
-               float *scores, int32_t *cand, int32_t *cand_n, const int32_t *cand_in, const int32_t *cand_in_n,
-               double *counters)
+int oracle_run2(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk, int32_t c, int32_t agg,
+                int32_t member_causal, const void *q, const float *w, const void *k, const int64_t *units,
+                int64_t n_units, int32_t *indices, float *scores, int32_t *cand, int32_t *cand_n,
+                const int32_t *cand_in, const int32_t *cand_in_n, double *counters)
 {
     if (!check_problem(p) || !q || !w || !k || !indices || topk < 1) return OR_BAD_ARG;
     if (variant < VAR_DENSE || variant > VAR_REFINE) return OR_BAD_ARG;
+    if (agg < AGG_MEAN || agg > AGG_LAST) return OR_BAD_ARG;
+    if (member_causal && variant != VAR_REUSE) return OR_BAD_ARG;
     if (variant == VAR_DENSE) g = 1;
     if (g < 1) return OR_BAD_ARG;
     if (variant == VAR_REFINE && c < topk) return OR_BAD_ARG;
@@ -305,7 +348,7 @@ int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk
                 int64_t nc = 0; /* |C| */
 
                 if (!(variant == VAR_REFINE && cand_in)) {
-                    pool_group(p, g, q, w, b, m, qv, wv);
+                    proxy_of_group(p, g, agg, q, w, b, m, qv, wv);
                     /* eq. (5): one scan of the prefix s <= t_last */
                     for (int64_t s = 0; s <= t_last; ++s) {
                         row[s].s = index_score(p->H, p->d, qv, wv, kf + s * p->d);
@@ -314,6 +357,17 @@ int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk
                     c_proxy += (double)p->H * (double)(t_last + 1);
                 }
 
+                if (variant == VAR_REUSE && member_causal) {
+                    /* eq. (6) per member: the proxy's top-k over s <= t */
+                    for (int64_t r = r0; r < r1; ++r) {
+                        int64_t t = p->Lk - p->Lq + r;
+                        memcpy(cset, row, sizeof(scored_t) * (size_t)(t + 1));
+                        int64_t n = top_k_by_rank(cset, t + 1, topk);
+                        int64_t o = (b * p->Lq + r) * topk;
+                        write_row(indices + o, scores ? scores + o : NULL, topk, cset, n);
+                    }
+                    continue;
+                }
                 if (variant == VAR_REUSE) {
                     /* eq. (6): the proxy's top-k is every member's row */
                     int64_t n = top_k_by_rank(row, t_last + 1, topk);
@@ -378,6 +432,15 @@ int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk
         counters[2] = c_dense;
     }
     return rc;
+}
+
+int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk, int32_t c, const void *q,
+               const float *w, const void *k, const int64_t *units, int64_t n_units, int32_t *indices,
+               float *scores, int32_t *cand, int32_t *cand_n, const int32_t *cand_in, const int32_t *cand_in_n,
+               double *counters)
+{
+    return oracle_run2(p, variant, g, topk, c, AGG_MEAN, 0, q, w, k, units, n_units, indices, scores, cand, cand_n,
+                       cand_in, cand_in_n, counters);
 }
 
 int oracle_num_threads(void)

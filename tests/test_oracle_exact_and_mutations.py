@@ -124,6 +124,14 @@ MUTATIONS = {
                                    "int64_t t_last = p->Lk - p->Lq + r0;"),
     "proxy_not_rounded_to_bf16": ("qbar[i] = p->dtype == 1 ? round_to_bf16(mean) : mean;", "qbar[i] = mean;"),
     "wrong_key_row": ("kf + s * p->d);\n                        row[s].i", "kf + (s > 0 ? s - 1 : 0) * p->d);\n                        row[s].i"),
+    "member_causal_uses_group_bound": ("memcpy(cset, row, sizeof(scored_t) * (size_t)(t + 1));\n"
+                                       "                        int64_t n = top_k_by_rank(cset, t + 1, topk);",
+                                       "memcpy(cset, row, sizeof(scored_t) * (size_t)(t_last + 1));\n"
+                                       "                        int64_t n = top_k_by_rank(cset, t_last + 1, topk);"),
+    "first_member_proxy_off_by_one": ("widen_query_row(p, q, w, b, r0, qbar, wbar);",
+                                      "widen_query_row(p, q, w, b, r0 + (r1 - r0 > 1), qbar, wbar);"),
+    "last_member_proxy_is_first": ("widen_query_row(p, q, w, b, r1 - 1, qbar, wbar);",
+                                   "widen_query_row(p, q, w, b, r0, qbar, wbar);"),
 }
 
 
@@ -147,6 +155,18 @@ def _pin_battery(lib):
         np.testing.assert_array_equal(o["scores"].astype(np.float64), bs)
         o = oracle.refine(q, w, k, g, topk, c, lib_path=lib)
         bi, bs, _ = brute.refine(q, w, k, g, topk, c, dt)
+        np.testing.assert_array_equal(o["indices"], bi)
+        np.testing.assert_array_equal(o["scores"].astype(np.float64), bs)
+    # variant knobs: member proxies and member-causal Reuse
+    for (B, Lq, Lk, H, d, g, topk, c, dt) in cases[:2]:
+        q, w, k = exact_random(5, B, Lq, Lk, H, d, dt)
+        for agg in ("first", "last"):
+            o = oracle.reuse(q, w, k, g, topk, agg=agg, lib_path=lib)
+            bi, bs = brute.reuse(q, w, k, g, topk, dt, agg=agg)
+            np.testing.assert_array_equal(o["indices"], bi)
+            np.testing.assert_array_equal(o["scores"].astype(np.float64), bs)
+        o = oracle.reuse(q, w, k, g, topk, member_causal=True, lib_path=lib)
+        bi, bs = brute.reuse(q, w, k, g, topk, dt, member_causal=True)
         np.testing.assert_array_equal(o["indices"], bi)
         np.testing.assert_array_equal(o["scores"].astype(np.float64), bs)
     # ties fall back to position
