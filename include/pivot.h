@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 1
+#define PIVOT_ABI_VERSION 2
 
 typedef enum {
     PIVOT_OK = 0,
@@ -71,7 +71,19 @@ typedef enum {
 
 typedef enum { PIVOT_F32 = 0, PIVOT_BF16 = 1 } pivot_dtype;
 
-typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2 } pivot_variant;
+/* PIVOT_AUTO (pivot_index only): the short-context guardrail of the pages'
+ * efficiency results (PIVOT falls back to dense DSA at short context): dense
+ * when lk < dense_below, else the configured auto_variant. */
+typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2, PIVOT_AUTO = 3 } pivot_variant;
+
+/* How a group becomes its proxy (the pages' aggregation hyperparameter,
+ * section "Ablation Studies"): the per-head mean of eq. (4), or the first or
+ * the last member's own q and w taken unchanged. */
+typedef enum { PIVOT_AGG_MEAN = 0, PIVOT_AGG_FIRST = 1, PIVOT_AGG_LAST = 2 } pivot_aggregation;
+
+/* Default guardrail of PIVOT_AUTO: the key count below which dense (g = 1) is
+ * faster than PIVOT-Refine (g = 8, k = 2048, c = 4096) on MI355X. */
+#define PIVOT_DENSE_BELOW_DEFAULT 16384
 
 /* Problem shape. Prefill: batch = 1 (or more independent sequences), lq = lk.
  * Decode (eq. 3): lq = g rows at the last g positions of each sequence. */
@@ -106,10 +118,50 @@ pivot_status pivot_index_refine(const pivot_problem *p, const void *q, const flo
                                 int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates,
                                 int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
 
+/* One call with every knob (eqs. (1)-(9), the aggregation ablation and the
+ * guardrail). Zero-initialise the struct or start from pivot_config_init. */
+typedef struct {
+    int32_t variant;       /* pivot_variant */
+    int32_t g;             /* group size, >= 1 (Reuse, Refine) */
+    int32_t topk;          /* k, >= 1 */
+    int32_t c;             /* candidates per group, >= topk (Refine) */
+    int32_t aggregation;   /* pivot_aggregation of the proxy (Reuse, Refine) */
+    int32_t member_causal; /* 1: a Reuse member at t keeps the proxy's top-k over s <= t (eq. (6) read
+                              per member) instead of the group's one row over s <= t_last; needs
+                              topk + g - 1 <= 4096. Valid with PIVOT_REUSE, and with PIVOT_AUTO,
+                              where it applies when the call resolves to Reuse; an error with an
+                              explicit dense or Refine variant (Refine members already drop s > t) */
+    int32_t auto_variant;  /* PIVOT_AUTO: PIVOT_REUSE or PIVOT_REFINE above the guardrail */
+    int32_t reserved;      /* 0 */
+    int64_t dense_below;   /* PIVOT_AUTO: dense when lk < dense_below; 0 = PIVOT_DENSE_BELOW_DEFAULT */
+} pivot_config;
+
+/* Defaults: Refine, g = 8, topk = 2048, c = 4096, mean proxy, group rows,
+ * auto_variant = Refine, default guardrail. */
+pivot_status pivot_config_init(pivot_config *cfg);
+
+/* The variant a pivot_index call with this config runs (resolves PIVOT_AUTO). */
+pivot_status pivot_resolve_variant(const pivot_problem *p, const pivot_config *cfg, int32_t *variant);
+
+/* Bytes of workspace pivot_index needs for this config. */
+pivot_status pivot_index_workspace_size(const pivot_problem *p, const pivot_config *cfg, size_t *bytes);
+
+/* The indexer under cfg; outputs as for the three calls above. candidates /
+ * candidate_counts (may be NULL) are written only when the resolved variant is
+ * Refine. With member_causal, row t holds min(k, t + 1) entries, all s <= t. */
+pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                         const void *k, int32_t *indices, float *scores, int32_t *candidates,
+                         int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
+
 /* eq. (4) alone: qbar [batch, G, heads, dim] in the q dtype, wbar [batch, G,
  * heads] f32. Needs no workspace. */
 pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const float *w, void *qbar, float *wbar,
                         void *stream);
+
+/* pivot_pool with a pivot_aggregation (PIVOT_AGG_FIRST / LAST copy that
+ * member's q and w). */
+pivot_status pivot_pool_ex(const pivot_problem *p, int32_t g, int32_t aggregation, const void *q, const float *w,
+                           void *qbar, float *wbar, void *stream);
 
 /* eq. (5) alone, for inspection: out [batch, G, lk] f32 receives the proxy
  * score of every key s <= t_last of each group and -INFINITY after it.

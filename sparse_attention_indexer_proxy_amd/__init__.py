@@ -19,18 +19,22 @@ import os
 
 import torch
 
-__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "pool", "proxy_scores",
-           "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
-           "DENSE", "REUSE", "REFINE", "STAGES"]
+__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "resolve_variant", "pool",
+           "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
+           "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "DENSE_BELOW_DEFAULT",
+           "STAGES"]
 
-DENSE, REUSE, REFINE = 0, 1, 2
+DENSE, REUSE, REFINE, AUTO = 0, 1, 2, 3
+AGGREGATIONS = {"mean": 0, "first": 1, "last": 2}
+DENSE_BELOW_DEFAULT = 16384  # PIVOT_DENSE_BELOW_DEFAULT of the header
 _F32, _BF16 = 0, 1
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libpivot.so")
 _lib = None
 
 EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
-            "pivot_pool", "pivot_proxy_scores", "pivot_timing_enable", "pivot_timing_read",
+            "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
+            "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_timing_enable", "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
 STAGES = ("pool", "scan", "select", "refine")
 
@@ -44,6 +48,13 @@ class PivotError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("lq", ctypes.c_int64), ("lk", ctypes.c_int64),
                 ("heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Config(ctypes.Structure):
+    """pivot_config of the header."""
+    _fields_ = [("variant", ctypes.c_int32), ("g", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("c", ctypes.c_int32), ("aggregation", ctypes.c_int32), ("member_causal", ctypes.c_int32),
+                ("auto_variant", ctypes.c_int32), ("reserved", ctypes.c_int32), ("dense_below", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -65,10 +76,17 @@ def load_library(path: str | None = None):
     lib.pivot_index_dense.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.pivot_index_reuse.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.pivot_index_refine.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    C = ctypes.POINTER(Config)
+    lib.pivot_config_init.argtypes = [C]
+    lib.pivot_resolve_variant.argtypes = [P, C, ctypes.POINTER(i32)]
+    lib.pivot_index_workspace_size.argtypes = [P, C, ctypes.POINTER(sz)]
+    lib.pivot_index.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pivot_pool.argtypes = [P, i32, vp, vp, vp, vp, vp]
+    lib.pivot_pool_ex.argtypes = [P, i32, i32, vp, vp, vp, vp, vp]
     lib.pivot_proxy_scores.argtypes = [P, i32, vp, vp, vp, vp, vp]
     for name in ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
-                 "pivot_pool", "pivot_proxy_scores"):
+                 "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
+                 "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pivot_timing_enable.argtypes = [i32]
     lib.pivot_timing_enable.restype = ctypes.c_int
@@ -204,14 +222,81 @@ def index_refine(q, w, k, g: int, topk: int, c: int | None = None, *, return_sco
     return _finish(sq, *outs)
 
 
-def pool(q, w, g: int, stream=None):
-    """eq. (4): proxies qbar [B, G, H, d] (q dtype) and wbar [B, G, H] f32."""
+def make_config(variant: int = REFINE, g: int = 8, topk: int = 2048, c: int | None = None,
+                aggregation: str = "mean", member_causal: bool = False, auto_variant: int = REFINE,
+                dense_below: int = 0) -> Config:
+    """A pivot_config (c defaults to 2k; dense_below 0 = the library's
+    guardrail)."""
+    if aggregation not in AGGREGATIONS:
+        raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}")
+    cfg = Config()
+    _check(load_library().pivot_config_init(ctypes.byref(cfg)))
+    cfg.variant, cfg.g, cfg.topk = variant, g, topk
+    cfg.c = 2 * topk if c is None else c
+    cfg.aggregation = AGGREGATIONS[aggregation]
+    cfg.member_causal = 1 if member_causal else 0
+    cfg.auto_variant, cfg.dense_below = auto_variant, dense_below
+    return cfg
+
+
+def resolve_variant(B: int, Lq: int, Lk: int, H: int, D: int, dtype, cfg: Config) -> int:
+    """The variant (DENSE, REUSE or REFINE) a call with ``cfg`` runs."""
+    prob = Problem(B, Lq, Lk, H, D, _dtype_code(dtype))
+    out = ctypes.c_int32(0)
+    _check(load_library().pivot_resolve_variant(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def index(q, w, k, cfg: Config | None = None, *, return_scores: bool = False, return_candidates: bool = False,
+          workspace=None, stream=None, **knobs):
+    """The indexer under one config: ``cfg`` from ``make_config`` or the
+    same keywords (variant, g, topk, c, aggregation, member_causal,
+    auto_variant, dense_below). variant=AUTO is the short-context guardrail:
+    dense below ``dense_below`` keys, else ``auto_variant``. Candidates are
+    returned (None when the call resolved to another variant) only with
+    return_candidates."""
+    if cfg is None:
+        cfg = make_config(**knobs)
+    elif knobs:
+        raise TypeError("pass either cfg or keywords")
+    prob, q, w, k, sq = _prepare(q, w, k)
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    _check(lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    cand = cand_n = None
+    if return_candidates:
+        resolved = ctypes.c_int32(0)
+        _check(lib.pivot_resolve_variant(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(resolved)))
+        if resolved.value == REFINE:
+            G = -(-prob.lq // cfg.g)
+            cand = torch.empty((prob.batch, G, cfg.c), dtype=torch.int32, device=q.device)
+            cand_n = torch.empty((prob.batch, G), dtype=torch.int32, device=q.device)
+    _check(lib.pivot_index(ctypes.byref(prob), ctypes.byref(cfg), _ptr(q), _ptr(w), _ptr(k), _ptr(idx), _ptr(sc),
+                           _ptr(cand), _ptr(cand_n), _ptr(workspace), wsb, _stream_ptr(stream, q.device)))
+    outs = [idx]
+    if return_scores:
+        outs.append(sc)
+    if return_candidates:
+        outs += [None if cand is None else _finish(sq, cand), None if cand_n is None else _finish(sq, cand_n)]
+    return _finish(sq, *outs) if len(outs) > 1 else _finish(sq, idx)
+
+
+def pool(q, w, g: int, stream=None, aggregation: str = "mean"):
+    """eq. (4): proxies qbar [B, G, H, d] (q dtype) and wbar [B, G, H] f32.
+    aggregation "first" / "last" takes that member's q and w instead of the
+    mean."""
+    if aggregation not in AGGREGATIONS:
+        raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}")
     prob, q, w, _, sq = _prepare(q, w, q[..., 0, :] if q.dim() == 4 else q[:, 0, :])
     G = -(-prob.lq // g)
     qbar = torch.empty((prob.batch, G, prob.heads, prob.dim), dtype=q.dtype, device=q.device)
     wbar = torch.empty((prob.batch, G, prob.heads), dtype=torch.float32, device=q.device)
-    _check(load_library().pivot_pool(ctypes.byref(prob), g, _ptr(q), _ptr(w), _ptr(qbar), _ptr(wbar),
-                                     _stream_ptr(stream, q.device)))
+    _check(load_library().pivot_pool_ex(ctypes.byref(prob), g, AGGREGATIONS[aggregation], _ptr(q), _ptr(w),
+                                        _ptr(qbar), _ptr(wbar), _stream_ptr(stream, q.device)))
     return _finish(sq, qbar, wbar)
 
 

@@ -99,13 +99,22 @@ pivot::LaunchShape shape_of(const pivot_problem *p)
     return pivot::LaunchShape{p->batch, p->lq, p->lk, p->heads, p->dim, p->dtype == PIVOT_BF16};
 }
 
+// A call after PIVOT_AUTO has been resolved: variant is DENSE, REUSE or
+// REFINE, g = 1 for DENSE.
+struct Cfg {
+    int variant;
+    int32_t g, topk, c;
+    int agg;      // pivot_aggregation
+    bool causal;  // member-causal Reuse
+};
+
 struct Layout {
     int64_t G;
     int g, K, cap;
     bool pool;
     bool few;               // few groups: split scan into score rows + block selects
     int scan_splits, refine_splits;
-    size_t qbar, wbar, buf, rows, cand, cand_n, scratch, nvalid, total;
+    size_t qbar, wbar, buf, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
@@ -119,12 +128,48 @@ int64_t few_groups_threshold()
     return 256;
 }
 
-pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, int32_t c, Layout *L)
+// The short-context guardrail of PIVOT_AUTO: dense below this many keys.
+int64_t dense_below(const pivot_config *cfg)
+{
+    return cfg->dense_below > 0 ? cfg->dense_below : PIVOT_DENSE_BELOW_DEFAULT;
+}
+
+pivot_status resolve(const pivot_problem *p, const pivot_config *cfg, Cfg *out)
+{
+    if (!cfg) return fail(PIVOT_ERR_INVALID_ARG, "config is NULL");
+    pivot_status st = check_problem(p);
+    if (st != PIVOT_OK) return st;
+    Cfg c{};
+    c.variant = cfg->variant;
+    if (c.variant == PIVOT_AUTO) {
+        if (cfg->auto_variant != PIVOT_REUSE && cfg->auto_variant != PIVOT_REFINE)
+            return fail(PIVOT_ERR_INVALID_ARG, "auto_variant must be PIVOT_REUSE or PIVOT_REFINE (got %d)",
+                        cfg->auto_variant);
+        c.variant = p->lk < dense_below(cfg) ? PIVOT_DENSE : cfg->auto_variant;
+    }
+    if (c.variant < PIVOT_DENSE || c.variant > PIVOT_REFINE)
+        return fail(PIVOT_ERR_INVALID_ARG, "unknown variant %d", cfg->variant);
+    if (cfg->aggregation < PIVOT_AGG_MEAN || cfg->aggregation > PIVOT_AGG_LAST)
+        return fail(PIVOT_ERR_INVALID_ARG, "unknown aggregation %d", cfg->aggregation);
+    if (cfg->member_causal != 0 && cfg->member_causal != 1)
+        return fail(PIVOT_ERR_INVALID_ARG, "member_causal must be 0 or 1");
+    if (cfg->member_causal && cfg->variant != PIVOT_REUSE && !(cfg->variant == PIVOT_AUTO))
+        return fail(PIVOT_ERR_INVALID_ARG, "member_causal applies to PIVOT_REUSE only");
+    c.g = c.variant == PIVOT_DENSE ? 1 : cfg->g;
+    c.topk = cfg->topk;
+    c.c = c.variant == PIVOT_REFINE ? cfg->c : 0;
+    c.agg = c.variant == PIVOT_DENSE ? PIVOT_AGG_MEAN : cfg->aggregation;
+    c.causal = c.variant == PIVOT_REUSE && cfg->member_causal != 0;
+    *out = c;
+    return PIVOT_OK;
+}
+
+pivot_status plan(const pivot_problem *p, const Cfg &cfg, Layout *L)
 {
     pivot_status st = check_problem(p);
     if (st != PIVOT_OK) return st;
-    if (variant < PIVOT_DENSE || variant > PIVOT_REFINE) return fail(PIVOT_ERR_INVALID_ARG, "unknown variant %d", variant);
-    if (variant == PIVOT_DENSE) g = 1;
+    const int variant = cfg.variant;
+    const int32_t g = cfg.g, topk = cfg.topk, c = cfg.c;
     if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
     if (topk < 1 || topk > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "topk must be in [1, 2^28] (got %d)", topk);
     if (variant == PIVOT_REFINE) {
@@ -137,7 +182,18 @@ pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, 
     Layout l{};
     l.g = g;
     l.G = (p->lq + g - 1) / g;
-    l.K = variant == PIVOT_REFINE ? c : topk;
+    // scan selection size: c (Refine), k (Reuse, dense) or k + g - 1
+    // (member-causal Reuse: every member's top-k over s <= t lies in the
+    // group's top-(k + g - 1) over s <= t_last, since at most g - 1
+    // positions in (t, t_last] are dropped)
+    int64_t K = variant == PIVOT_REFINE ? c : topk;
+    if (cfg.causal) {
+        K = int64_t(topk) + g - 1;
+        if (pivot::member_select_slabs(static_cast<int>(K > kMaxSel ? kMaxSel : K)) == 0)
+            return fail(PIVOT_ERR_UNSUPPORTED, "member-causal Reuse needs topk + g - 1 <= 4096 (got %lld)",
+                        (long long)K);
+    }
+    l.K = static_cast<int>(K);
     int64_t cap = 2 * int64_t(l.K);
     if (cap < l.K + 64) cap = l.K + 64;
     cap = (cap + 63) / 64 * 64;
@@ -166,9 +222,12 @@ pivot_status plan(const pivot_problem *p, int variant, int32_t g, int32_t topk, 
         l.scan_splits = l.refine_splits = 1;
         l.buf = take(groups * 2 * cap * sizeof(float));
     }
-    if (variant == PIVOT_REFINE) {
-        l.cand = take(groups * static_cast<size_t>(c) * sizeof(int32_t));
+    if (variant == PIVOT_REFINE || cfg.causal) {
+        l.cand = take(groups * static_cast<size_t>(l.K) * sizeof(int32_t));
         l.cand_n = take(groups * sizeof(int32_t));
+    }
+    if (cfg.causal) l.cand_sc = take(groups * static_cast<size_t>(l.K) * sizeof(float));
+    if (variant == PIVOT_REFINE) {
         l.scratch = take(groups * static_cast<size_t>(g) * static_cast<size_t>(c) * sizeof(float));
         l.nvalid = take(static_cast<size_t>(p->batch) * static_cast<size_t>(p->lq) * sizeof(int32_t));
     }
@@ -183,13 +242,15 @@ pivot_status hip_status(hipError_t e, const char *what)
     return fail(PIVOT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-pivot_status run(const pivot_problem *p, int variant, const void *q, const float *w, const void *k, int32_t g,
-                 int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts,
-                 void *ws, size_t ws_bytes, void *stream)
+pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const void *k,
+                 int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts, void *ws,
+                 size_t ws_bytes, void *stream)
 {
     Layout L;
-    pivot_status st = plan(p, variant, g, topk, c, &L);
+    pivot_status st = plan(p, cfg, &L);
     if (st != PIVOT_OK) return st;
+    const int variant = cfg.variant;
+    const int32_t topk = cfg.topk, c = cfg.c;
     if (!q || !w || !k || !indices) return fail(PIVOT_ERR_INVALID_ARG, "q, w, k and indices must be non-NULL");
     if (!ws || ws_bytes < L.total)
         return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total, ws ? ws_bytes : size_t(0));
@@ -209,15 +270,18 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
         float *wbar = reinterpret_cast<float *>(base + L.wbar);
         {
             StageTimer tm(PIVOT_STAGE_POOL, s);
-            st = hip_status(pivot::launch_pool(sh, L.g, L.G, q, w, qbar, wbar, s), "pool launch");
+            st = hip_status(pivot::launch_pool(sh, L.g, L.G, q, w, qbar, wbar, cfg.agg, s), "pool launch");
         }
         if (st != PIVOT_OK) return st;
         qsrc = qbar;
         wsrc = wbar;
     }
 
-    int32_t *cand = candidates ? candidates : reinterpret_cast<int32_t *>(base + L.cand);
-    int32_t *cand_n = cand_counts ? cand_counts : reinterpret_cast<int32_t *>(base + L.cand_n);
+    const bool to_cand = variant == PIVOT_REFINE || cfg.causal;
+    int32_t *cand = (variant == PIVOT_REFINE && candidates) ? candidates : reinterpret_cast<int32_t *>(base + L.cand);
+    int32_t *cand_n =
+        (variant == PIVOT_REFINE && cand_counts) ? cand_counts : reinterpret_cast<int32_t *>(base + L.cand_n);
+    float *cand_sc = cfg.causal ? reinterpret_cast<float *>(base + L.cand_sc) : nullptr;
 
     pivot::ScanLaunch sl{};
     sl.qsrc = qsrc;
@@ -228,11 +292,11 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     sl.K = L.K;
     sl.cap = L.cap;
     sl.buf = L.few ? nullptr : reinterpret_cast<float *>(base + L.buf);
-    if (variant == PIVOT_REFINE) {
+    if (to_cand) {
         sl.out_idx = cand;
-        sl.out_sc = nullptr;
+        sl.out_sc = cand_sc;
         sl.out_count = cand_n;
-        sl.out_stride = c;
+        sl.out_stride = L.K;
         sl.to_candidates = 1;
     } else {
         sl.out_idx = indices;
@@ -266,7 +330,27 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
         StageTimer tm(PIVOT_STAGE_SCAN, s);
         st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
     }
-    if (st != PIVOT_OK || variant != PIVOT_REFINE) return st;
+    if (st != PIVOT_OK) return st;
+
+    if (cfg.causal) {
+        // eq. (6) per member: each member's top-k of the shared proxy
+        // scores over the candidates s <= t
+        pivot::MemberSelectLaunch ml{};
+        ml.G = L.G;
+        ml.g = L.g;
+        ml.topk = topk;
+        ml.c = L.K;
+        ml.cand = cand;
+        ml.cand_n = cand_n;
+        ml.row_nvalid = nullptr;
+        ml.scores = cand_sc;
+        ml.shared = 1;
+        ml.out_idx = indices;
+        ml.out_sc = scores;
+        StageTimer tm(PIVOT_STAGE_SELECT, s);
+        return hip_status(pivot::launch_select_members(sh, ml, s), "member select launch");
+    }
+    if (variant != PIVOT_REFINE) return st;
 
     pivot::RefineLaunch rl{};
     rl.q = q;
@@ -301,8 +385,10 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
         ml.topk = topk;
         ml.c = c;
         ml.cand = cand;
+        ml.cand_n = cand_n;
         ml.row_nvalid = rl.row_nvalid;
         ml.scores = rl.scratch;
+        ml.shared = 0;
         ml.out_idx = indices;
         ml.out_sc = scores;
         StageTimer tm(PIVOT_STAGE_SELECT, s);
@@ -325,6 +411,18 @@ pivot_status run(const pivot_problem *p, int variant, const void *q, const float
     return hip_status(pivot::launch_select_rows(sh, ms, s), "member select launch");
 }
 
+Cfg basic(int variant, int32_t g, int32_t topk, int32_t c)
+{
+    Cfg cfg{};
+    cfg.variant = variant;
+    cfg.g = variant == PIVOT_DENSE ? 1 : g;
+    cfg.topk = topk;
+    cfg.c = variant == PIVOT_REFINE ? c : 0;
+    cfg.agg = PIVOT_AGG_MEAN;
+    cfg.causal = false;
+    return cfg;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,8 +431,9 @@ pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32
                                   size_t *bytes)
 {
     if (!bytes) return fail(PIVOT_ERR_INVALID_ARG, "bytes is NULL");
+    if (variant < PIVOT_DENSE || variant > PIVOT_REFINE) return fail(PIVOT_ERR_INVALID_ARG, "unknown variant %d", variant);
     Layout L;
-    pivot_status st = plan(p, variant, g, topk, c, &L);
+    pivot_status st = plan(p, basic(variant, g, topk, c), &L);
     if (st != PIVOT_OK) return st;
     *bytes = L.total;
     return PIVOT_OK;
@@ -343,38 +442,95 @@ pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32
 pivot_status pivot_index_dense(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t topk,
                                int32_t *indices, float *scores, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run(p, PIVOT_DENSE, q, w, k, 1, topk, 0, indices, scores, nullptr, nullptr, workspace, workspace_bytes,
-               stream);
+    return run(p, basic(PIVOT_DENSE, 1, topk, 0), q, w, k, indices, scores, nullptr, nullptr, workspace,
+               workspace_bytes, stream);
 }
 
 pivot_status pivot_index_reuse(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
                                int32_t topk, int32_t *indices, float *scores, void *workspace, size_t workspace_bytes,
                                void *stream)
 {
-    return run(p, PIVOT_REUSE, q, w, k, g, topk, 0, indices, scores, nullptr, nullptr, workspace, workspace_bytes,
-               stream);
+    return run(p, basic(PIVOT_REUSE, g, topk, 0), q, w, k, indices, scores, nullptr, nullptr, workspace,
+               workspace_bytes, stream);
 }
 
 pivot_status pivot_index_refine(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
                                 int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates,
                                 int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run(p, PIVOT_REFINE, q, w, k, g, topk, c, indices, scores, candidates, candidate_counts, workspace,
+    return run(p, basic(PIVOT_REFINE, g, topk, c), q, w, k, indices, scores, candidates, candidate_counts, workspace,
                workspace_bytes, stream);
+}
+
+pivot_status pivot_config_init(pivot_config *cfg)
+{
+    if (!cfg) return fail(PIVOT_ERR_INVALID_ARG, "config is NULL");
+    std::memset(cfg, 0, sizeof *cfg);
+    cfg->variant = PIVOT_REFINE;
+    cfg->g = 8;
+    cfg->topk = 2048;
+    cfg->c = 4096;
+    cfg->aggregation = PIVOT_AGG_MEAN;
+    cfg->member_causal = 0;
+    cfg->auto_variant = PIVOT_REFINE;
+    cfg->dense_below = 0;
+    return PIVOT_OK;
+}
+
+pivot_status pivot_resolve_variant(const pivot_problem *p, const pivot_config *cfg, int32_t *variant)
+{
+    if (!variant) return fail(PIVOT_ERR_INVALID_ARG, "variant is NULL");
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    *variant = c.variant;
+    return PIVOT_OK;
+}
+
+pivot_status pivot_index_workspace_size(const pivot_problem *p, const pivot_config *cfg, size_t *bytes)
+{
+    if (!bytes) return fail(PIVOT_ERR_INVALID_ARG, "bytes is NULL");
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    Layout L;
+    st = plan(p, c, &L);
+    if (st != PIVOT_OK) return st;
+    *bytes = L.total;
+    return PIVOT_OK;
+}
+
+pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                         const void *k, int32_t *indices, float *scores, int32_t *candidates,
+                         int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    return run(p, c, q, w, k, indices, scores, candidates, candidate_counts, workspace, workspace_bytes, stream);
 }
 
 pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const float *w, void *qbar, float *wbar,
                         void *stream)
 {
+    return pivot_pool_ex(p, g, PIVOT_AGG_MEAN, q, w, qbar, wbar, stream);
+}
+
+pivot_status pivot_pool_ex(const pivot_problem *p, int32_t g, int32_t aggregation, const void *q, const float *w,
+                           void *qbar, float *wbar, void *stream)
+{
     pivot_status st = check_problem(p);
     if (st != PIVOT_OK) return st;
     if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
+    if (aggregation < PIVOT_AGG_MEAN || aggregation > PIVOT_AGG_LAST)
+        return fail(PIVOT_ERR_INVALID_ARG, "unknown aggregation %d", aggregation);
     if (!q || !w || !qbar || !wbar) return fail(PIVOT_ERR_INVALID_ARG, "q, w, qbar and wbar must be non-NULL");
     if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(qbar) % 16 != 0)
         return fail(PIVOT_ERR_INVALID_ARG, "q and qbar must be 16-byte aligned");
     const int64_t G = (p->lq + g - 1) / g;
-    return hip_status(pivot::launch_pool(shape_of(p), g, G, q, w, qbar, wbar, static_cast<hipStream_t>(stream)),
-                      "pool launch");
+    return hip_status(
+        pivot::launch_pool(shape_of(p), g, G, q, w, qbar, wbar, aggregation, static_cast<hipStream_t>(stream)),
+        "pool launch");
 }
 
 pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *qbar, const float *wbar, const void *k,

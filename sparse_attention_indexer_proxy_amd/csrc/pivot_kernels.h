@@ -49,14 +49,19 @@ struct RefineLaunch {
     int32_t *row_nvalid;  // [B, Lq], nullable, splits == 1: #{j : C[j] <= t} per row
 };
 
-// Per-member top-k over the re-scored candidate rows (MFMA refine, c <= 4096).
+// Per-member top-k over candidate score rows (c <= 4096): the members'
+// re-scores of C (Refine), or the group's proxy scores of C shared by every
+// member, each member keeping only C[j] <= its own position (member-causal
+// Reuse).
 struct MemberSelectLaunch {
     int64_t G;
     int g;
     int topk, c;
     const int32_t *cand;
-    const int32_t *row_nvalid;  // [B, Lq] from the refine launch
-    const float *scores;  // [B*G, g, c]
+    const int32_t *cand_n;      // read when row_nvalid is null
+    const int32_t *row_nvalid;  // [B, Lq] from the refine launch, or null
+    const float *scores;        // [B*G, g, c], or [B*G, c] when shared
+    int shared;
     int32_t *out_idx;
     float *out_sc;
 };
@@ -79,8 +84,9 @@ struct RowSelectLaunch {
 };
 
 bool mfma_shape(const LaunchShape &sh);
+// agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
-                       float *wbar, hipStream_t st);
+                       float *wbar, int agg, hipStream_t st);
 hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st);
 hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st);
 // Proxy score rows with the key axis split over `splits` workgroups per group.

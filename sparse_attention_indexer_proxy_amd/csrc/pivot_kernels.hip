@@ -341,8 +341,15 @@ __device__ void finish_group(const Geo &geo, const SelectionOut &o, int64_t b, i
     const int l = lane_id();
     if (o.to_candidates) {
         int32_t *ci = o.idx + (b * geo.G + m) * o.stride;
-        const int n = wave_emit(f.bs, f.bi, f.cnt, s, [&](int slot, int32_t p, float) { ci[slot] = p; });
-        for (int t = n + l; t < o.stride; t += kWave) ci[t] = -1;
+        float *cs = o.sc ? o.sc + (b * geo.G + m) * o.stride : nullptr;
+        const int n = wave_emit(f.bs, f.bi, f.cnt, s, [&](int slot, int32_t p, float v) {
+            ci[slot] = p;
+            if (cs) cs[slot] = v;
+        });
+        for (int t = n + l; t < o.stride; t += kWave) {
+            ci[t] = -1;
+            if (cs) cs[t] = -INFINITY;
+        }
         if (o.count && l == 0) o.count[b * geo.G + m] = n;
         return;
     }
@@ -369,10 +376,12 @@ __device__ void finish_group(const Geo &geo, const SelectionOut &o, int64_t b, i
 // ---------------------------------------------------------------- pool
 // eq. (4): thread per (b, m, head, VEC-element chunk). fp32 sum over members
 // in order, one IEEE division by the member count, RNE to the q dtype.
+// agg = 1 / 2 (the first / last-query proxies of the aggregation ablation):
+// the proxy is that member's q and w, copied unchanged.
 template <typename T>
 __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const float *__restrict__ w,
                                               T *__restrict__ qbar, float *__restrict__ wbar, Geo geo, int H,
-                                              int D)
+                                              int D, int agg)
 {
     constexpr int VEC = 16 / sizeof(T);
     const int chunks = D / VEC;
@@ -386,6 +395,13 @@ __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const flo
     const int64_t b = bm / geo.G, m = bm % geo.G;
     const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
     const float gm = static_cast<float>(r1 - r0);
+    if (agg != 0) {
+        const int64_t r = agg == 1 ? r0 : r1 - 1;
+        *reinterpret_cast<uint4 *>(qbar + (bm * H + h) * D + ch * VEC) =
+            *reinterpret_cast<const uint4 *>(q + ((b * geo.Lq + r) * H + h) * D + ch * VEC);
+        if (ch == 0) wbar[bm * H + h] = w[(b * geo.Lq + r) * H + h];
+        return;
+    }
 
     float acc[VEC];
 #pragma unroll
@@ -1164,8 +1180,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         const Sel s = block_select(sc, n, a.K, sh);
         if (a.to_candidates) {
             int32_t *ci = a.out_idx + gid * a.out_stride;
-            const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float) { ci[slot] = p; });
-            for (int t = got + tid; t < a.out_stride; t += kSelThreads) ci[t] = -1;
+            float *cs = a.out_sc ? a.out_sc + gid * a.out_stride : nullptr;
+            const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float v) {
+                ci[slot] = p;
+                if (cs) cs[slot] = v;
+            });
+            for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
+                ci[t] = -1;
+                if (cs) cs[t] = -INFINITY;
+            }
             if (a.out_count && tid == 0) a.out_count[gid] = got;
             return;
         }
@@ -1235,8 +1258,11 @@ struct MemberSelectArgs {
     Geo geo;
     int topk, c;
     const int32_t *cand;        // [B*G, c], ascending, -1 pad
-    const int32_t *row_nvalid;  // [B, Lq]: entries of C at or before the row's position
-    const float *scores;        // [B*G, g, c] member scores over C
+    const int32_t *cand_n;      // [B*G] |C|; read only when row_nvalid is null
+    const int32_t *row_nvalid;  // [B, Lq] entries of C at or before the row's position, or null:
+                                // counted here from C
+    const float *scores;        // [B*G, g, c] member scores over C, or [B*G, c] shared by the members
+    int shared;                 // 1: one score row per group (member-causal Reuse)
     int32_t *out_idx;           // [B, Lq, topk]
     float *out_sc;              // nullable
 };
@@ -1289,15 +1315,31 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
     const int64_t gid = b * geo.G + m;
     const int mi = static_cast<int>(r - geo.first_row(m));
     const int32_t *C = a.cand + gid * a.c;
-    const float *sc = a.scores + (gid * geo.g + mi) * static_cast<int64_t>(a.c);
+    const float *sc = a.scores + (a.shared ? gid : gid * geo.g + mi) * static_cast<int64_t>(a.c);
 
     // The score loads depend only on the row; entries past the valid
-    // prefix are masked once nvalid has arrived. Keys: 0 marks an empty
-    // slot (every float maps to a key >= 0x007FFFFF).
-    // Raw buffer loads over the row (c entries): one lane offset plus an
-    // immediate per slab, and entries past the row read as 0 without a
-    // branch, so nothing per entry outlives the loads.
-    const int nvalid = a.row_nvalid[row];
+    // prefix (nvalid) are masked once it is known. Raw buffer loads over
+    // the row (c entries): one lane offset plus an immediate per slab, and
+    // entries past the row read as 0 without a branch, so nothing per entry
+    // outlives the loads. Keys: 0 marks an empty slot (every float maps to a
+    // key >= 0x007FFFFF).
+    int nvalid;
+    if (a.row_nvalid) {
+        nvalid = a.row_nvalid[row];
+    } else {
+        // the candidates s <= t are a prefix of C (ascending): the last
+        // 64-entry slab whose first entry is <= t holds its end
+        const int64_t t = geo.Lk - geo.Lq + r;
+        const int nc = a.cand_n[gid];
+        const int jh = kWave * l;
+        const bool head = l < NV && jh < nc && C[jh] <= t;
+        const int nh = popc(ballot(head));
+        nvalid = 0;
+        if (nh > 0) {
+            const int j = kWave * (nh - 1) + l;
+            nvalid = kWave * (nh - 1) + popc(ballot(j < nc && C[j] <= t));
+        }
+    }
     const __amdgpu_buffer_rsrc_t rs = row_buffer(sc, a.c);
     const __amdgpu_buffer_rsrc_t rc = row_buffer(C, a.c);
     uint32_t kv[NV];
@@ -1673,7 +1715,7 @@ __global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
 
 // --------------------------------------------------------------- launchers
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
-                       float *wbar, hipStream_t st)
+                       float *wbar, int agg, hipStream_t st)
 {
     Geo geo{sh.B, G, sh.Lq, sh.Lk, g};
     const int vec = sh.bf16 ? 8 : 4;
@@ -1681,10 +1723,10 @@ hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, c
     const int64_t blocks = (total + 255) / 256;
     if (sh.bf16) {
         hipLaunchKernelGGL(k_pool<uint16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(q), w, static_cast<uint16_t *>(qbar), wbar, geo, sh.H, sh.D);
+                           static_cast<const uint16_t *>(q), w, static_cast<uint16_t *>(qbar), wbar, geo, sh.H, sh.D, agg);
     } else {
         hipLaunchKernelGGL(k_pool<float>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
-                           static_cast<const float *>(q), w, static_cast<float *>(qbar), wbar, geo, sh.H, sh.D);
+                           static_cast<const float *>(q), w, static_cast<float *>(qbar), wbar, geo, sh.H, sh.D, agg);
     }
     return hipGetLastError();
 }
@@ -1795,8 +1837,10 @@ hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch
     a.topk = L.topk;
     a.c = L.c;
     a.cand = L.cand;
+    a.cand_n = L.cand_n;
     a.row_nvalid = L.row_nvalid;
     a.scores = L.scores;
+    a.shared = L.shared;
     a.out_idx = L.out_idx;
     a.out_sc = L.out_sc;
     const int64_t rows = sh.B * sh.Lq;

@@ -104,3 +104,86 @@ def test_python_binding_raises_on_bad_tensors():
         pv.index_dense(q, w, k, 4)          # host tensors are refused
     with pytest.raises(ValueError):
         pv.index_dense(q, w[:, :4], k, 4)   # shape mismatch
+
+
+def _cfg(**kw):
+    cfg = pv.Config()
+    cfg.variant, cfg.g, cfg.topk, cfg.c = pv.REFINE, 8, 16, 32
+    cfg.auto_variant = pv.REFINE
+    for key, v in kw.items():
+        setattr(cfg, key, v)
+    return cfg
+
+
+def test_config_init_defaults(pivot_lib):
+    cfg = pv.Config()
+    assert pivot_lib.pivot_config_init(ctypes.byref(cfg)) == 0
+    assert (cfg.variant, cfg.g, cfg.topk, cfg.c) == (pv.REFINE, 8, 2048, 4096)
+    assert (cfg.aggregation, cfg.member_causal, cfg.auto_variant, cfg.dense_below) == (0, 0, pv.REFINE, 0)
+    assert pivot_lib.pivot_config_init(None) == 1
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(aggregation=3), 1),                                   # unknown aggregation
+    (dict(member_causal=2), 1),
+    (dict(member_causal=1), 1),                                 # Refine already masks per member
+    (dict(variant=pv.DENSE, member_causal=1), 1),
+    (dict(variant=pv.AUTO, auto_variant=pv.DENSE), 1),          # AUTO must fall back to a PIVOT variant
+    (dict(variant=7), 1),
+    (dict(variant=pv.REUSE, member_causal=1, topk=4000, g=200), 2),  # top-(k+g-1) above 4096
+    (dict(variant=pv.REUSE, member_causal=1, topk=4000, g=97), 0),   # exactly 4096
+    (dict(variant=pv.REUSE, member_causal=1), 0),
+    (dict(variant=pv.AUTO, auto_variant=pv.REUSE, member_causal=1), 0),
+    (dict(aggregation=2), 0),
+])
+def test_config_validation(pivot_lib, kw, expect):
+    prob = _prob(Lq=4096, Lk=4096)
+    out = ctypes.c_size_t(0)
+    st = pivot_lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(_cfg(**kw)), ctypes.byref(out))
+    assert st == expect, pivot_lib.pivot_last_error().decode()
+    if expect == 0:
+        assert out.value > 0
+
+
+def test_auto_resolves_by_key_count(pivot_lib):
+    def resolved(lk, **kw):
+        v = ctypes.c_int32(-1)
+        prob = _prob(Lq=lk, Lk=lk)
+        assert pivot_lib.pivot_resolve_variant(ctypes.byref(prob), ctypes.byref(_cfg(**kw)), ctypes.byref(v)) == 0
+        return v.value
+
+    d = pv.DENSE_BELOW_DEFAULT
+    assert resolved(d - 1, variant=pv.AUTO) == pv.DENSE
+    assert resolved(d, variant=pv.AUTO) == pv.REFINE
+    assert resolved(d, variant=pv.AUTO, auto_variant=pv.REUSE) == pv.REUSE
+    assert resolved(99, variant=pv.AUTO, dense_below=100) == pv.DENSE
+    assert resolved(100, variant=pv.AUTO, dense_below=100) == pv.REFINE
+    assert resolved(10, variant=pv.REUSE) == pv.REUSE   # explicit variants are never rewritten
+    m = re.search(r"#define PIVOT_DENSE_BELOW_DEFAULT (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == pv.DENSE_BELOW_DEFAULT
+
+
+def test_member_causal_workspace_holds_the_wider_selection(pivot_lib):
+    prob = _prob(Lq=4096, Lk=4096)
+    sizes = []
+    for causal in (0, 1):
+        out = ctypes.c_size_t(0)
+        cfg = _cfg(variant=pv.REUSE, member_causal=causal)
+        assert pivot_lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(out)) == 0
+        sizes.append(out.value)
+    assert sizes[1] > sizes[0]
+
+
+def test_config_call_validates_before_launch(pivot_lib):
+    prob = _prob()
+    fake = ctypes.c_void_p(1 << 20)
+    idx = ctypes.c_void_p(1 << 21)
+    assert pivot_lib.pivot_index(ctypes.byref(prob), None, fake, fake, fake, idx, None, None, None, fake, 1 << 30,
+                                 None) == 1
+    cfg = _cfg(member_causal=1)
+    assert pivot_lib.pivot_index(ctypes.byref(prob), ctypes.byref(cfg), fake, fake, fake, idx, None, None, None,
+                                 fake, 1 << 30, None) == 1
+    cfg = _cfg(variant=pv.REUSE)
+    assert pivot_lib.pivot_index(ctypes.byref(prob), ctypes.byref(cfg), fake, fake, fake, idx, None, None, None,
+                                 fake, 16, None) == 3
+    assert pivot_lib.pivot_pool_ex(ctypes.byref(prob), 4, 5, fake, fake, fake, fake, None) == 1
