@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 2
+#define PIVOT_ABI_VERSION 3
 
 typedef enum {
     PIVOT_OK = 0,
@@ -175,8 +175,18 @@ pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *q
  * recorded events, adds the elapsed milliseconds of each stage into ms[s] and
  * the number of launches into launches[s] (arrays of PIVOT_STAGES entries;
  * either may be NULL), then forgets the records. Disabling also forgets them. */
-#define PIVOT_STAGES 4
-typedef enum { PIVOT_STAGE_POOL = 0, PIVOT_STAGE_SCAN = 1, PIVOT_STAGE_SELECT = 2, PIVOT_STAGE_REFINE = 3 } pivot_stage;
+#define PIVOT_STAGES 5
+/* POOL: eq. (4); SCAN: eq. (5) with its streaming filter; SCAN_SELECT: the
+ * group's final top-k / top-c of eqs. (6)-(7) when the scan leaves survivors
+ * for a separate kernel; SELECT: per-row selects (eq. (9), few-groups rows);
+ * REFINE: eq. (8). */
+typedef enum {
+    PIVOT_STAGE_POOL = 0,
+    PIVOT_STAGE_SCAN = 1,
+    PIVOT_STAGE_SELECT = 2,
+    PIVOT_STAGE_REFINE = 3,
+    PIVOT_STAGE_SCAN_SELECT = 4
+} pivot_stage;
 pivot_status pivot_timing_enable(int32_t on);
 pivot_status pivot_timing_read(double *ms, int64_t *launches);
 

@@ -36,7 +36,7 @@ EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "p
             "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
             "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_timing_enable", "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
-STAGES = ("pool", "scan", "select", "refine")
+STAGES = ("pool", "scan", "select", "refine", "scan_select")
 
 
 class PivotError(RuntimeError):

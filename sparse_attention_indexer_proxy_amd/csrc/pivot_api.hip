@@ -114,7 +114,7 @@ struct Layout {
     bool pool;
     bool few;               // few groups: split scan into score rows + block selects
     int scan_splits, refine_splits;
-    size_t qbar, wbar, buf, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
+    size_t qbar, wbar, buf, buf_n, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
@@ -221,6 +221,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, Layout *L)
     } else {
         l.scan_splits = l.refine_splits = 1;
         l.buf = take(groups * 2 * cap * sizeof(float));
+        l.buf_n = take(groups * sizeof(int32_t));
     }
     if (variant == PIVOT_REFINE || cfg.causal) {
         l.cand = take(groups * static_cast<size_t>(l.K) * sizeof(int32_t));
@@ -292,6 +293,7 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     sl.K = L.K;
     sl.cap = L.cap;
     sl.buf = L.few ? nullptr : reinterpret_cast<float *>(base + L.buf);
+    sl.buf_n = L.few ? nullptr : reinterpret_cast<int32_t *>(base + L.buf_n);
     if (to_cand) {
         sl.out_idx = cand;
         sl.out_sc = cand_sc;
@@ -327,8 +329,14 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
         StageTimer tm(PIVOT_STAGE_SELECT, s);
         st = hip_status(pivot::launch_select_rows(sh, rs, s), "select launch");
     } else {
-        StageTimer tm(PIVOT_STAGE_SCAN, s);
-        st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
+        {
+            StageTimer tm(PIVOT_STAGE_SCAN, s);
+            st = hip_status(pivot::launch_scan(sh, sl, s), "scan launch");
+        }
+        if (st == PIVOT_OK && pivot::mfma_shape(sh)) {
+            StageTimer tm(PIVOT_STAGE_SCAN_SELECT, s);
+            st = hip_status(pivot::launch_select_groups(sh, sl, s), "group select launch");
+        }
     }
     if (st != PIVOT_OK) return st;
 

@@ -23,6 +23,7 @@ struct ScanLaunch {
     int g;
     int K, cap;         // selection size and per-group buffer capacity
     float *buf;         // [B*G, 2*cap]: cap scores then cap int32 positions per group
+    int32_t *buf_n;     // [B*G] buffered entries (MFMA shape, selection mode)
     int32_t *out_idx;   // rows [B, Lq, stride] or candidates [B, G, stride]
     float *out_sc;      // rows only, nullable
     int32_t *out_count; // candidates only, nullable
@@ -87,7 +88,12 @@ bool mfma_shape(const LaunchShape &sh);
 // agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st);
+// eqs. (5)-(7). On the MFMA shape in selection mode the scan leaves each
+// group's survivors in L.buf / L.buf_n and launch_select_groups must follow
+// on the same stream; the exact-order kernels select in-kernel.
 hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st);
+// The final top-K of every group's survivor buffer into L's outputs.
+hipError_t launch_select_groups(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st);
 hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st);
 // Proxy score rows with the key axis split over `splits` workgroups per group.
 hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int splits, hipStream_t st);

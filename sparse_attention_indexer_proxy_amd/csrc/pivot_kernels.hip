@@ -458,8 +458,9 @@ struct ScanArgs {
     int H, D;
     // kFilter
     int K, cap;
-    float *buf_s;  // [B*G][2*cap]: cap scores, then cap positions (int32)
-    SelectionOut out;
+    float *buf_s;     // [B*G][2*cap]: cap scores, then cap positions (int32)
+    int32_t *buf_n;   // [B*G] entries buffered (MFMA scan; k_select_groups selects them)
+    SelectionOut out; // exact-order scan: selected in-kernel
     // kRows
     float *rows;  // [B, G, Lk]
 };
@@ -572,41 +573,74 @@ __device__ __forceinline__ void mfma_regs(const bf16x8 (&afr)[RB][4], const bf16
 // the eight 16-key blocks: block cb+2's B fragments are read from LDS while
 // block cb's MFMAs run, and block cb-1's ReLU-weighted reduction overlaps
 // them; the first half's transpose overlaps the second half's MFMAs.
-template <int RB>
-__device__ __forceinline__ void tile_scores_128(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4],
-                                                const uint16_t *tile, int l, float (&score)[2])
+// Fence for the instruction scheduler: nothing moves across it, so the
+// source order below is the issue order.
+#define PIVOT_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One tile of NBLK 16-key blocks, software-pipelined in issue order: the 16
+// MFMAs of block cb alternate one-for-one with the ReLU-weighted reduction
+// of block cb - 1 (one max and one FMA each), so the matrix core never waits
+// on the reduction and the reduction reads accumulators finished 16 MFMAs
+// earlier; the B fragments of block cb + 2 are read from LDS while block cb
+// runs. The pipeline also runs across tiles: the last block of a tile is
+// handed over in `carry` (its MFMAs may still be in flight through the
+// barrier) and reduced beside the next tile's first block, with `pc` holding
+// the reduced blocks NBLK - 4 .. NBLK - 2 of that last 64-key quarter.
+// emit(q, score) receives each finished quarter: q = -1 for the previous
+// tile's last quarter (only when have_prev), q = 0 .. NBLK / 4 - 2 for this
+// tile's; lane l's score is that of key 64 q + l.
+template <int RB, int NBLK, class Emit>
+__device__ __forceinline__ void tile_step(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4], const uint16_t *tile,
+                                          int l, f32x4 (&carry)[RB], float (&pc)[3], bool have_prev, Emit &&emit)
 {
-    f32x4 acc0[RB], acc1[RB];
-    bf16x8 b0[4], b1[4];
-    float p[8];
-    load_b(tile, 0, l, b0);
-    load_b(tile, 1, l, b1);
-    mfma_regs<RB>(afr, b0, acc0);
-    load_b(tile, 2, l, b0);
-    mfma_regs<RB>(afr, b1, acc1);
-    load_b(tile, 3, l, b1);
-    p[0] = relu_weighted<RB>(acc0, wr);
-    mfma_regs<RB>(afr, b0, acc0);
-    load_b(tile, 4, l, b0);
-    p[1] = relu_weighted<RB>(acc1, wr);
-    mfma_regs<RB>(afr, b1, acc1);
-    load_b(tile, 5, l, b1);
-    p[2] = relu_weighted<RB>(acc0, wr);
-    mfma_regs<RB>(afr, b0, acc0);
-    load_b(tile, 6, l, b0);
-    p[3] = relu_weighted<RB>(acc1, wr);
-    mfma_regs<RB>(afr, b1, acc1);
-    load_b(tile, 7, l, b1);
-    p[4] = relu_weighted<RB>(acc0, wr);
-    mfma_regs<RB>(afr, b0, acc0);
-    p[5] = relu_weighted<RB>(acc1, wr);
-    mfma_regs<RB>(afr, b1, acc1);
-    p[6] = relu_weighted<RB>(acc0, wr);
-    p[7] = relu_weighted<RB>(acc1, wr);
-    const float lo[4] = {p[0], p[1], p[2], p[3]};
-    const float hi[4] = {p[4], p[5], p[6], p[7]};
-    score[0] = quarter_transpose_sum(lo);
-    score[1] = quarter_transpose_sum(hi);
+    static_assert(RB == 4, "one reduction element per MFMA needs 16 MFMAs per block");
+    static_assert(NBLK % 4 == 0 && NBLK >= 4, "whole 64-key quarters");
+    f32x4 acc[2][RB];
+    bf16x8 bq[2][4];
+    float p[NBLK];
+    load_b(tile, 0, l, bq[0]);
+    load_b(tile, 1, l, bq[1]);
+    PIVOT_SCHED_FENCE();
+#pragma unroll
+    for (int cb = 0; cb < NBLK; ++cb) {
+        f32x4 (&ac)[RB] = acc[cb & 1];
+        const f32x4 (&pv)[RB] = cb == 0 ? carry : acc[(cb + 1) & 1];  // block cb - 1
+        float sum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                ac[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bq[cb & 1][kb],
+                                                                kb == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : ac[rb], 0, 0, 0);
+                // element (kb, rb) of block cb - 1: accumulator kb, lane slot rb
+                const float relu = __int_as_float(max(__float_as_int(pv[kb][rb]), 0));
+                sum = fmaf(wr[kb][rb], relu, sum);
+                asm volatile("" : "+v"(sum));  // keep the partial sum here, beside this MFMA
+                PIVOT_SCHED_FENCE();
+            }
+            if (cb + 2 < NBLK) {
+                bq[cb & 1][kb] = b_frag(tile, cb + 2, kb, l);
+                PIVOT_SCHED_FENCE();
+            }
+        }
+        if (cb == 0) {
+            if (have_prev) {
+                const float q4[4] = {pc[0], pc[1], pc[2], sum};
+                emit(-1, quarter_transpose_sum(q4));
+            }
+        } else {
+            p[cb - 1] = sum;
+            if (cb % 4 == 0) {
+                const float q4[4] = {p[cb - 4], p[cb - 3], p[cb - 2], p[cb - 1]};
+                emit(cb / 4 - 1, quarter_transpose_sum(q4));
+            }
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) carry[rb] = acc[(NBLK - 1) & 1][rb];
+    pc[0] = p[NBLK - 4];
+    pc[1] = p[NBLK - 3];
+    pc[2] = p[NBLK - 2];
 }
 
 template <int H>
@@ -649,12 +683,35 @@ constexpr float kSampleSigmas = 6.0f;
 #ifndef PIVOT_SCAN_WAVES
 #define PIVOT_SCAN_WAVES 8
 #endif
+#ifndef PIVOT_SCAN_TILE
+#define PIVOT_SCAN_TILE 128
+#endif
 #ifndef PIVOT_SCAN_BUFS
 #define PIVOT_SCAN_BUFS 2
 #endif
 constexpr int kScanWaves = PIVOT_SCAN_WAVES;
 constexpr int kScanBufs = PIVOT_SCAN_BUFS;
+constexpr int kScanTileKeys = PIVOT_SCAN_TILE;  // keys per LDS tile (one barrier each)
+static_assert(kScanTileKeys % 64 == 0, "whole 64-key quarters");
 static_assert(kScanBufs == 2 || kScanBufs == 3, "two or three tile buffers");
+
+// One wave's share of a key tile: rows [base, base + NT) of kseq become one
+// buffer resource of the bytes that exist, so rows past lk read as zero
+// (their scores are masked) and each 1 KiB slice is one LDS DMA instruction
+// on the lane's fixed byte offset voff[j]; slice j lands at dst + 512 j.
+constexpr int kDmaSlices = kScanTileKeys * 256 / 1024 / kScanWaves;  // 1 KiB slices per wave per tile
+__device__ __forceinline__ void dma_key_tile(const uint16_t *kseq, int64_t base, int64_t lk, uint16_t *dst,
+                                             const uint32_t *voff)
+{
+    constexpr int NT = kScanTileKeys, D = 128, SLICES = kDmaSlices;
+    const int64_t rows_left = lk - base;
+    const uint32_t nbytes = static_cast<uint32_t>(rows_left < NT ? rows_left : NT) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kseq + base * D), 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < SLICES; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + j * 512), 16, voff[j], 0, 0, 0);
+}
 
 // Workgroup barrier without a memory fence. LDS tiles are written only by
 // global_load_lds, whose completion each wave establishes with an explicit
@@ -673,9 +730,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
     constexpr int RB = H / 16;
-    constexpr int NT = 2 * kTileKeys;                     // 128 keys per tile
-    constexpr int SLICES = NT * D * 2 / 1024;             // 1 KiB slices per tile (32)
-    constexpr int SLICES_PER_WAVE = SLICES / kScanWaves;  // DMA instructions per lane per tile (4)
+    constexpr int NT = kScanTileKeys;                     // keys per tile
+    constexpr int NQ = NT / kWave;                        // 64-key quarters per tile
+    constexpr int SLICES = NT * D * 2 / 1024;             // 1 KiB slices per tile
+    constexpr int SLICES_PER_WAVE = SLICES / kScanWaves;  // DMA instructions per lane per tile
     static_assert(SLICES % kScanWaves == 0, "each wave issues the same number of slices");
     constexpr int NB = kScanBufs;
     constexpr int AHEAD = (NB - 2) * SLICES_PER_WAVE;     // vmcnt that leaves the newer tiles in flight
@@ -690,7 +748,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     __shared__ uint32_t hist[kScanWaves][256];
 
     const Geo &geo = a.geo;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: per-wave values live in SGPRs
     const int l = threadIdx.x & 63;
     const int64_t nblk = (geo.G + kScanWaves - 1) / kScanWaves;
     const int64_t b = blockIdx.x % geo.B;
@@ -721,24 +779,17 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     }
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
-    // This lane's DMA rows for a tile: slices wv * SLICES_PER_WAVE + j.
-    int slice_off[SLICES_PER_WAVE], slice_rowi[SLICES_PER_WAVE];
+    // This lane's byte offset within a tile for each of its DMA slices
+    // (slices wv * SLICES_PER_WAVE + j).
+    uint32_t slice_voff[SLICES_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < SLICES_PER_WAVE; ++j) {
         const int slice = wv * SLICES_PER_WAVE + j;
-        slice_rowi[j] = slice_row(slice, l);
-        slice_off[j] = slice_col(slice, l);
+        slice_voff[j] = static_cast<uint32_t>((slice_row(slice, l) * D + slice_col(slice, l)) * 2);
     }
     auto issue_tile = [&](int buf, int64_t base) {
         uint16_t *dst = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
-#pragma unroll
-        for (int j = 0; j < SLICES_PER_WAVE; ++j) {
-            int64_t s = base + slice_rowi[j];
-            s = s < geo.Lk ? s : geo.Lk - 1;  // past the end: any valid row (its scores are masked)
-            const uint16_t *src = kseq + s * D + slice_off[j];
-            __builtin_amdgcn_global_load_lds((global_cptr)src,
-                                             (lds_ptr)(dst + (wv * SLICES_PER_WAVE + j) * 512), 16, 0, 0);
-        }
+        dma_key_tile(kseq, base, geo.Lk, dst + wv * SLICES_PER_WAVE * 512, slice_voff);
     };
 
     // Phases of a pass over the tiles; the per-score work is chosen at run
@@ -748,13 +799,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     int nsv = 0;          // valid sampled keys (phase Sample)
     bool redo = false;    // phase Redo: this wave repeats its selection
     float *smp = f.bs;    // sample slots (phase Sample; the buffer is empty then)
-    auto on_score = [&](int phase, int it, int half, int64_t base, float score) {
+    auto on_score = [&](int phase, int it, int quarter, int64_t base, float score) {
         const int64_t s = base + l;
-        const bool valid = s <= my_tlast;
+        // lanes at or below lim hold keys s <= t_last (wave-uniform; positions
+        // are below 2^31, so the difference fits 32 bits)
+        const int lim = static_cast<int>(my_tlast) - static_cast<int>(base);
+        const bool valid = l <= lim;
         if (phase == kPhaseRows) {
             if (active && s < geo.Lk) row[s] = valid ? score : -INFINITY;
         } else if (phase == kPhaseSample) {
-            if (active) smp[(it / stride) * NT + half * (NT / 2) + l] = valid ? score : -INFINITY;
+            if (active) smp[(it / stride) * NT + quarter * kWave + l] = valid ? score : -INFINITY;
             nsv += popc(ballot(valid));
         } else if (phase == kPhaseFilter) {
             if (active) f.push(valid, score, static_cast<int32_t>(s));
@@ -774,6 +828,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
         }
         tile_barrier();
         int buf = 0;
+        f32x4 carry[RB];  // the previous tile's last block, not yet reduced
+        float pc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) carry[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        int prev_it = 0;
         for (int i = 0; i < nt; ++i) {
             const int it = i * step;
             const int64_t base = static_cast<int64_t>(it) * NT;
@@ -781,15 +840,19 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             // finished reading before the last barrier
             const bool ahead = i + NB - 1 < nt;
             if (ahead) issue_tile(buf == 0 ? NB - 1 : buf - 1, base + (NB - 1) * tstep);
-            float sc2[2];
+            auto emit = [&](int qt, float score) {
+                if (qt < 0)
+                    on_score(phase, prev_it, NQ - 1, static_cast<int64_t>(prev_it) * NT + (NQ - 1) * kWave, score);
+                else
+                    on_score(phase, it, qt, base + qt * kWave, score);
+            };
             if (buf == 0)
-                tile_scores_128<RB>(afr, wr, tile0, l, sc2);
+                tile_step<RB, NT / 16>(afr, wr, tile0, l, carry, pc, i > 0, emit);
             else if (NB == 2 || buf == 1)
-                tile_scores_128<RB>(afr, wr, tile1, l, sc2);
+                tile_step<RB, NT / 16>(afr, wr, tile1, l, carry, pc, i > 0, emit);
             else
-                tile_scores_128<RB>(afr, wr, tile2, l, sc2);
-            on_score(phase, it, 0, base, sc2[0]);
-            on_score(phase, it, 1, base + NT / 2, sc2[1]);
+                tile_step<RB, NT / 16>(afr, wr, tile2, l, carry, pc, i > 0, emit);
+            prev_it = it;
             // tile i + 1 must be in LDS; with three buffers tile i + 2's DMAs
             // may stay in flight (vector memory counts complete in issue
             // order, so stores issued after them only make this wait longer)
@@ -800,6 +863,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             tile_barrier();
             buf = buf == NB - 1 ? 0 : buf + 1;
         }
+        // the last tile's last quarter
+        const float q4[4] = {pc[0], pc[1], pc[2], relu_weighted<RB>(carry, wr)};
+        on_score(phase, prev_it, NQ - 1, static_cast<int64_t>(prev_it) * NT + (NQ - 1) * kWave,
+                 quarter_transpose_sum(q4));
     };
 
     if (Mode == kRows) {
@@ -845,8 +912,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
         pass(kPhaseRedo, 1);
     }
 
-    if (!active) return;
-    finish_group(geo, a.out, b, m, f);
+    // the group's survivors (ascending position, at least min(K, n_valid)
+    // of them) are selected by k_select_groups, at full occupancy
+    if (active && l == 0) a.buf_n[gid] = f.cnt;
 }
 
 // ---------------------------------------------- split scan (few groups)
@@ -1298,77 +1366,53 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
-template <int NV>
-__global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelectArgs a)
+// The best K of n entries (score desc, then lower entry index), emitted in
+// entry order. Entry j's score is the 32-bit float at byte 4 j of rs and its
+// position the int32 at byte 4 j of rc (both raw buffers, so loads past
+// their ends read 0 without a branch); n <= 64 NV. Keys (ord_key) sit in
+// registers, 64 NV per wave; the K-th largest is found by bisection over the
+// 32 key bits with wave-uniform counts (v_cmp + s_bcnt1). Once the bracket
+// holding it has at most kMsMid keys they are compacted into `mid` (kMsMid
+// words of LDS, wave-private) and the remaining bits are resolved over them
+// alone. A bracket that stays crowded is checked every 8 bits for a single
+// repeated key (many exact zeros), which ends the search. emit(slot,
+// position, score) is called for every selected entry, slots dense and
+// ascending; positions are loaded a chunk ahead. Returns the count.
+template <int NV, class Emit>
+__device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rc, int n, int K,
+                                              uint32_t *mid, Emit &&emit)
 {
-    static_assert(NV >= 1 && NV <= kWave, "slab count");
+    static_assert(NV >= 1 && NV <= 2 * kWave, "slab count");
     constexpr int CH = NV < kMsChunk ? NV : kMsChunk;
     static_assert(NV % CH == 0, "whole chunks");
-    __shared__ uint32_t mid_all[kMsWaves][kMsMid];
-    const Geo &geo = a.geo;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row addressing
-    const int l = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kMsWaves + wv;
-    if (row >= geo.B * geo.Lq) return;  // wave-uniform; the waves never synchronise
-    const int64_t b = row / geo.Lq, r = row - b * geo.Lq;
-    const int64_t m = r / geo.g;
-    const int64_t gid = b * geo.G + m;
-    const int mi = static_cast<int>(r - geo.first_row(m));
-    const int32_t *C = a.cand + gid * a.c;
-    const float *sc = a.scores + (a.shared ? gid : gid * geo.g + mi) * static_cast<int64_t>(a.c);
-
-    // The score loads depend only on the row; entries past the valid
-    // prefix (nvalid) are masked once it is known. Raw buffer loads over
-    // the row (c entries): one lane offset plus an immediate per slab, and
-    // entries past the row read as 0 without a branch, so nothing per entry
-    // outlives the loads. Keys: 0 marks an empty slot (every float maps to a
-    // key >= 0x007FFFFF).
-    int nvalid;
-    if (a.row_nvalid) {
-        nvalid = a.row_nvalid[row];
-    } else {
-        // the candidates s <= t are a prefix of C (ascending): the last
-        // 64-entry slab whose first entry is <= t holds its end
-        const int64_t t = geo.Lk - geo.Lq + r;
-        const int nc = a.cand_n[gid];
-        const int jh = kWave * l;
-        const bool head = l < NV && jh < nc && C[jh] <= t;
-        const int nh = popc(ballot(head));
-        nvalid = 0;
-        if (nh > 0) {
-            const int j = kWave * (nh - 1) + l;
-            nvalid = kWave * (nh - 1) + popc(ballot(j < nc && C[j] <= t));
-        }
-    }
-    const __amdgpu_buffer_rsrc_t rs = row_buffer(sc, a.c);
-    const __amdgpu_buffer_rsrc_t rc = row_buffer(C, a.c);
+    const int l = lane_id();
+    // Keys: 0 marks an empty slot (every float maps to a key >= 0x007FFFFF).
     uint32_t kv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) kv[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (kWave * i + l) * 4, 0, 0);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) kv[i] = l < nvalid - kWave * i ? ord_key(__uint_as_float(kv[i])) : 0u;
+    for (int i = 0; i < NV; ++i) kv[i] = l < n - kWave * i ? ord_key(__uint_as_float(kv[i])) : 0u;
 
-    const int K = a.topk;
     // selected: key > kth, plus the first `quota` keys equal to kth;
     // ties_all: every key equal to kth is selected
     uint32_t kth = 1u;
     int quota = 0;
     bool ties_all = true;
-    if (nvalid > K) {
+    if (n > K) {
         // invariant: kth in [T, T + 2^bit); n_lo = #{key >= T} >= K,
         // n_hi = #{key >= T + 2^bit} < K
         uint32_t T = 0;
-        int n_lo = nvalid, n_hi = 0;
+        int n_lo = n, n_hi = 0;
         int bit = 32;
         while (bit > 0 && n_lo - n_hi > kMsMid) {
             --bit;
             const uint32_t x = T | (1u << bit);
-            const int n = count_ge(kv, x);
-            if (n >= K) {
+            const int c = count_ge(kv, x);
+            if (c >= K) {
                 T = x;
-                n_lo = n;
+                n_lo = c;
             } else {
-                n_hi = n;
+                n_hi = c;
             }
             if ((bit & 7) == 0 && bit > 0 && n_lo - n_hi > kMsMid) {
                 // a bracket that stays crowded may hold one repeated key
@@ -1389,7 +1433,6 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
         }
         if (bit > 0) {
             // compact the keys of the bracket into LDS, then finish there
-            uint32_t *mid = mid_all[wv];
             int nm = 0;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
@@ -1421,15 +1464,13 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
 
     // ordered emission; the next chunk of positions is loaded while the
     // current one is written
-    int32_t *oi = a.out_idx + row * a.topk;
-    float *os = a.out_sc ? a.out_sc + row * a.topk : nullptr;
     int out = 0, eq_seen = 0;
     int32_t cv[CH];
 #pragma unroll
     for (int e = 0; e < CH; ++e) cv[e] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(rc, (kWave * e + l) * 4, 0, 0));
 #pragma unroll
     for (int i0 = 0; i0 < NV; i0 += CH) {
-        if (kWave * i0 >= nvalid) break;
+        if (kWave * i0 >= n) break;
         int32_t cn[CH];
         if (i0 + CH < NV) {
 #pragma unroll
@@ -1449,11 +1490,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
                 take = key > kth || (eq && rank < quota);
             }
             const uint64_t tm = ballot(take);
-            if (take) {
-                const int slot = out + mbcnt(tm);
-                oi[slot] = cv[e];
-                if (os) os[slot] = key_float(key);
-            }
+            if (take) emit(out + mbcnt(tm), cv[e], key_float(key));
             out += popc(tm);
         }
         if (i0 + CH < NV) {
@@ -1461,9 +1498,127 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
             for (int e = 0; e < CH; ++e) cv[e] = cn[e];
         }
     }
-    for (int x = out + l; x < K; x += kWave) {
+    return out;
+}
+
+template <int NV>
+__global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelectArgs a)
+{
+    __shared__ uint32_t mid_all[kMsWaves][kMsMid];
+    const Geo &geo = a.geo;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row addressing
+    const int l = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kMsWaves + wv;
+    if (row >= geo.B * geo.Lq) return;  // wave-uniform; the waves never synchronise
+    const int64_t b = row / geo.Lq, r = row - b * geo.Lq;
+    const int64_t m = r / geo.g;
+    const int64_t gid = b * geo.G + m;
+    const int mi = static_cast<int>(r - geo.first_row(m));
+    const int32_t *C = a.cand + gid * a.c;
+    const float *sc = a.scores + (a.shared ? gid : gid * geo.g + mi) * static_cast<int64_t>(a.c);
+
+    // The candidates a member may take are the prefix of C at or before its
+    // position (nvalid entries).
+    int nvalid;
+    if (a.row_nvalid) {
+        nvalid = a.row_nvalid[row];
+    } else {
+        // the candidates s <= t are a prefix of C (ascending): the last
+        // 64-entry slab whose first entry is <= t holds its end
+        const int64_t t = geo.Lk - geo.Lq + r;
+        const int nc = a.cand_n[gid];
+        const int jh = kWave * l;
+        const bool head = l < NV && jh < nc && C[jh] <= t;
+        const int nh = popc(ballot(head));
+        nvalid = 0;
+        if (nh > 0) {
+            const int j = kWave * (nh - 1) + l;
+            nvalid = kWave * (nh - 1) + popc(ballot(j < nc && C[j] <= t));
+        }
+    }
+    int32_t *oi = a.out_idx + row * a.topk;
+    float *os = a.out_sc ? a.out_sc + row * a.topk : nullptr;
+    const int out = wave_topk_emit<NV>(row_buffer(sc, a.c), row_buffer(C, a.c), nvalid, a.topk, mid_all[wv],
+                                       [&](int slot, int32_t pos, float v) {
+                                           oi[slot] = pos;
+                                           if (os) os[slot] = v;
+                                       });
+    for (int x = out + l; x < a.topk; x += kWave) {
         oi[x] = -1;
         if (os) os[x] = -INFINITY;
+    }
+}
+
+// Final selection of the fused scan's groups: one wave per group selects
+// the best K of the group's survivor buffer (cnt entries in ascending
+// position, written by k_scan_mfma) and writes the group's candidate set
+// (Refine) or the row of every member (Reuse, dense). NV > 0: the register
+// select above (cnt <= 64 NV); NV == 0: the streaming radix select over the
+// buffer in global memory, for any size.
+struct GroupSelectArgs {
+    Geo geo;
+    int K, cap;
+    const float *buf;     // [B*G][2*cap]: cap scores, then cap int32 positions
+    const int32_t *cnt;   // [B*G] buffered entries
+    SelectionOut out;
+};
+
+template <int NV>
+__global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectArgs a)
+{
+    __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid : 256];
+    const Geo &geo = a.geo;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kMsWaves + wv;
+    if (gid >= geo.B * geo.G) return;  // wave-uniform; the waves never synchronise
+    const int64_t b = gid / geo.G, m = gid - b * geo.G;
+    const float *bs = a.buf + gid * 2 * static_cast<int64_t>(a.cap);
+    const int32_t *bi = reinterpret_cast<const int32_t *>(bs + a.cap);
+    const int n = a.cnt[gid];
+    if (NV == 0) {
+        Filter f;
+        f.bs = const_cast<float *>(bs);
+        f.bi = const_cast<int32_t *>(bi);
+        f.cap = a.cap;
+        f.K = a.K;
+        f.cnt = n;
+        f.tau = -INFINITY;
+        f.hist = lds[wv];
+        finish_group(geo, a.out, b, m, f);
+        return;
+    }
+    const SelectionOut &o = a.out;
+    const __amdgpu_buffer_rsrc_t rs = row_buffer(bs, n), rp = row_buffer(bi, n);
+    if (o.to_candidates) {
+        int32_t *ci = o.idx + gid * o.stride;
+        float *cs = o.sc ? o.sc + gid * o.stride : nullptr;
+        const int got = wave_topk_emit<(NV > 0 ? NV : 1)>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
+            ci[slot] = p;
+            if (cs) cs[slot] = v;
+        });
+        for (int t = got + l; t < o.stride; t += kWave) {
+            ci[t] = -1;
+            if (cs) cs[t] = -INFINITY;
+        }
+        if (o.count && l == 0) o.count[gid] = got;
+        return;
+    }
+    const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+    const int64_t stride = o.stride;
+    const int got = wave_topk_emit<(NV > 0 ? NV : 1)>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
+        for (int64_t r = r0; r < r1; ++r) {
+            const int64_t off = (b * geo.Lq + r) * stride + slot;
+            o.idx[off] = p;
+            if (o.sc) o.sc[off] = v;
+        }
+    });
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int t = got + l; t < o.stride; t += kWave) {
+            const int64_t off = (b * geo.Lq + r) * stride + t;
+            o.idx[off] = -1;
+            if (o.sc) o.sc[off] = -INFINITY;
+        }
     }
 }
 
@@ -1745,6 +1900,7 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     a.K = L.K;
     a.cap = L.cap;
     a.buf_s = L.buf;
+    a.buf_n = L.buf_n;
     a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
     a.rows = L.rows;
     const int64_t blocks = sh.B * ((L.G + 3) / 4);
@@ -1820,6 +1976,35 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.rows = L.rows;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
     hipLaunchKernelGGL((k_scan_split<64, 128>), grid, dim3(256), 0, st, a, splits);
+    return hipGetLastError();
+}
+
+int group_select_slabs(int cap)
+{
+    for (int nv : {8, 16, 32, 64, 128})
+        if (cap <= kWave * nv) return nv;
+    return 0;
+}
+
+hipError_t launch_select_groups(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st)
+{
+    if (!mfma_shape(sh) || L.rows || !L.buf_n) return hipErrorInvalidValue;
+    GroupSelectArgs a{};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.K = L.K;
+    a.cap = L.cap;
+    a.buf = L.buf;
+    a.cnt = L.buf_n;
+    a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
+    const dim3 grid(static_cast<uint32_t>((sh.B * L.G + kMsWaves - 1) / kMsWaves)), block(kMsWaves * kWave);
+    switch (group_select_slabs(L.cap)) {
+    case 8: hipLaunchKernelGGL(k_select_groups<8>, grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL(k_select_groups<16>, grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL(k_select_groups<32>, grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_select_groups<64>, grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_select_groups<128>, grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL(k_select_groups<0>, grid, block, 0, st, a); break;
+    }
     return hipGetLastError();
 }
 
