@@ -214,7 +214,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, Layout *L)
         const int64_t tiles = (p->lk + 63) / 64;
         int64_t ss = (2048 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.scan_splits = static_cast<int>(ss < tiles ? ss : tiles);
-        const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 63) / 64;
+        const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 127) / 128;  // refine tiles of 128
         int64_t rs = (512 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.refine_splits = static_cast<int>(rs < ctiles ? rs : ctiles);
         l.rows = take(groups * static_cast<size_t>(p->lk) * sizeof(float));

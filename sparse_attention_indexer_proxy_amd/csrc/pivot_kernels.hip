@@ -1732,27 +1732,66 @@ __device__ void finish_member(const RefineArgs &a, int64_t b, int64_t r, const i
     }
 }
 
-// One workgroup (4..8 waves) per group; wave w re-scores member
-// (round * nwaves + w). Each 64-candidate tile of keys is gathered once into
-// LDS (global_load_lds, same swizzle as the scan) and shared by every member
-// wave; candidate positions are prefetched one tile ahead.
-template <int H, int D>
-__global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
+// Number of entries of the ascending list C[0..n) at or below t (one wave;
+// a ballot over 64 slab heads per step finds the slab holding the end).
+__device__ __forceinline__ int prefix_le(const int32_t *C, int n, int64_t t)
+{
+    const int l = lane_id();
+    int done = 0;
+    for (int s0 = 0; s0 < n; s0 += kWave * kWave) {
+        const int jh = s0 + kWave * l;
+        const int nh = popc(ballot(jh < n && C[jh] <= t));
+        if (nh == 0) break;
+        const int j = s0 + kWave * (nh - 1) + l;
+        const int last = kWave * (nh - 1) + popc(ballot(j < n && C[j] <= t));
+        done = s0 + last;
+        if (nh < kWave) break;
+    }
+    return done;
+}
+
+// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+// workgroup i is given unit (i % 8) * (n / 8) + i / 8 and each XCD's L2
+// serves a contiguous run of units (the tail beyond a multiple of 8 keeps
+// its index).
+__device__ __forceinline__ int64_t xcd_unit(int64_t i, int64_t n)
+{
+    constexpr int kXcds = 8;
+    const int64_t full = n / kXcds * kXcds;
+    if (i >= full) return i;
+    return (i % kXcds) * (n / kXcds) + i / kXcds;
+}
+
+// One workgroup of NW waves (4 or 8) per group (or per slice of C when
+// splits > 1); wave w re-scores member (round * NW + w), and a wave without
+// a member in the last round only helps gather. Each 128-candidate tile of
+// key rows is gathered once into LDS (global_load_lds, the scan's swizzle)
+// and shared by every member wave; candidate positions are prefetched a tile
+// ahead, and the scoring is the scan's pipelined tile_step. Groups are
+// ordered per XCD, so neighbouring groups (whose candidate sets overlap)
+// share an L2.
+template <int H, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
-    constexpr int RB = H / 16, NT = kTileKeys;
-    constexpr int kSlices = 16;  // 1 KiB slices per tile
+    constexpr int RB = H / 16;
+    constexpr int NT = 2 * kTileKeys;          // candidates per tile
+    constexpr int NQ = NT / kWave;             // 64-candidate quarters per tile
+    constexpr int kSlices = NT * D * 2 / 1024; // 1 KiB slices per tile (32)
+    constexpr int kMaxSlices = kSlices / NW;   // per wave
+    static_assert(kSlices % NW == 0, "each wave gathers the same number of slices");
 
     __shared__ __attribute__((aligned(1024))) uint16_t tile0[NT * D];
     __shared__ __attribute__((aligned(1024))) uint16_t tile1[NT * D];
     __shared__ uint32_t hist[8][256];
 
     const Geo &geo = a.geo;
-    const int nwaves = blockDim.x >> 6;
-    const int wv = threadIdx.x >> 6;
+    constexpr int nwaves = NW;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
-    const int64_t gid = blockIdx.x / a.splits;
-    const int split = blockIdx.x % a.splits;
+    const int64_t unit = xcd_unit(blockIdx.x, static_cast<int64_t>(gridDim.x));
+    const int64_t gid = unit / a.splits;
+    const int split = static_cast<int>(unit % a.splits);
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
     const int gm = static_cast<int>(r1 - r0);
@@ -1767,24 +1806,23 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
     if (tile_lo >= tile_hi) return;  // uniform over the workgroup
     const int ntiles = tile_hi - tile_lo;
 
-    // positions of the rows this lane gathers for a tile (slices wv, wv+nwaves, ...)
-    auto load_pos = [&](int tile_idx, int32_t (&pos)[4]) {
+    // positions of the key rows this lane gathers for a tile: slices
+    // wv + nwaves j (< kSlices), rows slice_row(slice, l)
+    auto load_pos = [&](int tile_idx, int32_t (&pos)[kMaxSlices]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kMaxSlices; ++j) {
             const int slice = wv + nwaves * j;
             const int cj = tile_idx * NT + slice_row(slice, l);
-            pos[j] = (slice < kSlices && cj < nc) ? C[cj] : 0;  // row 0: any valid key row
+            pos[j] = cj < nc ? C[cj] : 0;  // row 0: any valid key row (masked)
         }
     };
-    auto issue_tile = [&](int buf, const int32_t (&pos)[4]) {
+    auto issue_tile = [&](int buf, const int32_t (&pos)[kMaxSlices]) {
+        uint16_t *dst = buf ? tile1 : tile0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kMaxSlices; ++j) {
             const int slice = wv + nwaves * j;
-            if (slice < kSlices) {
-                const uint16_t *src = kseq + static_cast<int64_t>(pos[j]) * D + slice_col(slice, l);
-                uint16_t *dst = buf ? tile1 : tile0;
-                __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
-            }
+            const uint16_t *src = kseq + static_cast<int64_t>(pos[j]) * D + slice_col(slice, l);
+            __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
 
@@ -1800,35 +1838,54 @@ __global__ __launch_bounds__(512) void k_refine_mfma(RefineArgs a)
         load_a<H>(static_cast<const uint16_t *>(a.q) + (b * geo.Lq + r) * H * D, l, afr);
         load_w<H>(a.w + (b * geo.Lq + r) * H, l, wr);
 
-        int32_t pos[4], pos_next[4];
+        int32_t pos[kMaxSlices];
         load_pos(tile_lo, pos);
         issue_tile(0, pos);
-        if (ntiles > 1) load_pos(tile_lo + 1, pos_next);
-        int32_t cpos = tile_lo * NT + l < nc ? C[tile_lo * NT + l] : 0;
-        int nvalid = 0;
+        if (ntiles > 1) load_pos(tile_lo + 1, pos);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
+        tile_barrier();
 
+        f32x4 carry[RB];
+        float pc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) carry[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        auto store = [&](int tile_idx, int qt, float score) {
+            const int j = tile_idx * NT + qt * kWave + l;
+            if (active && j < nc) srow[j] = score;
+        };
         for (int it = 0; it < ntiles; ++it) {
             const int cur = it & 1;
-            const int j = (tile_lo + it) * NT + l;
-            const int32_t cpos_here = cpos;
+            // the buffer of tile it + 1 held tile it - 1, which every wave
+            // finished reading before the last barrier
             if (it + 1 < ntiles) {
-                issue_tile(cur ^ 1, pos_next);
-                if (it + 2 < ntiles) load_pos(tile_lo + it + 2, pos_next);
-                cpos = (j + NT < nc) ? C[j + NT] : 0;
+                issue_tile(cur ^ 1, pos);
+                if (it + 2 < ntiles) load_pos(tile_lo + it + 2, pos);
             }
-            const float score = cur ? tile_scores<RB>(afr, wr, tile1, l) : tile_scores<RB>(afr, wr, tile0, l);
-            if (active) {
-                const bool in = j < nc;
-                nvalid += popc(ballot(in && cpos_here <= t));
-                if (in) srow[j] = score;
+            const int ti = tile_lo + it;
+            auto emit = [&](int qt, float score) {
+                if (qt < 0)
+                    store(ti - 1, NQ - 1, score);
+                else
+                    store(ti, qt, score);
+            };
+            if (!active) {
+            } else if (cur == 0) {
+                tile_step<RB, NT / 16>(afr, wr, tile0, l, carry, pc, it > 0, emit);
+            } else {
+                tile_step<RB, NT / 16>(afr, wr, tile1, l, carry, pc, it > 0, emit);
             }
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile in LDS
-            __syncthreads();
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile is in LDS
+            tile_barrier();
         }
-        if (active && a.row_nvalid && l == 0) a.row_nvalid[b * geo.Lq + r] = nvalid;
-        if (active && a.finish) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+        if (active) {
+            const float q4[4] = {pc[0], pc[1], pc[2], relu_weighted<RB>(carry, wr)};
+            store(tile_hi - 1, NQ - 1, quarter_transpose_sum(q4));
+        }
+        if (active && (a.row_nvalid || a.finish)) {
+            const int nvalid = prefix_le(C, nc, t);
+            if (a.row_nvalid && l == 0) a.row_nvalid[b * geo.Lq + r] = nvalid;
+            if (a.finish) finish_member(a, b, r, C, srow, nvalid, hist[wv]);
+        }
     }
 }
 
@@ -1948,9 +2005,11 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     a.row_nvalid = a.splits == 1 ? L.row_nvalid : nullptr;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * a.splits));
     if (mfma_shape(sh)) {
-        int nw = L.g < 8 ? L.g : 8;  // 4..8 member waves; more members loop
-        if (nw < 4) nw = 4;
-        hipLaunchKernelGGL((k_refine_mfma<64, 128>), grid, dim3(64 * nw), 0, st, a);
+        // 4 or 8 member waves; more members loop in rounds
+        if (L.g <= 4)
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4>), grid, dim3(64 * 4), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8>), grid, dim3(64 * 8), 0, st, a);
     } else if (sh.bf16) {
         hipLaunchKernelGGL(k_refine_exact<uint16_t>, grid, dim3(256), 0, st, a);
     } else {
