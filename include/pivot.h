@@ -82,8 +82,10 @@ typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2, PIVOT_AUTO = 
 typedef enum { PIVOT_AGG_MEAN = 0, PIVOT_AGG_FIRST = 1, PIVOT_AGG_LAST = 2 } pivot_aggregation;
 
 /* Default guardrail of PIVOT_AUTO: the key count below which dense (g = 1) is
- * faster than PIVOT-Refine (g = 8, k = 2048, c = 4096) on MI355X. */
-#define PIVOT_DENSE_BELOW_DEFAULT 16384
+ * faster than PIVOT-Refine (g = 8, k = 2048, c = 4096) on MI355X, measured on
+ * one GPU over L = 4K..64K (dense 0.18 / 0.85 / 1.62 ms against Refine
+ * 0.38 / 0.80 / 1.32 ms at L = 4096 / 8192 / 12288). */
+#define PIVOT_DENSE_BELOW_DEFAULT 8192
 
 /* Problem shape. Prefill: batch = 1 (or more independent sequences), lq = lk.
  * Decode (eq. 3): lq = g rows at the last g positions of each sequence. */

@@ -26,7 +26,7 @@ __all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", 
 
 DENSE, REUSE, REFINE, AUTO = 0, 1, 2, 3
 AGGREGATIONS = {"mean": 0, "first": 1, "last": 2}
-DENSE_BELOW_DEFAULT = 16384  # PIVOT_DENSE_BELOW_DEFAULT of the header
+DENSE_BELOW_DEFAULT = 8192  # PIVOT_DENSE_BELOW_DEFAULT of the header
 _F32, _BF16 = 0, 1
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libpivot.so")
