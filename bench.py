@@ -145,6 +145,40 @@ def copy_calibration(torch, mib):
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
+def bench_stats(torch, pv, W, args, g, tq, tw, tk, ws):
+    """The O1-O3 diagnostics on this workload's rows: one JSON line with the
+    time per call and the statistics' means. Algorithmic bytes: the index and
+    score rows read once (mass reads both)."""
+    if args.variant == "refine":
+        idx, sc = pv.index_refine(tq, tw, tk, g, W.topk, W.c, workspace=ws, return_scores=True)
+    elif args.variant == "reuse":
+        idx, sc = pv.index_reuse(tq, tw, tk, g, W.topk, workspace=ws, return_scores=True)
+    else:
+        idx, sc = pv.index_dense(tq, tw, tk, W.topk, workspace=ws, return_scores=True)
+    torch.cuda.synchronize()
+    sg = max(g, W.g)
+    out = pv.index_stats(idx, sc, d=1, g=sg)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        out = pv.index_stats(idx, sc, d=1, g=sg)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2.0 * idx.numel() * 4
+    ov = out["overlap"]
+    res = {"metric": "index-row diagnostics (O1-O3) per call", "value": ms, "unit": "ms", "higher_is_better": False,
+           "config": {"workload": f"{W.name} PIVOT-{args.variant} rows", "g": g, "group_g": sg, "topk": W.topk},
+           "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+           "adjacent_overlap_over_k": float(ov[ov >= 0].float().mean()) / W.topk,
+           "group_union_over_k": float(out["union"].float().mean()) / W.topk,
+           "group_inter_over_k": float(out["inter"].float().mean()) / W.topk,
+           "mass_at_k4_k2_3k4": [float(x) for x in out["mass"].nanmean(dim=(0, 1)).cpu()]}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +189,8 @@ def main():
     ap.add_argument("--g", type=int, default=None, help="group size (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats", action="store_true",
+                    help="time the O1-O3 diagnostics (pivot_index_stats) on the variant's rows instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scales HBM byte counters)")
     args = ap.parse_args()
@@ -194,6 +230,8 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
+    if args.stats:
+        return bench_stats(torch, pv, W, args, g, tq, tw, tk, ws)
 
     # timed region: plain calls, as a caller would make them
     torch.cuda.synchronize()

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 3
+#define PIVOT_ABI_VERSION 4
 
 typedef enum {
     PIVOT_OK = 0,
@@ -170,6 +170,29 @@ pivot_status pivot_pool_ex(const pivot_problem *p, int32_t g, int32_t aggregatio
  * qbar/wbar as produced by pivot_pool (pass q, w with g = 1 for eq. 1). */
 pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *qbar, const float *wbar,
                                 const void *k, float *out, void *stream);
+
+/* O1-O3 diagnostics of index rows (the key observations of the pages'
+ * summary, Figure 2) on device buffers, for any rows the calls above return:
+ * indices [batch, lq, k] int32, each row its selected positions ascending,
+ * then -1. Outputs (each may be NULL; at least one must be given):
+ *   overlap     [batch, lq] int32: |T_t ∩ T_{t+d}| for rows t and t + d of
+ *               one sequence (d = 1: adjacent queries; d = g - 1: across a
+ *               group), -1 where t + d >= lq;
+ *   group_union / group_inter [batch, ceil(lq / g)] int32: the size of the
+ *               union and of the intersection of each group of g consecutive
+ *               rows (the last group may be short);
+ *   mass        [batch, lq, 3] f32: for f = 1/4, 1/2, 3/4, the sum of the
+ *               floor(f k) largest scores of the row over the sum of all its
+ *               scores (the whole row when it is shorter), NaN when that sum
+ *               is not positive; needs scores [batch, lq, k] f32 aligned with
+ *               indices.
+ * Limits: 1 <= k <= 4096; d >= 1; for the group outputs 1 <= g <= 64 and
+ * P * K <= 16384, P the next power of two >= g and K = k rounded up to a
+ * multiple of 32 (g = 8, k = 2048 fits). Sums are fp32. Enqueued on
+ * `stream`; nothing allocated. */
+pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32_t *indices, const float *scores,
+                               int32_t d, int32_t g, int32_t *overlap, int32_t *group_union, int32_t *group_inter,
+                               float *mass, void *stream);
 
 /* Optional per-kernel timing (instrumentation for benchmarks). While enabled
  * on the calling thread, every kernel a pivot_* call enqueues is bracketed by

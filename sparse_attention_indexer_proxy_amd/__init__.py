@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "resolve_variant", "pool",
+__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "resolve_variant", "pool", "index_stats",
            "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
            "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "DENSE_BELOW_DEFAULT",
            "STAGES"]
@@ -34,7 +34,8 @@ _lib = None
 
 EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
             "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
-            "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_timing_enable", "pivot_timing_read",
+            "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_index_stats", "pivot_timing_enable",
+            "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
 STAGES = ("pool", "scan", "select", "refine", "scan_select")
 
@@ -84,7 +85,8 @@ def load_library(path: str | None = None):
     lib.pivot_pool.argtypes = [P, i32, vp, vp, vp, vp, vp]
     lib.pivot_pool_ex.argtypes = [P, i32, i32, vp, vp, vp, vp, vp]
     lib.pivot_proxy_scores.argtypes = [P, i32, vp, vp, vp, vp, vp]
-    for name in ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
+    lib.pivot_index_stats.argtypes = [ctypes.c_int64, ctypes.c_int64, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    for name in ("pivot_index_stats","pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
                  "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
                  "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores"):
         getattr(lib, name).restype = ctypes.c_int
@@ -315,6 +317,36 @@ def proxy_scores(qbar, wbar, k, g: int, lq: int, stream=None):
     _check(load_library().pivot_proxy_scores(ctypes.byref(prob), g, _ptr(qbar), _ptr(wbar), _ptr(k), _ptr(out),
                                              _stream_ptr(stream, qbar.device)))
     return out
+
+
+def index_stats(indices, scores=None, *, d: int = 1, g: int | None = None, stream=None):
+    """O1-O3 diagnostics of index rows [B, Lq, k] (or [Lq, k]): returns a dict
+    with "overlap" [B, Lq] (|T_t ∩ T_{t+d}|, -1 past the end), and, when g is
+    given, "union" and "inter" [B, ceil(Lq/g)]; with scores, "mass"
+    [B, Lq, 3] (share of the row's score mass in its best k/4, k/2, 3k/4)."""
+    squeeze = indices.dim() == 2
+    if squeeze:
+        indices = indices.unsqueeze(0)
+        scores = scores.unsqueeze(0) if scores is not None else None
+    if indices.dim() != 3 or indices.dtype != torch.int32 or not indices.is_cuda:
+        raise ValueError("indices must be an int32 device tensor [B, Lq, k]")
+    if scores is not None and (tuple(scores.shape) != tuple(indices.shape) or scores.dtype != torch.float32):
+        raise ValueError("scores must be float32 with the shape of indices")
+    B, Lq, k = indices.shape
+    indices = indices.contiguous()
+    scores = scores.contiguous() if scores is not None else None
+    dev = indices.device
+    out = {"overlap": torch.empty((B, Lq), dtype=torch.int32, device=dev)}
+    if g is not None:
+        G = -(-Lq // g)
+        out["union"] = torch.empty((B, G), dtype=torch.int32, device=dev)
+        out["inter"] = torch.empty((B, G), dtype=torch.int32, device=dev)
+    if scores is not None:
+        out["mass"] = torch.empty((B, Lq, 3), dtype=torch.float32, device=dev)
+    _check(load_library().pivot_index_stats(B, Lq, k, _ptr(indices), _ptr(scores), d, g or 1, _ptr(out["overlap"]),
+                                            _ptr(out.get("union")), _ptr(out.get("inter")), _ptr(out.get("mass")),
+                                            _stream_ptr(stream, dev)))
+    return {name: (t[0] if squeeze else t) for name, t in out.items()}
 
 
 def timing_enable(on: bool = True):

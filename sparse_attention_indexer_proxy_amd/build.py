@@ -12,7 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "pivot_kernels.hip"), os.path.join(CSRC, "pivot_api.hip")]
+SOURCES = [os.path.join(CSRC, "pivot_kernels.hip"), os.path.join(CSRC, "pivot_diag.hip"),
+           os.path.join(CSRC, "pivot_api.hip")]
 LIB = os.path.join(PKG, "libpivot.so")
 PROBE_SRC = os.path.join(CSRC, "mfma_probe.hip")
 PROBE = os.path.join(PKG, "mfma_probe")  # practical MFMA / copy ceilings (measurement only)

@@ -518,6 +518,38 @@ pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const 
     return run(p, c, q, w, k, indices, scores, candidates, candidate_counts, workspace, workspace_bytes, stream);
 }
 
+pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32_t *indices, const float *scores,
+                               int32_t d, int32_t g, int32_t *overlap, int32_t *group_union, int32_t *group_inter,
+                               float *mass, void *stream)
+{
+    if (batch < 1 || lq < 1) return fail(PIVOT_ERR_INVALID_ARG, "batch and lq must be >= 1");
+    if (k < 1 || k > pivot::stats_row_max())
+        return fail(PIVOT_ERR_UNSUPPORTED, "row width k must be in [1, %d] (got %d)", pivot::stats_row_max(), k);
+    if (!indices) return fail(PIVOT_ERR_INVALID_ARG, "indices is NULL");
+    if (!overlap && !group_union && !group_inter && !mass) return fail(PIVOT_ERR_INVALID_ARG, "no output requested");
+    if (overlap && d < 1) return fail(PIVOT_ERR_INVALID_ARG, "overlap distance d must be >= 1 (got %d)", d);
+    const bool groups = group_union || group_inter;
+    if (groups && (g < 1 || g > 64)) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be in [1, 64] (got %d)", g);
+    if (groups && !pivot::stats_group_fits(g, k))
+        return fail(PIVOT_ERR_UNSUPPORTED,
+                    "group sets need pow2ceil(g) * roundup(k, 32) <= 16384 (got g = %d, k = %d)", g, k);
+    if (mass && !scores) return fail(PIVOT_ERR_INVALID_ARG, "mass needs scores");
+    pivot::StatsArgs a{};
+    a.idx = indices;
+    a.scores = scores;
+    a.B = batch;
+    a.Lq = lq;
+    a.k = k;
+    a.d = overlap ? d : 1;
+    a.g = groups ? g : 1;
+    a.G = (lq + a.g - 1) / a.g;
+    a.overlap = overlap;
+    a.group_union = group_union;
+    a.group_inter = group_inter;
+    a.mass = mass;
+    return hip_status(pivot::launch_stats(a, static_cast<hipStream_t>(stream)), "stats launch");
+}
+
 pivot_status pivot_pool(const pivot_problem *p, int32_t g, const void *q, const float *w, void *qbar, float *wbar,
                         void *stream)
 {

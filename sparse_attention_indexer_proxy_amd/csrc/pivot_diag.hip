@@ -1,0 +1,310 @@
+// O1-O3 diagnostics of selected index rows (PIVOT paper summary, "Key
+// observations", Figure 2): how much adjacent queries' top-k sets overlap,
+// how large a group's union and intersection are, and how fast each row's
+// indexer-score mass saturates. Rows are the indexer's outputs: the selected
+// positions in ascending order, then -1.
+//
+//   k_row_overlap   one wave per row t: |T_t ∩ T_{t+d}|; the partner row sits
+//                   in LDS and every entry of T_t is found by a branch-free
+//                   binary search over it.
+//   k_group_sets    one workgroup per group: its rows merged pairwise in LDS
+//                   into one sorted multiset; distinct values = union, values
+//                   occurring in every row = intersection.
+//   k_row_mass      one wave per row: the row's scores as ordered keys in
+//                   registers; the j-th largest (three j at once) by bisection
+//                   over the key bits; the mass of the best j = the sum above
+//                   it plus its ties.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pivot_kernels.h"
+
+namespace pivot {
+namespace {
+
+constexpr int kW = 64;            // wavefront
+constexpr int kRowMax = 4096;     // row width limit (LDS / registers)
+constexpr int kGroupMax = 16384;  // padded g * k limit of the group kernel (LDS)
+constexpr int kDiagWaves = 4;
+
+__device__ __forceinline__ int lane() { return threadIdx.x & (kW - 1); }
+__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+// A row's entries, lane l holding entries 64 i + l (all loads issued at once;
+// past k reads as -1), and its valid length: the prefix before the first -1.
+template <int NV>
+__device__ __forceinline__ int load_row(const int32_t *row, int k, int32_t (&v)[NV])
+{
+    const int l = lane();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = kW * i + l < k ? row[kW * i + l] : -1;
+    int n = NV * kW < k ? NV * kW : k;
+#pragma unroll
+    for (int i = NV - 1; i >= 0; --i) n = v[i] < 0 ? kW * i + l : n;  // this lane's first pad
+    for (int o = kW / 2; o > 0; o >>= 1) {
+        const int x = __shfl_xor(n, o);
+        n = x < n ? x : n;
+    }
+    return n;
+}
+
+// Whether x is among the n ascending entries p[0..n).
+__device__ __forceinline__ bool sorted_has(const int32_t *p, int n, int32_t x)
+{
+    int pos = 0;
+    for (int step = 1 << 12; step > 0; step >>= 1)
+        if (pos + step <= n && p[pos + step - 1] < x) pos += step;
+    return pos < n && p[pos] == x;
+}
+
+template <int NV>
+__global__ __launch_bounds__(kDiagWaves * kW) void k_row_overlap(StatsArgs a)
+{
+    extern __shared__ int32_t dyn[];  // kDiagWaves rows of a.k entries
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane();
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kDiagWaves + wv;
+    if (row >= a.B * a.Lq) return;  // wave-uniform; no workgroup barrier below
+    const int64_t b = row / a.Lq, t = row - b * a.Lq;
+    if (t + a.d >= a.Lq) {
+        if (l == 0) a.overlap[row] = -1;
+        return;
+    }
+    int32_t v0[NV], v1[NV];
+    const int n0 = load_row(a.idx + row * a.k, a.k, v0);
+    const int n1 = load_row(a.idx + (row + a.d) * a.k, a.k, v1);
+    int32_t *p = dyn + wv * a.k;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (kW * i + l < n1) p[kW * i + l] = v1[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int j = kW * i + l;
+        cnt += popc64(__ballot(j < n0 && sorted_has(p, n1, v0[i])));
+    }
+    if (l == 0) a.overlap[row] = cnt;
+}
+
+// A group's rows are merged into one sorted multiset (rows are sets, so a
+// value occurs at most once per row): the union is the number of distinct
+// values, the intersection the number of values occurring in every row
+// (v[p] == v[p + gm - 1]). The rows, padded with a sentinel to kp entries
+// (a multiple of the per-thread segment) and to a power-of-two count P,
+// are merged pairwise in LDS, log2 P levels, each output segment found by a
+// merge-path search (equal values: the left run first).
+constexpr int kSetThreads = 512;
+constexpr int kSeg = kGroupMax / kSetThreads;  // outputs per thread per level (32)
+constexpr int32_t kSentinel = 0x7FFFFFFF;
+
+__global__ __launch_bounds__(kSetThreads) void k_group_sets(StatsArgs a)
+{
+    __shared__ int32_t buf[2][kGroupMax];
+    __shared__ int32_t cnt[2];
+    const int64_t gid = blockIdx.x;
+    const int64_t b = gid / a.G, m = gid - b * a.G;
+    const int64_t t0 = m * a.g;
+    const int gm = static_cast<int>((t0 + a.g < a.Lq ? t0 + a.g : a.Lq) - t0);
+    const int kp = (a.k + kSeg - 1) / kSeg * kSeg;  // padded run length
+    int P = 1;
+    while (P < gm) P <<= 1;
+    const int N = P * kp;  // <= kGroupMax (checked by the caller)
+    const int tid = threadIdx.x;
+    if (tid < 2) cnt[tid] = 0;
+    // every thread loads its (at most kSeg) entries with all loads in flight
+    const int32_t *g0 = a.idx + (b * a.Lq + t0) * a.k;
+    int32_t ld[kSeg];
+#pragma unroll
+    for (int q = 0; q < kSeg; ++q) {
+        const int e = tid + q * kSetThreads;
+        const int r = e / kp, j = e - r * kp;
+        ld[q] = (e < N && r < gm && j < a.k) ? g0[r * a.k + j] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kSeg; ++q) {
+        const int e = tid + q * kSetThreads;
+        if (e < N) buf[0][e] = ld[q] < 0 ? kSentinel : ld[q];
+    }
+    __syncthreads();
+    int src = 0;
+    for (int L = kp; L < N; L <<= 1) {
+        const int32_t *in = buf[src];
+        int32_t *out = buf[src ^ 1];
+        for (int o0 = tid * kSeg; o0 < N; o0 += kSetThreads * kSeg) {
+            const int pair = o0 / (2 * L), d = o0 - pair * 2 * L;
+            const int32_t *A = in + pair * 2 * L, *Bv = A + L;
+            int lo = d > L ? d - L : 0, hi = d < L ? d : L;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (A[mid] <= Bv[d - 1 - mid]) lo = mid + 1;
+                else hi = mid;
+            }
+            int i = lo, j = d - lo;
+            for (int e = 0; e < kSeg; ++e) {
+                const bool take_a = j >= L || (i < L && A[i] <= Bv[j]);
+                out[o0 + e] = take_a ? A[i] : Bv[j];
+                i += take_a ? 1 : 0;
+                j += take_a ? 0 : 1;
+            }
+        }
+        __syncthreads();
+        src ^= 1;
+    }
+    const int32_t *v = buf[src];
+    int nu = 0, ni = 0;
+    for (int p = tid; p < N; p += kSetThreads) {
+        const int32_t x = v[p];
+        if (x == kSentinel) continue;
+        nu += (p == 0 || v[p - 1] != x) ? 1 : 0;
+        ni += (p + gm - 1 < N && v[p + gm - 1] == x) ? 1 : 0;
+    }
+    for (int o = kW / 2; o > 0; o >>= 1) {
+        nu += __shfl_xor(nu, o);
+        ni += __shfl_xor(ni, o);
+    }
+    if (lane() == 0) {
+        atomicAdd(&cnt[0], nu);
+        atomicAdd(&cnt[1], ni);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        if (a.group_union) a.group_union[gid] = cnt[0];
+        if (a.group_inter) a.group_inter[gid] = cnt[1];
+    }
+}
+
+// Orderable key of a float: larger floats give larger keys, and every float
+// maps to a key >= 0x007FFFFF (0 marks an empty slot).
+__device__ __forceinline__ uint32_t okey(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int o = kW / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <int NV>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&kv)[NV], uint32_t x)
+{
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) n += popc64(__ballot(kv[i] >= x));
+    return n;
+}
+
+__device__ __forceinline__ float okey_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int NV>
+__global__ __launch_bounds__(kDiagWaves * kW) void k_row_mass(StatsArgs a)
+{
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane();
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kDiagWaves + wv;
+    if (row >= a.B * a.Lq) return;  // wave-uniform
+    const int32_t *ri = a.idx + row * a.k;
+    const float *rs = a.scores + row * a.k;
+    uint32_t kv[NV];
+    float part = 0.0f;
+    int n;
+    {
+        int32_t iv[NV];
+        float sv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) sv[i] = kW * i + l < a.k ? rs[kW * i + l] : 0.0f;
+        n = load_row(ri, a.k, iv);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const bool in = kW * i + l < n;
+            kv[i] = in ? okey(sv[i]) : 0u;
+            part += in ? sv[i] : 0.0f;
+        }
+    }
+    const float total = wave_sum(part);
+    // floor(f k) for f = 1/4, 1/2, 3/4 (exact integer arithmetic)
+    const int jsel[3] = {a.k / 4, a.k / 2, 3 * a.k / 4};
+    // the jsel-th largest key of each: the largest T with #{key >= T} >= jsel;
+    // the three searches share each pass over the keys
+    uint32_t T[3] = {0u, 0u, 0u};
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t x0 = T[0] | (1u << bit), x1 = T[1] | (1u << bit), x2 = T[2] | (1u << bit);
+        // per-lane counts, packed 3 x 10 bits (<= NV <= 64 each), then one
+        // butterfly sum over the wave (totals <= 4096 fit 13 bits: widen first)
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            c += (kv[i] >= x0 ? 1u : 0u) | (kv[i] >= x1 ? 1u << 10 : 0u) | (kv[i] >= x2 ? 1u << 20 : 0u);
+        uint64_t cw = (c & 0x3FFu) | (uint64_t((c >> 10) & 0x3FFu) << 21) | (uint64_t(c >> 20) << 42);
+        for (int o = kW / 2; o > 0; o >>= 1) cw += __shfl_xor(cw, o);
+        const int c0 = static_cast<int>(cw & 0x1FFFFF), c1 = static_cast<int>((cw >> 21) & 0x1FFFFF),
+                  c2 = static_cast<int>(cw >> 42);
+        T[0] = c0 >= jsel[0] ? x0 : T[0];
+        T[1] = c1 >= jsel[1] ? x1 : T[1];
+        T[2] = c2 >= jsel[2] ? x2 : T[2];
+    }
+    for (int f = 0; f < 3; ++f) {
+        float top = total;
+        if (jsel[f] == 0) {
+            top = 0.0f;
+        } else if (jsel[f] < n) {
+            const uint32_t t = T[f];
+            int above = 0;
+            float sabove = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                above += popc64(__ballot(kv[i] > t));
+                sabove += kv[i] > t ? okey_float(kv[i]) : 0.0f;
+            }
+            top = wave_sum(sabove) + static_cast<float>(jsel[f] - above) * okey_float(t);
+        }
+        a.mass[row * 3 + f] = total > 0.0f ? top / total : NAN;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stats(const StatsArgs &a, hipStream_t st)
+{
+    const int64_t rows = a.B * a.Lq;
+    const dim3 block(kDiagWaves * kW);
+    const dim3 rgrid(static_cast<uint32_t>((rows + kDiagWaves - 1) / kDiagWaves));
+    if (a.overlap) {
+        const size_t lds = static_cast<size_t>(kDiagWaves) * a.k * sizeof(int32_t);
+        if (a.k <= 1024)
+            hipLaunchKernelGGL(k_row_overlap<16>, rgrid, block, lds, st, a);
+        else
+            hipLaunchKernelGGL(k_row_overlap<64>, rgrid, block, lds, st, a);
+    }
+    if (a.group_union || a.group_inter)
+        hipLaunchKernelGGL(k_group_sets, dim3(static_cast<uint32_t>(a.B * a.G)), dim3(kSetThreads), 0, st, a);
+    if (a.mass) {
+        if (a.k <= 1024)
+            hipLaunchKernelGGL(k_row_mass<16>, rgrid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(k_row_mass<64>, rgrid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+int stats_row_max() { return kRowMax; }
+
+int stats_group_fits(int g, int k)
+{
+    int P = 1;
+    while (P < g) P <<= 1;
+    const int64_t kp = (int64_t(k) + kSeg - 1) / kSeg * kSeg;
+    return P * kp <= kGroupMax;
+}
+
+}  // namespace pivot

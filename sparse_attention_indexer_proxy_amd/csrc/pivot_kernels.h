@@ -84,6 +84,24 @@ struct RowSelectLaunch {
     int c;
 };
 
+// O1-O3 diagnostics of index rows (pivot_diag.hip).
+struct StatsArgs {
+    const int32_t *idx;     // [B, Lq, k] ascending valid prefix, then -1
+    const float *scores;    // [B, Lq, k] aligned with idx (mass only)
+    int64_t B, Lq;
+    int k, d, g;
+    int64_t G;              // ceil(Lq / g)
+    int32_t *overlap;       // [B, Lq] |T_t ∩ T_{t+d}|, -1 past the sequence; nullable
+    int32_t *group_union;   // [B, G]; nullable
+    int32_t *group_inter;   // [B, G]; nullable
+    float *mass;            // [B, Lq, 3]; nullable
+};
+hipError_t launch_stats(const StatsArgs &a, hipStream_t st);
+int stats_row_max();    // largest row width k
+// Whether groups of g rows of width k fit the group-set kernel: the next
+// power of two >= g, times k rounded up to 32, at most 16384.
+int stats_group_fits(int g, int k);
+
 bool mfma_shape(const LaunchShape &sh);
 // agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,

@@ -187,3 +187,17 @@ def test_config_call_validates_before_launch(pivot_lib):
     assert pivot_lib.pivot_index(ctypes.byref(prob), ctypes.byref(cfg), fake, fake, fake, idx, None, None, None,
                                  fake, 16, None) == 3
     assert pivot_lib.pivot_pool_ex(ctypes.byref(prob), 4, 5, fake, fake, fake, fake, None) == 1
+
+
+def test_index_stats_validates_before_launch(pivot_lib):
+    fake = ctypes.c_void_p(1 << 20)
+    out = ctypes.c_void_p(1 << 21)
+    call = pivot_lib.pivot_index_stats
+    assert call(1, 8, 16, None, None, 1, 1, out, None, None, None, None) == 1       # null indices
+    assert call(1, 8, 16, fake, None, 1, 1, None, None, None, None, None) == 1      # no output
+    assert call(1, 8, 5000, fake, None, 1, 1, out, None, None, None, None) == 2     # k too wide
+    assert call(1, 8, 16, fake, None, 0, 1, out, None, None, None, None) == 1       # d < 1
+    assert call(1, 8, 16, fake, None, 1, 65, None, out, None, None, None) == 1      # g > 64
+    assert call(1, 8, 4096, fake, None, 1, 8, None, None, out, None, None) == 2     # g * k > 16384
+    assert call(1, 8, 16, fake, None, 1, 1, None, None, None, out, None) == 1       # mass without scores
+    assert call(0, 8, 16, fake, None, 1, 1, out, None, None, None, None) == 1
