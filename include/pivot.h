@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 4
+#define PIVOT_ABI_VERSION 5
 
 typedef enum {
     PIVOT_OK = 0,
@@ -154,6 +154,44 @@ pivot_status pivot_index_workspace_size(const pivot_problem *p, const pivot_conf
 pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
                          const void *k, int32_t *indices, float *scores, int32_t *candidates,
                          int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Keys of a ragged and/or paged batch (batched decode with per-sequence
+ * prefixes, in the page layout of a serving KV cache). The pages print no
+ * batch format; this one is the library's own.
+ *   k           contiguous: [batch, lk, dim] (row stride lk per sequence);
+ *               paged: a pool [num_pages, page_size, dim]; q's dtype, device.
+ *   seq_lens    [batch] int32 (device) or NULL: sequence b holds seq_lens[b]
+ *               keys (its key positions 0 .. seq_lens[b] - 1), and its lq
+ *               query rows sit at its last lq positions; NULL: lk each.
+ *               Values are expected in [lq, lk]; values outside [0, lk] are
+ *               clamped (no key outside the storage is read), and a row whose
+ *               position falls below 0 selects nothing (all -1).
+ *   page_table  [batch, max_pages] int32 (device) or NULL (contiguous): the
+ *               pool page holding keys [j * page_size, (j + 1) * page_size)
+ *               of sequence b is page_table[b * max_pages + j]; entries
+ *               outside [0, num_pages) are clamped into the pool. Only the
+ *               pages covering each sequence's keys are read.
+ *   page_size   keys per page (>= 1); max_pages >= ceil(lk / page_size).
+ * Positions in the outputs are logical (0 .. seq_lens[b] - 1). */
+typedef struct {
+    const void *k;
+    const int32_t *seq_lens;
+    const int32_t *page_table;
+    int64_t num_pages;
+    int32_t page_size;
+    int32_t max_pages;
+} pivot_keys;
+
+/* pivot_index over a ragged / paged batch (p->lk is the key capacity per
+ * sequence). With paged keys the bf16 64-head / 128-dim shape takes the
+ * split-key scan (the decode path) whatever the number of groups. */
+pivot_status pivot_index_kv(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                            const pivot_keys *keys, int32_t *indices, float *scores, int32_t *candidates,
+                            int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace pivot_index_kv needs. */
+pivot_status pivot_index_kv_workspace_size(const pivot_problem *p, const pivot_config *cfg, const pivot_keys *keys,
+                                           size_t *bytes);
 
 /* eq. (4) alone: qbar [batch, G, heads, dim] in the q dtype, wbar [batch, G,
  * heads] f32. Needs no workspace. */

@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "resolve_variant", "pool", "index_stats",
+__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "index_kv", "resolve_variant", "pool",
+           "index_stats",
            "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
            "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "DENSE_BELOW_DEFAULT",
            "STAGES"]
@@ -34,6 +35,7 @@ _lib = None
 
 EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
             "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
+            "pivot_index_kv", "pivot_index_kv_workspace_size",
             "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_index_stats", "pivot_timing_enable",
             "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
@@ -56,6 +58,12 @@ class Config(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("g", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("c", ctypes.c_int32), ("aggregation", ctypes.c_int32), ("member_causal", ctypes.c_int32),
                 ("auto_variant", ctypes.c_int32), ("reserved", ctypes.c_int32), ("dense_below", ctypes.c_int64)]
+
+
+class Keys(ctypes.Structure):
+    """pivot_keys of the header."""
+    _fields_ = [("k", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -82,11 +90,14 @@ def load_library(path: str | None = None):
     lib.pivot_resolve_variant.argtypes = [P, C, ctypes.POINTER(i32)]
     lib.pivot_index_workspace_size.argtypes = [P, C, ctypes.POINTER(sz)]
     lib.pivot_index.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    KP = ctypes.POINTER(Keys)
+    lib.pivot_index_kv.argtypes = [P, C, vp, vp, KP, vp, vp, vp, vp, vp, sz, vp]
+    lib.pivot_index_kv_workspace_size.argtypes = [P, C, KP, ctypes.POINTER(sz)]
     lib.pivot_pool.argtypes = [P, i32, vp, vp, vp, vp, vp]
     lib.pivot_pool_ex.argtypes = [P, i32, i32, vp, vp, vp, vp, vp]
     lib.pivot_proxy_scores.argtypes = [P, i32, vp, vp, vp, vp, vp]
     lib.pivot_index_stats.argtypes = [ctypes.c_int64, ctypes.c_int64, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
-    for name in ("pivot_index_stats","pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
+    for name in ("pivot_index_stats", "pivot_index_kv", "pivot_index_kv_workspace_size","pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
                  "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
                  "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores"):
         getattr(lib, name).restype = ctypes.c_int
@@ -285,6 +296,77 @@ def index(q, w, k, cfg: Config | None = None, *, return_scores: bool = False, re
     if return_candidates:
         outs += [None if cand is None else _finish(sq, cand), None if cand_n is None else _finish(sq, cand_n)]
     return _finish(sq, *outs) if len(outs) > 1 else _finish(sq, idx)
+
+
+def index_kv(q, w, k, seq_lens=None, page_table=None, *, page_size: int = 0, lk: int | None = None,
+             cfg: Config | None = None, return_scores: bool = False, return_candidates: bool = False,
+             workspace=None, stream=None, **knobs):
+    """The indexer over a ragged and/or paged batch (pivot_index_kv).
+
+    q [B, Lq, H, d], w [B, Lq, H]; k is either contiguous [B, Lk, d] or, with
+    page_table [B, max_pages] int32, a page pool [num_pages, page_size, d];
+    seq_lens [B] int32 gives each sequence's key count (its queries are its
+    last Lq positions). lk is the key capacity per sequence (default: k's
+    second dimension, or max_pages * page_size when paged). Outputs as for
+    index()."""
+    if cfg is None:
+        cfg = make_config(**knobs)
+    elif knobs:
+        raise TypeError("pass either cfg or keywords")
+    if q.dim() != 4 or w.dim() != 3:
+        raise ValueError("expected q [B, Lq, H, d] and w [B, Lq, H]")
+    B, Lq, H, D = q.shape
+    for name, t in (("q", q), ("w", w), ("k", k)):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a device tensor on q's device")
+    if k.dtype != q.dtype or w.dtype != torch.float32 or tuple(w.shape) != (B, Lq, H) or k.shape[-1] != D:
+        raise ValueError("q, w, k dtypes or shapes do not match")
+    q, w, k = q.contiguous(), w.contiguous(), k.contiguous()
+    keys = Keys()
+    keys.k = k.data_ptr()
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,) or seq_lens.device != q.device:
+            raise ValueError("seq_lens must be an int32 device tensor [B]")
+        seq_lens = seq_lens.contiguous()
+        keys.seq_lens = seq_lens.data_ptr()
+    if page_table is not None:
+        if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+            raise ValueError("page_table must be an int32 device tensor [B, max_pages]")
+        if k.dim() != 3 or k.shape[1] != page_size:
+            raise ValueError("paged k must be [num_pages, page_size, d]")
+        page_table = page_table.contiguous()
+        keys.page_table = page_table.data_ptr()
+        keys.num_pages, keys.page_size, keys.max_pages = k.shape[0], page_size, page_table.shape[1]
+        cap = lk if lk is not None else page_table.shape[1] * page_size
+    else:
+        if k.dim() != 3 or k.shape[0] != B:
+            raise ValueError("contiguous k must be [B, Lk, d]")
+        cap = lk if lk is not None else k.shape[1]
+    prob = Problem(B, Lq, cap, H, D, _dtype_code(q.dtype))
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    _check(lib.pivot_index_kv_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(keys),
+                                             ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    cand = cand_n = None
+    if return_candidates:
+        resolved = ctypes.c_int32(0)
+        _check(lib.pivot_resolve_variant(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(resolved)))
+        if resolved.value == REFINE:
+            G = -(-Lq // cfg.g)
+            cand = torch.empty((B, G, cfg.c), dtype=torch.int32, device=q.device)
+            cand_n = torch.empty((B, G), dtype=torch.int32, device=q.device)
+    _check(lib.pivot_index_kv(ctypes.byref(prob), ctypes.byref(cfg), _ptr(q), _ptr(w), ctypes.byref(keys), _ptr(idx),
+                              _ptr(sc), _ptr(cand), _ptr(cand_n), _ptr(workspace), wsb, _stream_ptr(stream, q.device)))
+    outs = [idx]
+    if return_scores:
+        outs.append(sc)
+    if return_candidates:
+        outs += [cand, cand_n]
+    return tuple(outs) if len(outs) > 1 else idx
 
 
 def pool(q, w, g: int, stream=None, aggregation: str = "mean"):

@@ -164,7 +164,9 @@ pivot_status resolve(const pivot_problem *p, const pivot_config *cfg, Cfg *out)
     return PIVOT_OK;
 }
 
-pivot_status plan(const pivot_problem *p, const Cfg &cfg, Layout *L)
+// paged: keys in pages (the MFMA shape then takes the split scan, which
+// translates every key row it reads).
+pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
 {
     pivot_status st = check_problem(p);
     if (st != PIVOT_OK) return st;
@@ -209,7 +211,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, Layout *L)
     };
     l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
-    l.few = pivot::mfma_shape(sh) && static_cast<int64_t>(groups) < few_groups_threshold();
+    l.few = pivot::mfma_shape(sh) && (paged || static_cast<int64_t>(groups) < few_groups_threshold());
     if (l.few) {
         const int64_t tiles = (p->lk + 63) / 64;
         int64_t ss = (2048 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
@@ -243,12 +245,43 @@ pivot_status hip_status(hipError_t e, const char *what)
     return fail(PIVOT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const void *k,
+// The keys of a call: contiguous [batch, lk, dim] (lens, pages.table null)
+// or ragged / paged (pivot_keys).
+struct KeysIn {
+    const void *k;
+    const int32_t *lens;
+    pivot::KeyPages pages;
+};
+
+KeysIn contiguous(const void *k) { return KeysIn{k, nullptr, pivot::KeyPages{nullptr, 0, 0, 0}}; }
+
+pivot_status check_keys(const pivot_problem *p, const pivot_keys *keys, KeysIn *out)
+{
+    if (!keys) return fail(PIVOT_ERR_INVALID_ARG, "keys is NULL");
+    KeysIn kin = contiguous(keys->k);
+    kin.lens = keys->seq_lens;
+    if (keys->page_table) {
+        if (keys->page_size < 1) return fail(PIVOT_ERR_INVALID_ARG, "page_size must be >= 1 (got %d)", keys->page_size);
+        if (keys->num_pages < 1) return fail(PIVOT_ERR_INVALID_ARG, "num_pages must be >= 1");
+        const int64_t need = (p->lk + keys->page_size - 1) / keys->page_size;
+        if (keys->max_pages < need)
+            return fail(PIVOT_ERR_INVALID_ARG, "max_pages (%d) must cover lk keys (%lld pages)", keys->max_pages,
+                        (long long)need);
+        if (keys->num_pages * int64_t(keys->page_size) >= (int64_t(1) << 40))
+            return fail(PIVOT_ERR_UNSUPPORTED, "key pool too large");
+        kin.pages = pivot::KeyPages{keys->page_table, keys->num_pages, keys->page_size, keys->max_pages};
+    }
+    *out = kin;
+    return PIVOT_OK;
+}
+
+pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const KeysIn &kin,
                  int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts, void *ws,
                  size_t ws_bytes, void *stream)
 {
     Layout L;
-    pivot_status st = plan(p, cfg, &L);
+    const void *k = kin.k;
+    pivot_status st = plan(p, cfg, kin.pages.table != nullptr, &L);
     if (st != PIVOT_OK) return st;
     const int variant = cfg.variant;
     const int32_t topk = cfg.topk, c = cfg.c;
@@ -260,7 +293,9 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0)
         return fail(PIVOT_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
 
-    const pivot::LaunchShape sh = shape_of(p);
+    pivot::LaunchShape sh = shape_of(p);
+    sh.lens = kin.lens;
+    sh.pages = kin.pages;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *base = static_cast<char *>(ws);
 
@@ -441,7 +476,7 @@ pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32
     if (!bytes) return fail(PIVOT_ERR_INVALID_ARG, "bytes is NULL");
     if (variant < PIVOT_DENSE || variant > PIVOT_REFINE) return fail(PIVOT_ERR_INVALID_ARG, "unknown variant %d", variant);
     Layout L;
-    pivot_status st = plan(p, basic(variant, g, topk, c), &L);
+    pivot_status st = plan(p, basic(variant, g, topk, c), false, &L);
     if (st != PIVOT_OK) return st;
     *bytes = L.total;
     return PIVOT_OK;
@@ -450,24 +485,24 @@ pivot_status pivot_workspace_size(const pivot_problem *p, int32_t variant, int32
 pivot_status pivot_index_dense(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t topk,
                                int32_t *indices, float *scores, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run(p, basic(PIVOT_DENSE, 1, topk, 0), q, w, k, indices, scores, nullptr, nullptr, workspace,
-               workspace_bytes, stream);
+    return run(p, basic(PIVOT_DENSE, 1, topk, 0), q, w, contiguous(k), indices, scores, nullptr, nullptr,
+               workspace, workspace_bytes, stream);
 }
 
 pivot_status pivot_index_reuse(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
                                int32_t topk, int32_t *indices, float *scores, void *workspace, size_t workspace_bytes,
                                void *stream)
 {
-    return run(p, basic(PIVOT_REUSE, g, topk, 0), q, w, k, indices, scores, nullptr, nullptr, workspace,
-               workspace_bytes, stream);
+    return run(p, basic(PIVOT_REUSE, g, topk, 0), q, w, contiguous(k), indices, scores, nullptr, nullptr,
+               workspace, workspace_bytes, stream);
 }
 
 pivot_status pivot_index_refine(const pivot_problem *p, const void *q, const float *w, const void *k, int32_t g,
                                 int32_t topk, int32_t c, int32_t *indices, float *scores, int32_t *candidates,
                                 int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run(p, basic(PIVOT_REFINE, g, topk, c), q, w, k, indices, scores, candidates, candidate_counts, workspace,
-               workspace_bytes, stream);
+    return run(p, basic(PIVOT_REFINE, g, topk, c), q, w, contiguous(k), indices, scores, candidates,
+               candidate_counts, workspace, workspace_bytes, stream);
 }
 
 pivot_status pivot_config_init(pivot_config *cfg)
@@ -502,7 +537,24 @@ pivot_status pivot_index_workspace_size(const pivot_problem *p, const pivot_conf
     pivot_status st = resolve(p, cfg, &c);
     if (st != PIVOT_OK) return st;
     Layout L;
-    st = plan(p, c, &L);
+    st = plan(p, c, false, &L);
+    if (st != PIVOT_OK) return st;
+    *bytes = L.total;
+    return PIVOT_OK;
+}
+
+pivot_status pivot_index_kv_workspace_size(const pivot_problem *p, const pivot_config *cfg, const pivot_keys *keys,
+                                           size_t *bytes)
+{
+    if (!bytes) return fail(PIVOT_ERR_INVALID_ARG, "bytes is NULL");
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    KeysIn kin;
+    st = check_keys(p, keys, &kin);
+    if (st != PIVOT_OK) return st;
+    Layout L;
+    st = plan(p, c, kin.pages.table != nullptr, &L);
     if (st != PIVOT_OK) return st;
     *bytes = L.total;
     return PIVOT_OK;
@@ -515,7 +567,21 @@ pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const 
     Cfg c;
     pivot_status st = resolve(p, cfg, &c);
     if (st != PIVOT_OK) return st;
-    return run(p, c, q, w, k, indices, scores, candidates, candidate_counts, workspace, workspace_bytes, stream);
+    return run(p, c, q, w, contiguous(k), indices, scores, candidates, candidate_counts, workspace, workspace_bytes,
+               stream);
+}
+
+pivot_status pivot_index_kv(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                            const pivot_keys *keys, int32_t *indices, float *scores, int32_t *candidates,
+                            int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    KeysIn kin;
+    st = check_keys(p, keys, &kin);
+    if (st != PIVOT_OK) return st;
+    return run(p, c, q, w, kin, indices, scores, candidates, candidate_counts, workspace, workspace_bytes, stream);
 }
 
 pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32_t *indices, const float *scores,

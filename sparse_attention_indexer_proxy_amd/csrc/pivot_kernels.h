@@ -7,10 +7,20 @@
 
 namespace pivot {
 
+// Key storage: contiguous [B, Lk, D], or pages [num_pages, page, D] named by
+// a per-sequence table [B, max_pages] of physical page ids (device memory).
+struct KeyPages {
+    const int32_t *table;  // null: contiguous
+    int64_t num_pages;
+    int page, max_pages;
+};
+
 struct LaunchShape {
-    int64_t B, Lq, Lk;
+    int64_t B, Lq, Lk;              // Lk: key capacity per sequence
     int H, D;
     bool bf16;
+    const int32_t *lens = nullptr;  // [B] keys of each sequence (device), null: Lk each
+    KeyPages pages{};               // table == null: contiguous keys
 };
 
 // One scan launch: eq. (5) for every group, then either the streaming

@@ -96,12 +96,40 @@ template <> __device__ __forceinline__ float widen<uint16_t>(uint16_t x) { retur
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
 // ------------------------------------------------------ group geometry
+// Sequence b holds lk(b) keys (lens[b], or the capacity Lk); its query row r
+// sits at position lk(b) - Lq + r (a ragged batch: each sequence's queries
+// are the last Lq positions of its own prefix).
 struct Geo {
     int64_t B, G, Lq, Lk;
     int g;
+    const int32_t *lens;  // [B] or null
     __device__ __forceinline__ int64_t first_row(int64_t m) const { return m * g; }
     __device__ __forceinline__ int64_t end_row(int64_t m) const { return (m + 1) * g < Lq ? (m + 1) * g : Lq; }
-    __device__ __forceinline__ int64_t t_last(int64_t m) const { return Lk - Lq + end_row(m) - 1; }
+    // lens outside [0, Lk] are clamped, so no key outside the storage is read
+    __device__ __forceinline__ int64_t lk(int64_t b) const
+    {
+        if (!lens) return Lk;
+        const int64_t v = lens[b];
+        return v < 0 ? 0 : (v > Lk ? Lk : v);
+    }
+    __device__ __forceinline__ int64_t pos(int64_t b, int64_t r) const { return lk(b) - Lq + r; }
+    __device__ __forceinline__ int64_t t_last(int64_t b, int64_t m) const { return lk(b) - Lq + end_row(m) - 1; }
+};
+
+// Row index of key s of sequence b in the key storage: contiguous rows
+// b * Lk + s, or page table[b][s / page] (clamped into the pool, so a
+// malformed table cannot address outside it), row s % page.
+struct Keys {
+    const void *base;
+    KeyPages pg;
+    int64_t Lk;
+    __device__ __forceinline__ int64_t row(int64_t b, int64_t s) const
+    {
+        if (!pg.table) return b * Lk + s;
+        int64_t ph = pg.table[b * pg.max_pages + s / pg.page];
+        ph = ph < 0 ? 0 : (ph >= pg.num_pages ? pg.num_pages - 1 : ph);
+        return ph * pg.page + s % pg.page;
+    }
 };
 
 // ------------------------------------------------------------ wave select
@@ -453,7 +481,7 @@ enum ScanMode { kFilter = 0, kRows = 1 };
 struct ScanArgs {
     const void *qsrc;   // [B, G, H, D] proxies (the queries themselves when g == 1)
     const float *wsrc;  // [B, G, H]
-    const void *k;      // [B, Lk, D]
+    Keys keys;          // [B, Lk, D] contiguous, or paged
     Geo geo;
     int H, D;
     // kFilter
@@ -756,10 +784,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     const int64_t m = blk * kScanWaves + wv;
     const bool active = m < geo.G;
     const int64_t m_hi = (blk * kScanWaves + kScanWaves - 1 < geo.G - 1) ? blk * kScanWaves + kScanWaves - 1 : geo.G - 1;
-    const int64_t wg_tlast = geo.t_last(m_hi);
-    const int64_t my_tlast = active ? geo.t_last(m) : -1;
+    const int64_t wg_tlast = geo.t_last(b, m_hi);
+    const int64_t my_tlast = active ? geo.t_last(b, m) : -1;
     const int ntiles = static_cast<int>(wg_tlast / NT) + 1;
-    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    // contiguous keys only (paged calls take the split scan); rows up to the
+    // capacity exist, those past the sequence are masked
+    const uint16_t *kseq = static_cast<const uint16_t *>(a.keys.base) + b * geo.Lk * D;
     const int64_t gid = b * geo.G + (active ? m : blk * kScanWaves);
 
     bf16x8 afr[RB][4];
@@ -938,13 +968,14 @@ __global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
     const int64_t gid = blockIdx.x / splits;
     const int split = blockIdx.x % splits;
     const int64_t b = gid / geo.G, m = gid % geo.G;
-    const int64_t tl = geo.t_last(m);
+    const int64_t tl = geo.t_last(b, m);
     const int ntiles_all = static_cast<int>(tl / NT) + 1;
     const int per = (ntiles_all + splits - 1) / splits;
     const int t0 = split * per;
     const int t1 = t0 + per < ntiles_all ? t0 + per : ntiles_all;
     if (t0 >= t1) return;  // uniform over the workgroup
-    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
+    const int64_t lkb = geo.lk(b);
     float *row = a.rows + gid * geo.Lk;
 
     bf16x8 afr[RB][4];
@@ -957,8 +988,8 @@ __global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
         for (int j = 0; j < 4; ++j) {
             const int slice = wv * 4 + j;
             int64_t s = base + slice_row(slice, l);
-            s = s < geo.Lk ? s : geo.Lk - 1;
-            const uint16_t *src = kseq + s * D + slice_col(slice, l);
+            s = s < lkb ? s : (lkb > 0 ? lkb - 1 : 0);  // past the sequence: its last key (masked)
+            const uint16_t *src = kbase + a.keys.row(b, s) * D + slice_col(slice, l);
             uint16_t *dst = buf ? tile1 : tile0;
             __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
@@ -1208,7 +1239,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
     if (a.kind == 0) {
         const int64_t gid = blockIdx.x;
         const int64_t b = gid / geo.G, m = gid % geo.G;
-        int n = static_cast<int>(geo.t_last(m) + 1);
+        const int64_t tl1 = geo.t_last(b, m) + 1;
+        int n = static_cast<int>(tl1 > 0 ? tl1 : 0);
         const float *sc = a.rows + gid * geo.Lk;
         const int32_t *pos = nullptr;
 
@@ -1282,7 +1314,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
     const int64_t m = r / geo.g;
     const int64_t gid = b * geo.G + m;
     const int mi = static_cast<int>(r - geo.first_row(m));
-    const int64_t t = geo.Lk - geo.Lq + r;
+    const int64_t t = geo.pos(b, r);
     const int nc = a.cand_n[gid];
     const int32_t *C = a.cand + gid * a.c;
     // candidates s <= t are a prefix of C (ascending): count them
@@ -1525,7 +1557,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
     } else {
         // the candidates s <= t are a prefix of C (ascending): the last
         // 64-entry slab whose first entry is <= t holds its end
-        const int64_t t = geo.Lk - geo.Lq + r;
+        const int64_t t = geo.pos(b, r);
         const int nc = a.cand_n[gid];
         const int jh = kWave * l;
         const bool head = l < NV && jh < nc && C[jh] <= t;
@@ -1658,11 +1690,11 @@ __global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
     const int64_t blk = nblk - 1 - blockIdx.x / geo.B;
     const int64_t m = blk * 4 + wv;
     if (m >= geo.G) return;  // no workgroup barriers below
-    const int64_t tl = geo.t_last(m);
+    const int64_t tl = geo.t_last(b, m);
     const int64_t gid = b * geo.G + m;
     const T *qv = static_cast<const T *>(a.qsrc) + gid * a.H * a.D;
     const float *wv_ = a.wsrc + gid * a.H;
-    const T *kseq = static_cast<const T *>(a.k) + b * geo.Lk * a.D;
+    const T *kbase = static_cast<const T *>(a.keys.base);
 
     Filter f;
     f.K = a.K;
@@ -1679,7 +1711,7 @@ __global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
     for (int64_t base = 0; base <= tl; base += kWave) {
         const int64_t s = base + l;
         const bool valid = s <= tl;
-        const float score = valid ? exact_score<T>(qv, wv_, kseq + s * a.D, a.H, a.D) : 0.0f;
+        const float score = valid ? exact_score<T>(qv, wv_, kbase + a.keys.row(b, s) * a.D, a.H, a.D) : 0.0f;
         if (Mode == kFilter) {
             f.push(valid, score, static_cast<int32_t>(s));
         } else if (valid) {
@@ -1697,7 +1729,7 @@ __global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
 struct RefineArgs {
     const void *q;   // [B, Lq, H, D]
     const float *w;  // [B, Lq, H]
-    const void *k;   // [B, Lk, D]
+    Keys keys;       // [B, Lk, D] contiguous, or paged
     Geo geo;
     int H, D;
     int topk, c;
@@ -1797,7 +1829,7 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
     const int gm = static_cast<int>(r1 - r0);
     const int nc = a.cand_n[gid];
     const int32_t *C = a.cand + gid * a.c;
-    const uint16_t *kseq = static_cast<const uint16_t *>(a.k) + b * geo.Lk * D;
+    const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
     // this workgroup's tiles of C: [tile_lo, tile_hi)
     const int ntiles_all = (nc + NT - 1) / NT;
     const int per_split = (ntiles_all + a.splits - 1) / a.splits;
@@ -1821,7 +1853,7 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
 #pragma unroll
         for (int j = 0; j < kMaxSlices; ++j) {
             const int slice = wv + nwaves * j;
-            const uint16_t *src = kseq + static_cast<int64_t>(pos[j]) * D + slice_col(slice, l);
+            const uint16_t *src = kbase + a.keys.row(b, pos[j]) * D + slice_col(slice, l);
             __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
@@ -1830,7 +1862,7 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
         const int mi = round * nwaves + wv;
         const bool active = mi < gm;
         const int64_t r = r0 + (active ? mi : 0);
-        const int64_t t = geo.Lk - geo.Lq + r;
+        const int64_t t = geo.pos(b, r);
         float *srow = a.scratch + (gid * geo.g + (active ? mi : 0)) * a.c;
 
         bf16x8 afr[RB][4];
@@ -1904,10 +1936,10 @@ __global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
     const int gm = static_cast<int>(r1 - r0);
     const int nc = a.cand_n[gid];
     const int32_t *C = a.cand + gid * a.c;
-    const T *kseq = static_cast<const T *>(a.k) + b * geo.Lk * a.D;
+    const T *kbase = static_cast<const T *>(a.keys.base);
     for (int mi = wv; mi < gm; mi += 4) {
         const int64_t r = r0 + mi;
-        const int64_t t = geo.Lk - geo.Lq + r;
+        const int64_t t = geo.pos(b, r);
         const T *qv = static_cast<const T *>(a.q) + (b * geo.Lq + r) * a.H * a.D;
         const float *wv_ = a.w + (b * geo.Lq + r) * a.H;
         float *srow = a.scratch + (gid * geo.g + mi) * a.c;
@@ -1916,7 +1948,7 @@ __global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
             const int j = jb + l;
             const bool in = j < nc;
             const int32_t pos = in ? C[j] : 0;
-            if (in) srow[j] = exact_score<T>(qv, wv_, kseq + static_cast<int64_t>(pos) * a.D, a.H, a.D);
+            if (in) srow[j] = exact_score<T>(qv, wv_, kbase + a.keys.row(b, pos) * a.D, a.H, a.D);
             nvalid += popc(ballot(in && pos <= t));
         }
         finish_member(a, b, r, C, srow, nvalid, hist[wv]);
@@ -1929,7 +1961,7 @@ __global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st)
 {
-    Geo geo{sh.B, G, sh.Lq, sh.Lk, g};
+    Geo geo{sh.B, G, sh.Lq, sh.Lk, g, sh.lens};
     const int vec = sh.bf16 ? 8 : 4;
     const int64_t total = sh.B * G * sh.H * (sh.D / vec);
     const int64_t blocks = (total + 255) / 256;
@@ -1950,8 +1982,8 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     ScanArgs a{};
     a.qsrc = L.qsrc;
     a.wsrc = L.wsrc;
-    a.k = L.k;
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.keys = Keys{L.k, sh.pages, sh.Lk};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.H = sh.H;
     a.D = sh.D;
     a.K = L.K;
@@ -1989,8 +2021,8 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     RefineArgs a{};
     a.q = L.q;
     a.w = L.w;
-    a.k = L.k;
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.keys = Keys{L.k, sh.pages, sh.Lk};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.H = sh.H;
     a.D = sh.D;
     a.topk = L.topk;
@@ -2028,8 +2060,8 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     ScanArgs a{};
     a.qsrc = L.qsrc;
     a.wsrc = L.wsrc;
-    a.k = L.k;
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.keys = Keys{L.k, sh.pages, sh.Lk};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.H = sh.H;
     a.D = sh.D;
     a.rows = L.rows;
@@ -2049,7 +2081,7 @@ hipError_t launch_select_groups(const LaunchShape &sh, const ScanLaunch &L, hipS
 {
     if (!mfma_shape(sh) || L.rows || !L.buf_n) return hipErrorInvalidValue;
     GroupSelectArgs a{};
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.K = L.K;
     a.cap = L.cap;
     a.buf = L.buf;
@@ -2077,7 +2109,7 @@ int member_select_slabs(int c)
 hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch &L, hipStream_t st)
 {
     MemberSelectArgs a{};
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.topk = L.topk;
     a.c = L.c;
     a.cand = L.cand;
@@ -2102,7 +2134,7 @@ hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch
 hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, hipStream_t st)
 {
     RowSelectArgs a{};
-    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g};
+    a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.kind = L.kind;
     a.rows = L.rows;
     a.K = L.K;

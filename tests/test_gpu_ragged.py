@@ -1,0 +1,147 @@
+"""GPU parity of ragged and paged batches (pivot_index_kv): each sequence b
+holds its own number of keys and its queries are the last Lq positions of its
+own prefix; keys are contiguous [B, Lk, d] or scattered over a page pool
+through a page table. The oracle runs each sequence on its own key prefix
+(the same definitions, sequence by sequence), and the paged results must
+also equal the contiguous ones bit for bit.
+
+Exact inputs (q, k in {-3..3}/4, w powers of two) make every score exact, so
+indices, scores and candidate sets must match bit for bit on the MFMA
+kernels (split-key scan for paged keys; the fused scan too for contiguous
+ragged keys) and on the exact-order kernels.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import to_device
+from workloads import BF16, F32, exact_random
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparse_attention_indexer_proxy_amd as pv  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(pivot_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _oracle_ragged(variant, q, w, k, lens, g, topk, c):
+    """Per-sequence oracle: sequence b scored on keys 0 .. lens[b] - 1."""
+    B, Lq = q.shape[:2]
+    out_i = np.full((B, Lq, topk), -1, dtype=np.int32)
+    out_s = np.full((B, Lq, topk), -np.inf, dtype=np.float32)
+    for b in range(B):
+        qb, wb, kb = q[b:b + 1], w[b:b + 1], k[b:b + 1, :lens[b]]
+        if variant == "dense":
+            r = oracle.dense(qb, wb, kb, topk)
+        elif variant == "reuse":
+            r = oracle.reuse(qb, wb, kb, g, topk)
+        else:
+            r = oracle.refine(qb, wb, kb, g, topk, c)
+        out_i[b], out_s[b] = r["indices"][0], r["scores"][0]
+    return out_i, out_s
+
+
+def _paged(k, page, seed):
+    """The same keys in a shuffled page pool: (pool [P, page, d], table [B, maxp])."""
+    B, Lk, d = k.shape
+    maxp = -(-Lk // page)
+    r = np.random.default_rng(seed)
+    n_pages = B * maxp + 3
+    perm = r.permutation(n_pages)[:B * maxp].reshape(B, maxp).astype(np.int32)
+    pool = np.zeros((n_pages, page, d), dtype=k.dtype)
+    for b in range(B):
+        for j in range(maxp):
+            rows = k[b, j * page:(j + 1) * page]
+            pool[perm[b, j], :rows.shape[0]] = rows
+    return pool, perm
+
+
+def _dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+CASES = [
+    # name, B, Lq, Lk, H, d, g, topk, c, dtype
+    ("mfma_decode", 5, 4, 900, 64, 128, 4, 24, 48, BF16),
+    ("mfma_prefill", 2, 300, 700, 64, 128, 8, 16, 32, BF16),
+    ("exact_decode", 4, 4, 300, 3, 8, 4, 6, 12, F32),
+    ("exact_prefill_bf16", 3, 40, 90, 2, 16, 4, 5, 9, BF16),
+]
+
+
+@pytest.mark.parametrize("variant", ["dense", "reuse", "refine"])
+@pytest.mark.parametrize("page", [0, 16, 64])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_ragged_and_paged_match_oracle_bitwise(case, page, variant):
+    name, B, Lq, Lk, H, d, g, topk, c, dt = case
+    seed = zlib.crc32(name.encode()) % 1000
+    q, w, k = exact_random(seed, B, Lq, Lk, H, d, dt)
+    r = np.random.default_rng(seed)
+    lens = r.integers(Lq, Lk + 1, size=B).astype(np.int32)
+    lens[0] = Lk
+    ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
+    tq, tw = _dev(q), _dev(w)
+    kw = dict(variant={"dense": pv.DENSE, "reuse": pv.REUSE, "refine": pv.REFINE}[variant], g=g, topk=topk, c=c)
+    tl = torch.from_numpy(lens).cuda()
+    if page:
+        pool, table = _paged(k, page, seed)
+        i, s = pv.index_kv(tq, tw, _dev(pool), tl, torch.from_numpy(table).cuda(), page_size=page, lk=Lk,
+                           return_scores=True, **kw)
+    else:
+        i, s = pv.index_kv(tq, tw, _dev(k), tl, return_scores=True, **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(i.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(s.cpu().numpy(), ref_s)
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_contiguous_ragged_on_both_scan_paths(path, monkeypatch):
+    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if path == "fused" else str(1 << 40))
+    B, Lq, Lk, g, topk, c = 3, 500, 1200, 8, 32, 64
+    q, w, k = exact_random(41, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([1200, 777, 501], dtype=np.int32)
+    tq, tw, tk = _dev(q), _dev(w), _dev(k)
+    tl = torch.from_numpy(lens).cuda()
+    for variant, v in (("refine", pv.REFINE), ("reuse", pv.REUSE)):
+        i, s = pv.index_kv(tq, tw, tk, tl, return_scores=True, variant=v, g=g, topk=topk, c=c)
+        torch.cuda.synchronize()
+        ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
+        np.testing.assert_array_equal(i.cpu().numpy(), ref_i)
+        np.testing.assert_array_equal(s.cpu().numpy(), ref_s)
+
+
+def test_uniform_kv_call_equals_plain_call():
+    B, Lq, Lk, g, topk, c = 4, 4, 2000, 4, 32, 64
+    q, w, k = exact_random(43, B, Lq, Lk, 64, 128, BF16)
+    tq, tw, tk = to_device(q, w, k)
+    a = pv.index_refine(tq, tw, tk, g, topk, c)
+    b = pv.index_kv(tq, tw, tk, variant=pv.REFINE, g=g, topk=topk, c=c)
+    pool, table = _paged(k, 128, 5)
+    cc = pv.index_kv(tq, tw, _dev(pool), None, torch.from_numpy(table).cuda(), page_size=128, lk=Lk,
+                     variant=pv.REFINE, g=g, topk=topk, c=c)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, cc)
+
+
+def test_lengths_below_the_query_count_select_nothing_for_early_rows():
+    """Dense rows whose position falls below 0 (seq_lens[b] < Lq) are empty;
+    the others score the keys that exist."""
+    B, Lq, Lk, topk = 2, 8, 64, 4
+    q, w, k = exact_random(44, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([5, 64], dtype=np.int32)
+    i = pv.index_kv(_dev(q), _dev(w), _dev(k), torch.from_numpy(lens).cuda(), variant=pv.DENSE, topk=topk)
+    torch.cuda.synchronize()
+    got = i.cpu().numpy()
+    assert np.all(got[0, :3] == -1)                     # positions -3 .. -1
+    ref = oracle.dense(q[:1, 3:], w[:1, 3:], k[:1, :5], topk)["indices"]
+    np.testing.assert_array_equal(got[0, 3:], ref[0])
+    np.testing.assert_array_equal(got[1], oracle.dense(q[1:], w[1:], k[1:], topk)["indices"][0])
