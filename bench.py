@@ -46,15 +46,25 @@ def group_last_positions(Lq, Lk, g):
 
 
 def scan_flops(W, g):
-    tl = group_last_positions(W.Lq, W.Lk, g)
-    return 2.0 * W.d * W.H * W.B * float((tl + 1).sum())
+    from workloads import seq_lens
+    return sum(2.0 * W.d * W.H * float((group_last_positions(W.Lq, int(n), g) + 1).sum()) for n in seq_lens(W))
 
 
 def refine_flops(W, g, c):
-    tl = group_last_positions(W.Lq, W.Lk, g)
-    G = len(tl)
-    gm = np.minimum((np.arange(G) + 1) * g, W.Lq) - np.arange(G) * g
-    return 2.0 * W.d * W.H * W.B * float((gm * np.minimum(c, tl + 1)).sum())
+    from workloads import seq_lens
+    total = 0.0
+    for n in seq_lens(W):
+        tl = group_last_positions(W.Lq, int(n), g)
+        G = len(tl)
+        gm = np.minimum((np.arange(G) + 1) * g, W.Lq) - np.arange(G) * g
+        total += 2.0 * W.d * W.H * float((gm * np.minimum(c, tl + 1)).sum())
+    return total
+
+
+def scan_key_bytes(W):
+    """Keys each group's scan must read once: every key s <= t_last."""
+    from workloads import seq_lens
+    return float(sum(int(n) for n in seq_lens(W))) * W.d * (2 if W.dtype == "bf16" else 4)
 
 
 def kernel_source_hash():
@@ -107,6 +117,25 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
     about budget_s seconds; returns the metric-unit rate."""
     import oracle
     threads = oracle.num_threads()
+    if W.kind == "decode_ragged":
+        from workloads import seq_lens
+        lens = seq_lens(W)
+        fn = {"dense": lambda b: oracle.dense(q[b:b + 1], w[b:b + 1], k[b:b + 1, :lens[b]], W.topk, want_scores=False),
+              "reuse": lambda b: oracle.reuse(q[b:b + 1], w[b:b + 1], k[b:b + 1, :lens[b]], g, W.topk,
+                                              want_scores=False),
+              "refine": lambda b: oracle.refine(q[b:b + 1], w[b:b + 1], k[b:b + 1, :lens[b]], g, W.topk, W.c,
+                                                want_scores=False, want_cand=False)}[variant]
+        t0 = time.perf_counter()
+        done = 0
+        for b in range(W.B):
+            fn(b)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": done * W.Lq / dt, "unit": "query positions/s", "cores": threads, "kind": "oracle",
+                "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                "sample": f"{done} of {W.B} sequences (each on its own key prefix), {dt:.1f} s on {threads} threads"}
     per_seq = W.Lq if variant == "dense" else -(-W.Lq // g)
     rows_per_unit = 1 if variant == "dense" else g
     run = {"dense": lambda u: oracle.dense(q, w, k, W.topk, rows=u, want_scores=False),
@@ -209,17 +238,30 @@ def main():
     W = ALL[args.workload]
     g = 1 if args.variant == "dense" else (args.g or W.g)
     t0 = time.perf_counter()
-    from workloads import generate, to_device
+    from workloads import generate, to_device, seq_lens, paged_layout
     q, w, k = generate(W)
     log(f"[bench] generated {W.name} in {time.perf_counter() - t0:.1f} s")
     tq, tw, tk = to_device(q, w, k)
     dev = tq.device
     variant_id = {"dense": pv.DENSE, "reuse": pv.REUSE, "refine": pv.REFINE}[args.variant]
-    ws = torch.empty(pv.workspace_size(variant_id, W.B, W.Lq, W.Lk, W.H, W.d, tq.dtype, g, W.topk, W.c),
-                     dtype=torch.uint8, device=dev)
-    log(f"[bench] workspace {ws.numel() / 2**30:.2f} GiB")
+    ragged = W.kind == "decode_ragged"
+    if ragged:
+        # ragged lengths, keys in a shuffled pool of 64-key pages
+        lens = seq_lens(W)
+        pool, table = paged_layout(k, lens, 64, W.seed)
+        tpool = to_device(q[:1], w[:1], pool)[2]
+        ttable, tlens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+        kcfg = pv.make_config(variant=variant_id, g=g, topk=W.topk, c=W.c)
+        ws = None
+        log(f"[bench] ragged: lengths {int(lens.min())}..{int(lens.max())}, {pool.shape[0]} pages of 64 keys")
+    else:
+        ws = torch.empty(pv.workspace_size(variant_id, W.B, W.Lq, W.Lk, W.H, W.d, tq.dtype, g, W.topk, W.c),
+                         dtype=torch.uint8, device=dev)
+        log(f"[bench] workspace {ws.numel() / 2**30:.2f} GiB")
 
     def step():
+        if ragged:
+            return pv.index_kv(tq, tw, tpool, tlens, ttable, page_size=64, lk=W.Lk, cfg=kcfg)
         if args.variant == "refine":
             return pv.index_refine(tq, tw, tk, g, W.topk, W.c, workspace=ws)
         if args.variant == "reuse":
@@ -275,6 +317,18 @@ def main():
     kernels = {name: round(ms / max(n, 1), 4) for name, (ms, n) in stages.items() if n}
     log(f"[bench] {args.variant} g={g}: {ms_per_step:.3f} ms/step, kernels (ms/launch) {kernels}")
 
+    if W.kind.startswith("decode"):
+        # one group per sequence: the split-key scan reads every key once and
+        # meets it with only H rows, so HBM bounds it
+        kbytes = scan_key_bytes(W)
+        gbs = kbytes / scan_avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                    "traffic": None, "kernel": "split-key proxy scan (k_scan_split)", "bytes_per_launch": kbytes}
+    else:
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": recorded_traffic(W.name, args.variant, g),
+                    "kernel": "proxy scan + top-K selection (k_scan_mfma)", "flops_per_launch": sflops}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, w, k, W, args.variant, g, args.cpu_seconds)
@@ -296,11 +350,7 @@ def main():
         "config": {"workload": f"{W.name} PIVOT-{args.variant}", "batch": W.B, "seq_len": W.Lk,
                    "query_rows": W.Lq, "heads": W.H, "dim": W.d, "g": g, "topk": W.topk,
                    "c": W.c if args.variant == "refine" else None, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": recorded_traffic(W.name, args.variant, g),
-                     "kernel": "proxy scan + top-K selection (k_scan_mfma)",
-                     "flops_per_launch": sflops},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "median_call_ms": median_call_ms,
         "practical_peak": practical,

@@ -983,25 +983,39 @@ __global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
     load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
     load_w<H>(a.wsrc + gid * H, l, wr);
 
-    auto issue_tile = [&](int buf, int64_t base) {
+    // storage rows of this lane's 4 slices of a tile; looked up a tile ahead
+    // (a page-table read), so the lookup latency hides behind the MFMAs
+    auto tile_rows = [&](int64_t base, int64_t (&pr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int64_t s = base + slice_row(wv * 4 + j, l);
+            s = s < lkb ? s : (lkb > 0 ? lkb - 1 : 0);  // past the sequence: its last key (masked)
+            pr[j] = a.keys.row(b, s);
+        }
+    };
+    auto issue_tile = [&](int buf, const int64_t (&pr)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int slice = wv * 4 + j;
-            int64_t s = base + slice_row(slice, l);
-            s = s < lkb ? s : (lkb > 0 ? lkb - 1 : 0);  // past the sequence: its last key (masked)
-            const uint16_t *src = kbase + a.keys.row(b, s) * D + slice_col(slice, l);
+            const uint16_t *src = kbase + pr[j] * D + slice_col(slice, l);
             uint16_t *dst = buf ? tile1 : tile0;
             __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
 
-    issue_tile(0, static_cast<int64_t>(t0) * NT);
+    int64_t prow[4];
+    tile_rows(static_cast<int64_t>(t0) * NT, prow);
+    issue_tile(0, prow);
+    if (t0 + 1 < t1) tile_rows(static_cast<int64_t>(t0 + 1) * NT, prow);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     int cur = 0;
     for (int it = t0; it < t1; ++it) {
         const int64_t base = static_cast<int64_t>(it) * NT;
-        if (it + 1 < t1) issue_tile(cur ^ 1, base + NT);
+        if (it + 1 < t1) {
+            issue_tile(cur ^ 1, prow);
+            if (it + 2 < t1) tile_rows(base + 2 * NT, prow);
+        }
         f32x4 acc[RB];
         mfma_block<RB>(afr, cur ? tile1 : tile0, wv, l, acc);
         const float p = relu_weighted<RB>(acc, wr);
@@ -1838,14 +1852,14 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
     if (tile_lo >= tile_hi) return;  // uniform over the workgroup
     const int ntiles = tile_hi - tile_lo;
 
-    // positions of the key rows this lane gathers for a tile: slices
-    // wv + nwaves j (< kSlices), rows slice_row(slice, l)
+    // positions of the key rows this lane gathers for a tile (slices
+    // wv + nwaves j, tile rows slice_row(slice, l)), loaded a tile ahead and
+    // consumed raw by the DMA issue, so the loads never stall the MFMAs
     auto load_pos = [&](int tile_idx, int32_t (&pos)[kMaxSlices]) {
 #pragma unroll
         for (int j = 0; j < kMaxSlices; ++j) {
-            const int slice = wv + nwaves * j;
-            const int cj = tile_idx * NT + slice_row(slice, l);
-            pos[j] = cj < nc ? C[cj] : 0;  // row 0: any valid key row (masked)
+            const int cj = tile_idx * NT + slice_row(wv + nwaves * j, l);
+            pos[j] = cj < nc ? C[cj] : 0;  // row 0: any valid key (masked)
         }
     };
     auto issue_tile = [&](int buf, const int32_t (&pos)[kMaxSlices]) {

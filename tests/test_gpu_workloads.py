@@ -7,6 +7,9 @@ configuration the benchmark times.
   prefill_L131072       Refine and Reuse for g in {4, 8, 16} and dense (g = 1),
                         float rule on sampled groups/rows + every-row structure
   mtp_decode            Refine, float rule on every group (32 sequences)
+  mtp_decode_ragged     Refine over ragged lengths and 64-key pages (the
+                        benchmark's layout), float rule on every sequence
+                        against the oracle run on that sequence's own prefix
   tiny_prefill_L512     covered bit for bit in test_gpu_parity.py
 """
 import numpy as np
@@ -14,7 +17,7 @@ import pytest
 
 import oracle
 from tests import parity
-from workloads import DECODE, EXACT, LONG_128K, PREFILL_32K, generate, to_device
+from workloads import DECODE, DECODE_RAGGED, EXACT, LONG_128K, PREFILL_32K, generate, paged_layout, seq_lens, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -172,3 +175,24 @@ def test_mtp_decode_refine_every_group():
     parity.structure_all_rows(f_i, W.Lq, W.Lk, W.topk)
     d = parity.check_refine_groups(q, w, k, W.g, W.topk, W.c, f_i, f_s, f_c, f_n, np.arange(W.B))
     _say(f"[decode] {W.B} groups checked, {d} boundary swaps")
+
+
+def test_mtp_decode_ragged_paged_refine_every_sequence():
+    W = DECODE_RAGGED
+    q, w, k = generate(W)
+    lens = seq_lens(W)
+    pool, table = paged_layout(k, lens, 64, W.seed)
+    tq, tw, tpool = to_device(q, w, pool)
+    f_i, f_s, f_c, f_n = pv.index_kv(tq, tw, tpool, torch.from_numpy(lens).cuda(), torch.from_numpy(table).cuda(),
+                                     page_size=64, lk=W.Lk, variant=pv.REFINE, g=W.g, topk=W.topk, c=W.c,
+                                     return_scores=True, return_candidates=True)
+    torch.cuda.synchronize()
+    f_i, f_s, f_c, f_n = _np(f_i), _np(f_s), _np(f_c), _np(f_n)
+    assert np.all(f_n == W.c)
+    d = 0
+    for b in range(W.B):
+        n = int(lens[b])
+        parity.structure_all_rows(f_i[b:b + 1], W.Lq, n, W.topk)
+        d += parity.check_refine_groups(q[b:b + 1], w[b:b + 1], k[b:b + 1, :n], W.g, W.topk, W.c, f_i[b:b + 1],
+                                        f_s[b:b + 1], f_c[b:b + 1], f_n[b:b + 1], np.arange(1))
+    _say(f"[decode ragged] {W.B} sequences checked, {d} boundary swaps")

@@ -15,7 +15,8 @@ Query row r of a sequence sits at position ``Lk - Lq + r`` (prefill has
 Lq == Lk; decode holds only the last g rows).
 
 Random streams: ``numpy.random.default_rng([seed, tensor_id, *extra])`` with
-tensor ids q=0, k=1, w=2, spike=3, drift=4, residual=5. Values are drawn in
+tensor ids q=0, k=1, w=2, spike=3, drift=4, residual=5, lengths=6, pages=7.
+Values are drawn in
 float64 and rounded to float32 (and then to bf16) with round-to-nearest-even.
 """
 from __future__ import annotations
@@ -26,7 +27,7 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-TID_Q, TID_K, TID_W, TID_SPIKE, TID_DRIFT, TID_RESID = 0, 1, 2, 3, 4, 5
+TID_Q, TID_K, TID_W, TID_SPIKE, TID_DRIFT, TID_RESID, TID_LENS, TID_PAGES = 0, 1, 2, 3, 4, 5, 6, 7
 
 _CHUNK = 4096  # positions generated per step (bounds the float64 working set)
 
@@ -65,7 +66,7 @@ def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
 class Workload:
     """One synthetic problem. ``kind`` selects the value recipe."""
     name: str
-    kind: str            # "gauss" | "exact" | "ar1" | "decode"
+    kind: str            # "gauss" | "exact" | "ar1" | "decode" | "decode_ragged"
     B: int
     Lq: int
     Lk: int
@@ -91,8 +92,12 @@ EXACT = Workload("exact_prefill_L8192", "exact", 1, 8192, 8192, 64, 128, BF16, 8
 PREFILL_32K = Workload("prefill_L32768", "ar1", 1, 32768, 32768, 64, 128, BF16, 8, 2048, 4096)
 LONG_128K = Workload("prefill_L131072", "ar1", 1, 131072, 131072, 64, 128, BF16, 8, 2048, 4096)
 DECODE = Workload("mtp_decode_B32_P65536", "decode", 32, 4, 65536, 64, 128, BF16, 4, 2048, 4096)
+# Ragged batched decode: the same recipe, each sequence with its own prefix
+# length (seq_lens), keys held in a page pool (paged_layout).
+DECODE_RAGGED = Workload("mtp_decode_ragged_B32_P65536", "decode_ragged", 32, 4, 65536, 64, 128, BF16, 4, 2048,
+                         4096)
 
-ALL = {w.name: w for w in (TINY, EXACT, PREFILL_32K, LONG_128K, DECODE)}
+ALL = {w.name: w for w in (TINY, EXACT, PREFILL_32K, LONG_128K, DECODE, DECODE_RAGGED)}
 LONG_G_SWEEP = (1, 4, 8, 16)
 
 AR_RHO = 0.95
@@ -186,6 +191,38 @@ def _ar1_prefill(w: Workload):
     return q, f64_to_f32(ww), k[None]
 
 
+def seq_lens(w: Workload) -> np.ndarray:
+    """Per-sequence key counts: Lk for every sequence, except the ragged
+    decode workload, whose lengths are uniform on [Lk / 4, Lk] (seeded)."""
+    if w.kind != "decode_ragged":
+        return np.full(w.B, w.Lk, dtype=np.int32)
+    r = _rng(w.seed, TID_LENS)
+    return r.integers(w.Lk // 4, w.Lk + 1, size=w.B).astype(np.int32)
+
+
+def paged_layout(k: np.ndarray, lens: np.ndarray, page: int, seed: int = 0):
+    """The keys of each sequence copied into a shuffled page pool: returns
+    (pool [num_pages, page, d], table [B, ceil(Lk / page)] int32). Pages
+    past a sequence's length get no pool page (table entry -1). Only moves
+    data."""
+    B, Lk, d = k.shape
+    maxp = -(-Lk // page)
+    used = [int(-(-int(n) // page)) for n in lens]
+    n_pages = max(1, sum(used))
+    perm = _rng(seed, TID_PAGES).permutation(n_pages).astype(np.int32)
+    pool = np.zeros((n_pages, page, d), dtype=k.dtype)
+    table = np.full((B, maxp), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        for j in range(used[b]):
+            ph = perm[at]
+            at += 1
+            rows = k[b, j * page:min((j + 1) * page, int(lens[b]))]
+            pool[ph, :rows.shape[0]] = rows
+            table[b, j] = ph
+    return pool, table
+
+
 def _decode(w: Workload):
     """B independent sequences, Lk-token key prefix each, and a group of Lq
     AR(1) queries at positions Lk-Lq .. Lk-1.
@@ -196,12 +233,14 @@ def _decode(w: Workload):
     start stationary at position Lk-Lq). This has the same joint law as H
     independent per-head AR(1) rows summed into z, without drawing all Lk rows.
     """
-    B, G, P, H, d = w.B, w.Lq, w.Lk, w.H, w.d
+    B, G, Lk, H, d = w.B, w.Lq, w.Lk, w.H, w.d
     out_dtype = np.uint16 if w.dtype == BF16 else np.float32
     q = np.empty((B, G, H, d), dtype=out_dtype)
-    k = np.empty((B, P, d), dtype=out_dtype)
+    k = np.zeros((B, Lk, d), dtype=out_dtype)
     ww = np.empty((B, G, H), dtype=np.float32)
+    lens = seq_lens(w)
     for b in range(B):
+        P = int(lens[b])  # this sequence's prefix; rows past it stay zero
         z = np.empty((P, d), dtype=np.float64)
         for s0, blk in _ar1_chunks(_rng(w.seed, TID_DRIFT, b), P, d, AR_RHO, np.sqrt(H)):
             z[s0:s0 + blk.shape[0]] = blk
@@ -212,11 +251,11 @@ def _decode(w: Workload):
         qb = z[P - G:, None, :] / H + resid
         q[b] = to_storage(qb, w.dtype)
         ww[b] = f64_to_f32(np.abs(_rng(w.seed, TID_W, b).standard_normal((G, H))) / 8.0)
-        k[b] = _spiked_keys(w, (b,), lambda a, c: z[a:c].copy())
+        k[b, :P] = _spiked_keys(w.replace(Lk=P), (b,), lambda a, c: z[a:c].copy())
     return q, ww, k
 
 
-_RECIPES = {"gauss": _gauss, "exact": _exact, "ar1": _ar1_prefill, "decode": _decode}
+_RECIPES = {"gauss": _gauss, "exact": _exact, "ar1": _ar1_prefill, "decode": _decode, "decode_ragged": _decode}
 
 
 def generate(w: Workload):
