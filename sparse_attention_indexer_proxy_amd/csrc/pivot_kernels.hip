@@ -1392,6 +1392,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *p, int 
 constexpr int kMsWaves = 4;     // rows (one per wave) per workgroup
 constexpr int kMsMid = 1024;    // LDS keys per wave for the final bits
 constexpr int kMsChunk = 16;    // slabs of positions loaded at a time
+constexpr int kHistBins = 256;  // value-range bins of the one-pass histogram
 
 // Number of keys in kv[] that are >= x (a wave-uniform count).
 template <int N>
@@ -1408,6 +1409,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     for (int o = 32; o > 0; o >>= 1) {
         const uint32_t x = __shfl_xor(v, o);
         v = x > v ? x : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = __shfl_xor(v, o);
+        v = x < v ? x : v;
     }
     return v;
 }
@@ -1445,11 +1455,100 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
     int quota = 0;
     bool ties_all = true;
     if (n > K) {
+        uint32_t T = 0;
+        bool found = false;
+        {
+            // One pass into kHistBins bins of equal width 2^shift over the
+            // keys' range [lo, hi] (LDS atomics) finds the bin holding the
+            // K-th largest key and the count above it; that bin's keys are
+            // compacted into `mid` and the key is resolved by bisection over
+            // the bin's values. A bin too crowded (many equal keys) falls
+            // back to the bisection over all keys below.
+            uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                lo = kv[i] != 0u && kv[i] < lo ? kv[i] : lo;
+                hi = kv[i] > hi ? kv[i] : hi;
+            }
+            lo = wave_min_u32(lo);
+            hi = wave_max_u32(hi);
+            int shift = 0;
+            while (((hi - lo) >> shift) >= static_cast<uint32_t>(kHistBins)) ++shift;
+            uint32_t *hist = mid + kMsMid;
+            for (int j = l; j < kHistBins; j += kWave) hist[j] = 0u;
+            wave_fence();
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (kv[i] != 0u) atomicAdd(&hist[(kv[i] - lo) >> shift], 1u);
+            wave_fence();
+            // lane l holds bins 4l .. 4l+3; suffix counts run from the top bin
+            const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+            const uint32_t tot = c0 + c1 + c2 + c3;
+            uint32_t suf = tot;
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t t = __shfl_down(suf, o);
+                if (l + o < kWave) suf += t;
+            }
+            const uint32_t above_lane = suf - tot;
+            const bool here = above_lane < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= suf;
+            const int src = __ffsll(static_cast<long long>(ballot(here))) - 1;
+            int bb = 0;
+            uint32_t abv = 0, cnt = 0;
+            if (here) {
+                uint32_t cum = above_lane;
+                if (cum + c3 >= static_cast<uint32_t>(K)) {
+                    bb = 4 * l + 3; cnt = c3;
+                } else if ((cum += c3) + c2 >= static_cast<uint32_t>(K)) {
+                    bb = 4 * l + 2; cnt = c2;
+                } else if ((cum += c2) + c1 >= static_cast<uint32_t>(K)) {
+                    bb = 4 * l + 1; cnt = c1;
+                } else {
+                    cum += c1;
+                    bb = 4 * l; cnt = c0;
+                }
+                abv = cum;
+            }
+            bb = __shfl(bb, src);
+            abv = __shfl(abv, src);
+            cnt = __shfl(cnt, src);
+            wave_fence();
+            if (cnt <= static_cast<uint32_t>(kMsMid)) {
+                const uint32_t blo = lo + (static_cast<uint32_t>(bb) << shift);
+                const uint32_t bw = (1u << shift) - 1u;
+                const uint32_t bhi = hi - blo < bw ? hi : blo + bw;
+                int nm = 0;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const bool in = kv[i] >= blo && kv[i] <= bhi;
+                    const uint64_t im = ballot(in);
+                    if (in) mid[nm + mbcnt(im)] = kv[i];
+                    nm += popc(im);
+                }
+                wave_fence();
+                uint32_t mv[kMsMid / kWave];
+#pragma unroll
+                for (int q = 0; q < kMsMid / kWave; ++q) {
+                    const int j = kWave * q + l;
+                    mv[q] = j < nm ? mid[j] : 0u;
+                }
+                // the largest x in [blo, bhi] with abv + #{bin key >= x} >= K
+                uint32_t a_lo = blo, a_hi = bhi;
+                while (a_lo < a_hi) {
+                    const uint32_t x = a_lo + (a_hi - a_lo) / 2u + 1u;
+                    if (static_cast<int>(abv) + count_ge(mv, x) >= K)
+                        a_lo = x;
+                    else
+                        a_hi = x - 1u;
+                }
+                T = a_lo;
+                found = true;
+            }
+            wave_fence();
+        }
         // invariant: kth in [T, T + 2^bit); n_lo = #{key >= T} >= K,
         // n_hi = #{key >= T + 2^bit} < K
-        uint32_t T = 0;
         int n_lo = n, n_hi = 0;
-        int bit = 32;
+        int bit = found ? 0 : 32;
         while (bit > 0 && n_lo - n_hi > kMsMid) {
             --bit;
             const uint32_t x = T | (1u << bit);
@@ -1550,7 +1649,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
 template <int NV>
 __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelectArgs a)
 {
-    __shared__ uint32_t mid_all[kMsWaves][kMsMid];
+    __shared__ uint32_t mid_all[kMsWaves][kMsMid + kHistBins];
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row addressing
     const int l = threadIdx.x & 63;
@@ -1612,7 +1711,7 @@ struct GroupSelectArgs {
 template <int NV>
 __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectArgs a)
 {
-    __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid : 256];
+    __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid + kHistBins : 256];
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
