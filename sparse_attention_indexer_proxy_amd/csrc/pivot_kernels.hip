@@ -18,15 +18,21 @@
 //                           score row (Mode = kRows)
 //   k_scan_exact<T, Mode>   the same for any shape/dtype, in the exact fp32
 //                           order of the definition (heads, then dims ascending)
-//   k_refine_mfma           eqs. (8)-(9) over a gathered candidate tile
-//   k_refine_exact<T>       the same in exact order
+//   k_select_groups<NV>     the final top-K of each group's survivors (eqs. 6-7)
+//   k_scan_split            eq. (5) with the key axis split over workgroups
+//                           (few groups: decode), score rows to HBM
+//   k_select_rows           block-wide selects of those rows (eqs. 6-7, 9)
+//   k_refine_mfma           eq. (8) over gathered candidate tiles
+//   k_select_members<NV>    eq. (9): each member's top-k of its re-scored C
+//   k_refine_exact<T>       eqs. (8)-(9) in exact order
 //
 // Selection: a wave keeps its group's survivors (score > tau) in a private
 // buffer in HBM, appended in ascending position. When the buffer is full the
 // wave radix-selects the K-th best (score desc, position asc), compacts the
 // buffer in place (stable) to exactly K entries and raises tau. At the end
-// the same select + stable compaction writes the rows in ascending position.
-// The full L/g x L score matrix never exists in memory.
+// k_select_groups (or, in the exact-order scan, the same wave select) picks
+// the best K and writes them in ascending position. The full L/g x L score
+// matrix never exists in memory.
 
 #include <hip/hip_runtime.h>
 
@@ -466,8 +472,8 @@ __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const flo
 }
 
 // -------------------------------------------------------- MFMA scan (bf16)
-// One workgroup = 4 waves = 4 consecutive groups of one sequence. The WG
-// streams 64-key tiles of k into LDS (double-buffered; global_load_lds puts
+// One workgroup = kScanWaves waves = as many consecutive groups of one
+// sequence. The WG streams tiles of k into LDS (double-buffered; LDS DMA puts
 // each 16-byte chunk straight into LDS at an XOR-swizzled slot, so the MFMA
 // operand reads are bank-conflict free) and every wave multiplies its proxy
 // (H x D, held in registers as MFMA A fragments) by the tile:
@@ -558,26 +564,6 @@ __device__ __forceinline__ float quarter_transpose_sum(const float (&p)[4])
     return (__uint_as_float(r[0]) + __uint_as_float(r[1])) + 0.0f;  // + 0: one zero, +0
 }
 
-// Score of key l of the tile for the wave's A (RB row blocks of 16 heads).
-// Two accumulator sets let the MFMAs of block cb+1 overlap the weighted
-// ReLU reduction of block cb.
-template <int RB>
-__device__ __forceinline__ float tile_scores(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4],
-                                             const uint16_t *tile, int l)
-{
-    f32x4 acc0[RB], acc1[RB];
-    float p[4];
-    mfma_block<RB>(afr, tile, 0, l, acc0);
-    mfma_block<RB>(afr, tile, 1, l, acc1);
-    p[0] = relu_weighted<RB>(acc0, wr);
-    mfma_block<RB>(afr, tile, 2, l, acc0);
-    p[1] = relu_weighted<RB>(acc1, wr);
-    mfma_block<RB>(afr, tile, 3, l, acc1);
-    p[2] = relu_weighted<RB>(acc0, wr);
-    p[3] = relu_weighted<RB>(acc1, wr);
-    return quarter_transpose_sum(p);
-}
-
 // B fragments of one 16-key block (all four 32-dim slices).
 __device__ __forceinline__ void load_b(const uint16_t *tile, int cb, int l, bf16x8 (&bfr)[4])
 {
@@ -585,22 +571,6 @@ __device__ __forceinline__ void load_b(const uint16_t *tile, int cb, int l, bf16
     for (int kb = 0; kb < 4; ++kb) bfr[kb] = b_frag(tile, cb, kb, l);
 }
 
-template <int RB>
-__device__ __forceinline__ void mfma_regs(const bf16x8 (&afr)[RB][4], const bf16x8 (&bfr)[4], f32x4 (&acc)[RB])
-{
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bfr[kb], acc[rb], 0, 0, 0);
-    }
-}
-
-// Scores of keys l and 64 + l of a 128-key tile. Software-pipelined over
-// the eight 16-key blocks: block cb+2's B fragments are read from LDS while
-// block cb's MFMAs run, and block cb-1's ReLU-weighted reduction overlaps
-// them; the first half's transpose overlaps the second half's MFMAs.
 // Fence for the instruction scheduler: nothing moves across it, so the
 // source order below is the issue order.
 #define PIVOT_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
