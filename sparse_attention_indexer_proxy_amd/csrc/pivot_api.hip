@@ -253,7 +253,7 @@ struct KeysIn {
     pivot::KeyPages pages;
 };
 
-KeysIn contiguous(const void *k) { return KeysIn{k, nullptr, pivot::KeyPages{nullptr, 0, 0, 0}}; }
+KeysIn contiguous(const void *k) { return KeysIn{k, nullptr, pivot::KeyPages{nullptr, 0, 0, 0, 0, 0}}; }
 
 pivot_status check_keys(const pivot_problem *p, const pivot_keys *keys, KeysIn *out)
 {
@@ -269,7 +269,7 @@ pivot_status check_keys(const pivot_problem *p, const pivot_keys *keys, KeysIn *
                         (long long)need);
         if (keys->num_pages * int64_t(keys->page_size) >= (int64_t(1) << 40))
             return fail(PIVOT_ERR_UNSUPPORTED, "key pool too large");
-        kin.pages = pivot::KeyPages{keys->page_table, keys->num_pages, keys->page_size, keys->max_pages};
+        kin.pages = pivot::make_key_pages(keys->page_table, keys->num_pages, keys->page_size, keys->max_pages);
     }
     *out = kin;
     return PIVOT_OK;

@@ -13,7 +13,21 @@ struct KeyPages {
     const int32_t *table;  // null: contiguous
     int64_t num_pages;
     int page, max_pages;
+    // s / page == (s * page_magic) >> page_shift for every s < 2^31:
+    // page_shift = 31 + ceil(log2 page), page_magic = 2^page_shift / page + 1
+    // (then page_magic * page - 2^page_shift lies in (0, page] and at most
+    // 2^(page_shift - 31), which keeps the rounding error below 1 / page)
+    uint32_t page_magic;
+    int page_shift;
 };
+
+inline KeyPages make_key_pages(const int32_t *table, int64_t num_pages, int page, int max_pages)
+{
+    int l = 0;
+    while ((int64_t(1) << l) < page) ++l;
+    const uint64_t magic = (uint64_t(1) << (31 + l)) / static_cast<uint64_t>(page) + 1;
+    return KeyPages{table, num_pages, page, max_pages, static_cast<uint32_t>(magic), 31 + l};
+}
 
 struct LaunchShape {
     int64_t B, Lq, Lk;              // Lk: key capacity per sequence

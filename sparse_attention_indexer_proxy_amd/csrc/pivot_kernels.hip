@@ -38,6 +38,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pivot_kernels.h"
 
@@ -61,6 +62,55 @@ __device__ __forceinline__ int mbcnt(uint64_t m)
 }
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+// Value of v in lane `src` (wave-uniform), without a trip through LDS.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int src)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), src));
+}
+
+// DPP lane moves within the wave (gfx9 encodings): row_shr:n shifts each
+// 16-lane row right by n, row_bcast:15 / row_bcast:31 pass lane 15 of a row
+// (31 of the half) on to the next row(s); lanes without a source (or outside
+// row_mask) take `fill`.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v, uint32_t fill)
+{
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(fill), static_cast<int>(v), Ctrl, RowMask, 0xF, false));
+}
+
+// Inclusive prefix sum over the lanes of a wave (Hillis-Steele on DPP).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v)
+{
+    v += dpp_move<0x111>(v, 0u);
+    v += dpp_move<0x112>(v, 0u);
+    v += dpp_move<0x114>(v, 0u);
+    v += dpp_move<0x118>(v, 0u);
+    v += dpp_move<0x142, 0xA>(v, 0u);
+    v += dpp_move<0x143, 0xC>(v, 0u);
+    return v;
+}
+
+// Inclusive suffix sum over lanes: lane l gets the sum over lanes >= l.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v)
+{
+    const uint32_t inc = wave_incl_sum(v);
+    return lane_value(inc, kWave - 1) - inc + v;
+}
+
+// Sum over the wave (wave-uniform).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return lane_value(wave_incl_sum(v), kWave - 1); }
+
+// Sum over lanes 0..15 (wave-uniform).
+__device__ __forceinline__ uint32_t row0_sum(uint32_t v)
+{
+    v += dpp_move<0x111>(v, 0u);
+    v += dpp_move<0x112>(v, 0u);
+    v += dpp_move<0x114>(v, 0u);
+    v += dpp_move<0x118>(v, 0u);
+    return lane_value(v, 15);
+}
 
 // Sum over the wave of a per-lane count in [0, 127].
 __device__ __forceinline__ int wave_total(uint32_t c)
@@ -129,12 +179,34 @@ struct Keys {
     const void *base;
     KeyPages pg;
     int64_t Lk;
+    __device__ __forceinline__ int64_t flat(int64_t b, int64_t s) const { return b * Lk + s; }
+    // A paged lookup in two halves, so that a kernel can read the table
+    // entries a tile ahead of the rows they yield. Positions are below 2^31,
+    // so s / page is one 32x32->64-bit multiply and a shift (the host's
+    // round-up reciprocal), with no branch between the table loads.
+    __device__ __forceinline__ uint32_t page_index(uint32_t s) const
+    {
+        return static_cast<uint32_t>((static_cast<uint64_t>(s) * pg.page_magic) >> pg.page_shift);
+    }
+    __device__ __forceinline__ int32_t entry(int64_t b, uint32_t s) const
+    {
+        return pg.table[b * pg.max_pages + page_index(s)];
+    }
+    __device__ __forceinline__ uint32_t page_offset(uint32_t s) const
+    {
+        return s - page_index(s) * static_cast<uint32_t>(pg.page);
+    }
+    // row `off` of page table entry `e`
+    __device__ __forceinline__ int64_t paged_row(int32_t e, uint32_t off) const
+    {
+        const int64_t ph = e < 0 ? 0 : (e >= pg.num_pages ? pg.num_pages - 1 : e);
+        return ph * pg.page + off;
+    }
     __device__ __forceinline__ int64_t row(int64_t b, int64_t s) const
     {
-        if (!pg.table) return b * Lk + s;
-        int64_t ph = pg.table[b * pg.max_pages + s / pg.page];
-        ph = ph < 0 ? 0 : (ph >= pg.num_pages ? pg.num_pages - 1 : ph);
-        return ph * pg.page + s % pg.page;
+        if (!pg.table) return flat(b, s);
+        const uint32_t su = static_cast<uint32_t>(s);
+        return paged_row(entry(b, su), page_offset(su));
     }
 };
 
@@ -171,13 +243,31 @@ __device__ __forceinline__ void hist_add(bool in, uint32_t key, uint32_t prefix,
     const uint64_t mm = ballot(match);
     if (mm == 0) return;
     const int first = __ffsll(static_cast<long long>(mm)) - 1;
-    const uint32_t d0 = __shfl(digit, first);
+    const uint32_t d0 = lane_value(digit, first);
     const uint64_t same = ballot(match && digit == d0);
     if (same == mm) {
         if (l == first) atomicAdd(&hist[d0], static_cast<uint32_t>(popc(mm)));
     } else if (match) {
         atomicAdd(&hist[digit], 1u);
     }
+}
+
+// hist_add for wave-private histograms: the lanes sharing the first matching
+// lane's digit (most of them in the leading digits) add with one atomic, the
+// others one each, so no address takes many atomics at once.
+__device__ __forceinline__ void hist_add_peel(bool in, uint32_t key, uint32_t prefix, uint32_t pmask, int shift,
+                                              uint32_t *hist, int l)
+{
+    const bool match = in && (key & pmask) == prefix;
+    const uint32_t digit = (key >> shift) & 0xFFu;
+    const uint64_t mm = ballot(match);
+    if (mm == 0) return;
+    const int first = __ffsll(static_cast<long long>(mm)) - 1;
+    const uint32_t d0 = lane_value(digit, first);
+    const bool other = match && digit != d0;
+    const uint64_t same = mm & ~ballot(other);
+    if (l == first) atomicAdd(&hist[d0], static_cast<uint32_t>(popc(same)));
+    if (other) atomicAdd(&hist[digit], 1u);
 }
 
 // Radix select over 8-bit digits of ord_key(score), most significant first,
@@ -214,7 +304,10 @@ __device__ Sel wave_select(const float *sc, int n, int K, uint32_t *hist)
         wave_fence();
         const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
         const uint32_t tot = c0 + c1 + c2 + c3;
-        uint32_t suf = tot;  // inclusive suffix sum over lanes (higher lanes hold higher bins)
+        // inclusive suffix sum over lanes (higher lanes hold higher bins);
+        // shuffles rather than DPP here: inlined into the fused scan, the
+        // DPP form shifts that kernel's register allocation and costs ~2%
+        uint32_t suf = tot;
         for (int o = 1; o < kWave; o <<= 1) {
             const uint32_t t = __shfl_down(suf, o);
             if (l + o < kWave) suf += t;
@@ -923,7 +1016,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 // the proxy scores are written to a row buffer [B*G, Lk] for k_select_rows.
 // The four waves of a workgroup share each 64-key tile and take one 16-key
 // block each; the scan is HBM-bound here (each key meets only H rows).
-template <int H, int D>
+template <int H, int D, bool PAGED>
 __global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
@@ -953,38 +1046,45 @@ __global__ __launch_bounds__(256) void k_scan_split(ScanArgs a, int splits)
     load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
     load_w<H>(a.wsrc + gid * H, l, wr);
 
-    // storage rows of this lane's 4 slices of a tile; looked up a tile ahead
-    // (a page-table read), so the lookup latency hides behind the MFMAs
-    auto tile_rows = [&](int64_t base, int64_t (&pr)[4]) {
+    // position of this lane's key in slice j of a tile (past the sequence:
+    // its last key, masked)
+    auto key_pos = [&](int64_t base, int j) {
+        const int64_t s = base + slice_row(wv * 4 + j, l);
+        return static_cast<uint32_t>(s < lkb ? s : (lkb > 0 ? lkb - 1 : 0));
+    };
+    // paged keys: the table entries of a tile are read a tile ahead, and
+    // only the DMA issue turns them into rows, so the table latency hides
+    // behind the MFMAs instead of holding up the key loads
+    auto load_entries = [&](int64_t base, int32_t (&e)[4]) {
+        if constexpr (PAGED) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t s = base + slice_row(wv * 4 + j, l);
-            s = s < lkb ? s : (lkb > 0 ? lkb - 1 : 0);  // past the sequence: its last key (masked)
-            pr[j] = a.keys.row(b, s);
+            for (int j = 0; j < 4; ++j) e[j] = a.keys.entry(b, key_pos(base, j));
         }
     };
-    auto issue_tile = [&](int buf, const int64_t (&pr)[4]) {
+    auto issue_tile = [&](int buf, int64_t base, const int32_t (&e)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int slice = wv * 4 + j;
-            const uint16_t *src = kbase + pr[j] * D + slice_col(slice, l);
+            const uint32_t s = key_pos(base, j);
+            const int64_t r = PAGED ? a.keys.paged_row(e[j], a.keys.page_offset(s)) : a.keys.flat(b, s);
+            const uint16_t *src = kbase + r * D + slice_col(slice, l);
             uint16_t *dst = buf ? tile1 : tile0;
             __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
 
-    int64_t prow[4];
-    tile_rows(static_cast<int64_t>(t0) * NT, prow);
-    issue_tile(0, prow);
-    if (t0 + 1 < t1) tile_rows(static_cast<int64_t>(t0 + 1) * NT, prow);
+    int32_t ent[4] = {0, 0, 0, 0};
+    load_entries(static_cast<int64_t>(t0) * NT, ent);
+    issue_tile(0, static_cast<int64_t>(t0) * NT, ent);
+    if (t0 + 1 < t1) load_entries(static_cast<int64_t>(t0 + 1) * NT, ent);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     int cur = 0;
     for (int it = t0; it < t1; ++it) {
         const int64_t base = static_cast<int64_t>(it) * NT;
         if (it + 1 < t1) {
-            issue_tile(cur ^ 1, prow);
-            if (it + 2 < t1) tile_rows(base + 2 * NT, prow);
+            issue_tile(cur ^ 1, base + NT, ent);
+            if (it + 2 < t1) load_entries(base + 2 * NT, ent);
         }
         f32x4 acc[RB];
         mfma_block<RB>(afr, cur ? tile1 : tile0, wv, l, acc);
@@ -1026,9 +1126,15 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 
 struct BlockShared {
-    uint32_t hist[kSelWaves][256];  // one histogram per wave (no inter-wave atomic contention)
+    alignas(16) uint32_t hist[kSelWaves][256];  // one histogram per wave (no inter-wave atomic contention)
     int wave_sum[2][kSelWaves];
     uint32_t bcast[4];
+    uint32_t key_and[kSelWaves], key_or[kSelWaves];  // block_select_regs
+    // block_filter_above: per-chunk survivor counts and their offsets, in
+    // (slot e, wave) order, double-buffered over chunks
+    alignas(16) int fcnt[2][kSelWaves * kSelWaves];
+    alignas(16) int foff[2][kSelWaves * kSelWaves];
+    int ftot[2];
 };
 
 // Exclusive prefix over the block's threads of per-thread counts c0, c1 in
@@ -1044,16 +1150,13 @@ __device__ __forceinline__ void block_prefix2(int c0, int c1, int *p0, int *p1, 
         sh.wave_sum[1][wv] = w1;
     }
     __syncthreads();
-    int b0 = 0, b1 = 0, s0 = 0, s1 = 0;
-    for (int i = 0; i < kSelWaves; ++i) {
-        const int x0 = sh.wave_sum[0][i], x1 = sh.wave_sum[1][i];
-        if (i < wv) {
-            b0 += x0;
-            b1 += x1;
-        }
-        s0 += x0;
-        s1 += x1;
-    }
+    // lane i < kSelWaves reads wave i's sums; sums over lanes 0..15 give
+    // the waves below this one and all waves
+    static_assert(kSelWaves == 16, "one DPP row of wave sums");
+    const int i = l & (kSelWaves - 1);
+    const uint32_t x0 = sh.wave_sum[0][i], x1 = sh.wave_sum[1][i];
+    const int b0 = static_cast<int>(row0_sum(i < wv ? x0 : 0u)), b1 = static_cast<int>(row0_sum(i < wv ? x1 : 0u));
+    const int s0 = static_cast<int>(row0_sum(x0)), s1 = static_cast<int>(row0_sum(x1));
     __syncthreads();
     *p0 = b0 + e0;
     *p1 = b1 + e1;
@@ -1107,11 +1210,7 @@ __device__ Sel block_select(const float *sc, int n, int K, BlockShared &sh)
             const uint32_t c0 = sh.hist[0][4 * l], c1 = sh.hist[0][4 * l + 1], c2 = sh.hist[0][4 * l + 2],
                            c3 = sh.hist[0][4 * l + 3];
             const uint32_t tot = c0 + c1 + c2 + c3;
-            uint32_t suf = tot;
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t t = __shfl_down(suf, o);
-                if (l + o < kWave) suf += t;
-            }
+            const uint32_t suf = wave_suffix_sum(tot);
             const uint32_t above = suf - tot;
             if (above < remaining && remaining <= suf) {
                 uint32_t cum = above, dig;
@@ -1147,10 +1246,261 @@ __device__ Sel block_select(const float *sc, int n, int K, BlockShared &sh)
     return r;
 }
 
-template <class F> __device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, BlockShared &sh, F &&emit)
+// Loads and stores through a typed address space (1: global, 3: LDS), so
+// the compiler emits global_load / ds_read rather than flat accesses, whose
+// completion shares the LDS wait counter (each LDS wait would also wait for
+// every global load in flight).
+constexpr int kGlobal = 1, kLds = 3;
+
+template <int AS, class T>
+__device__ __forceinline__ T load_as(const T *p, int64_t j)
+{
+    return ((const __attribute__((address_space(AS))) T *)p)[j];
+}
+
+template <int AS, class T>
+__device__ __forceinline__ void store_as(T *p, int64_t j, T v)
+{
+    ((__attribute__((address_space(AS))) T *)p)[j] = v;
+}
+
+// Block radix select over keys held in registers: thread tid holds the keys
+// of entries j = e * kSelThreads + tid (e < kSelRegs), valid for j < n. The
+// leading bits that every valid key shares (block AND / OR) are skipped, so
+// the first digit already splits the keys; per 8-bit digit each wave counts
+// its keys into its own 256-bin histogram (clearing it itself, so no atomics
+// meet across waves) and wave 0 sums the 16 histograms and finds the digit:
+// two barriers per digit. Digits are taken from the highest differing bit
+// down; the last one may overlap the prefix (those bits agree already).
+constexpr int kSelRegs = 16;  // keys per thread: rows of up to 16384 entries
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t v)
+{
+    v &= dpp_move<0x111>(v, ~0u);
+    v &= dpp_move<0x112>(v, ~0u);
+    v &= dpp_move<0x114>(v, ~0u);
+    v &= dpp_move<0x118>(v, ~0u);
+    v &= dpp_move<0x142, 0xA>(v, ~0u);
+    v &= dpp_move<0x143, 0xC>(v, ~0u);
+    return lane_value(v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+    v |= dpp_move<0x111>(v, 0u);
+    v |= dpp_move<0x112>(v, 0u);
+    v |= dpp_move<0x114>(v, 0u);
+    v |= dpp_move<0x118>(v, 0u);
+    v |= dpp_move<0x142, 0xA>(v, 0u);
+    v |= dpp_move<0x143, 0xC>(v, 0u);
+    return lane_value(v, kWave - 1);
+}
+
+__device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, BlockShared &sh)
+{
+    Sel r;
+    if (n <= K) {
+        r.all = true;
+        r.kth = 0;
+        r.quota = 0;
+        return r;
+    }
+    r.all = false;
+    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+    // bits shared by every valid key
+    uint32_t kand = ~0u, kor = 0u;
+#pragma unroll
+    for (int e = 0; e < kSelRegs; ++e) {
+        if (e * kSelThreads < n) {
+            const bool in = e * kSelThreads + tid < n;
+            kand &= in ? key[e] : ~0u;
+            kor |= in ? key[e] : 0u;
+        }
+    }
+    kand = wave_and(kand);
+    kor = wave_or(kor);
+    if (l == 0) {
+        sh.key_and[wv] = kand;
+        sh.key_or[wv] = kor;
+    }
+    __syncthreads();
+    {
+        const int i = l & (kSelWaves - 1);
+        kand = wave_and(sh.key_and[i]);
+        kor = wave_or(sh.key_or[i]);
+    }
+    const uint32_t diff = kand ^ kor;
+    if (diff == 0u) {  // every key equal: the first K of them
+        __syncthreads();  // key_and / key_or read before a next call rewrites them
+        r.kth = kand;
+        r.quota = K;
+        return r;
+    }
+    const int top = 31 - __builtin_clz(diff);  // highest differing bit
+    uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
+    uint32_t prefix = kand & pmask;
+    uint32_t remaining = static_cast<uint32_t>(K);
+    uint32_t *own = sh.hist[wv];
+    for (int sft = top - 7;; sft -= 8) {
+        const int shift = sft > 0 ? sft : 0;
+        for (int i = l; i < 256; i += kWave) own[i] = 0u;
+        wave_fence();
+#pragma unroll
+        for (int e = 0; e < kSelRegs; ++e)
+            if (e * kSelThreads < n) hist_add_peel(e * kSelThreads + tid < n, key[e], prefix, pmask, shift, own, l);
+        __syncthreads();
+        if (tid < kWave) {
+            uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+            for (int w = 0; w < kSelWaves; ++w) {
+                const uint4 h = *reinterpret_cast<const uint4 *>(&sh.hist[w][4 * l]);
+                c0 += h.x;
+                c1 += h.y;
+                c2 += h.z;
+                c3 += h.w;
+            }
+            const uint32_t tot = c0 + c1 + c2 + c3;
+            const uint32_t suf = wave_suffix_sum(tot);
+            const uint32_t above = suf - tot;
+            if (above < remaining && remaining <= suf) {
+                uint32_t cum = above, dig;
+                if (cum + c3 >= remaining) {
+                    dig = 4 * l + 3;
+                } else {
+                    cum += c3;
+                    if (cum + c2 >= remaining) {
+                        dig = 4 * l + 2;
+                    } else {
+                        cum += c2;
+                        if (cum + c1 >= remaining) {
+                            dig = 4 * l + 1;
+                        } else {
+                            cum += c1;
+                            dig = 4 * l;
+                        }
+                    }
+                }
+                sh.bcast[0] = dig;
+                sh.bcast[1] = cum;
+            }
+        }
+        __syncthreads();
+        remaining -= sh.bcast[1];
+        prefix |= sh.bcast[0] << shift;
+        pmask |= 0xFFu << shift;
+        if (shift == 0) break;
+    }
+    r.kth = prefix;
+    r.quota = static_cast<int>(remaining);
+    return r;
+}
+
+// Keys of entries j = e * kSelThreads + tid of sc[0, n) (n <= kSelRegs *
+// kSelThreads); every load instruction reads 256 contiguous bytes per wave,
+// and all of them are issued before the first key is formed.
+template <int AS>
+__device__ __forceinline__ void block_load_keys(const float *sc, int n, uint32_t (&key)[kSelRegs])
 {
     const int tid = threadIdx.x;
-    int eq_seen = 0, out = 0;
+    float x[kSelRegs];
+#pragma unroll
+    for (int e = 0; e < kSelRegs; ++e) {
+        const int j = e * kSelThreads + tid;
+        x[e] = e * kSelThreads < n ? load_as<AS>(sc, j < n ? j : n - 1) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kSelRegs; ++e) key[e] = e * kSelThreads + tid < n ? ord_key(x[e]) : 0u;
+}
+
+// Stable compaction of the entries of sc[0, n) (global memory, n >= 1)
+// whose score is above tau into out_v / out_p (score, position; LDS), in
+// ascending position; returns their number. A float comparison: the kept
+// set is {key > ord_key(tau)} (or {score > 0} when tau is -0), a threshold
+// set either way. A chunk whose survivors would pass cap is counted but not
+// written (the caller then falls back to the full row). A chunk is
+// kFiltRegs * kSelThreads entries, entry j0 + e * kSelThreads + tid in
+// thread tid, so each load instruction reads 256 contiguous bytes per wave
+// and a whole chunk is in flight while the previous one is compacted. Two
+// barriers per chunk: the (slot, wave) survivor counts are scanned by wave 0.
+constexpr int kFiltRegs = 16;
+
+__device__ int block_filter_above(const float *sc, int n, float tau, float *out_v, int32_t *out_p, int cap,
+                                  BlockShared &sh)
+{
+    static_assert(kFiltRegs == kSelWaves && kSelWaves * kSelWaves == 4 * kWave, "scan layout: 4 counts per lane");
+    constexpr int CH = kFiltRegs * kSelThreads;
+    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+    float vn[kFiltRegs];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int e = 0; e < kFiltRegs; ++e) {
+            const int j = j0 + e * kSelThreads + tid;
+            vn[e] = load_as<kGlobal>(sc, j < n ? j : n - 1);
+        }
+    };
+    int base = 0, par = 0;
+    auto chunk = [&](int j0, auto tail) {
+        float v[kFiltRegs];
+#pragma unroll
+        for (int e = 0; e < kFiltRegs; ++e) v[e] = vn[e];
+        if (j0 + CH < n) fetch(j0 + CH);
+        bool keep[kFiltRegs];
+        uint32_t cnt_l = 0;  // lane e < kFiltRegs: this wave's survivors in slot e
+#pragma unroll
+        for (int e = 0; e < kFiltRegs; ++e) {
+            keep[e] = v[e] > tau;
+            if constexpr (decltype(tail)::value) keep[e] = keep[e] && j0 + e * kSelThreads + tid < n;
+            // the ballot outside the conditional: every lane takes part
+            const uint32_t c = static_cast<uint32_t>(popc(ballot(keep[e])));
+            cnt_l = l == e ? c : cnt_l;
+        }
+        if (l < kFiltRegs) sh.fcnt[par][l * kSelWaves + wv] = static_cast<int>(cnt_l);
+        __syncthreads();
+        if (wv == 0) {
+            const int4 c = *reinterpret_cast<const int4 *>(sh.fcnt[par] + 4 * l);
+            const int tot = c.x + c.y + c.z + c.w;
+            const int ex = static_cast<int>(wave_incl_sum(static_cast<uint32_t>(tot))) - tot;
+            *reinterpret_cast<int4 *>(sh.foff[par] + 4 * l) = int4{ex, ex + c.x, ex + c.x + c.y, ex + c.x + c.y + c.z};
+            if (l == kWave - 1) sh.ftot[par] = ex + tot;
+        }
+        __syncthreads();
+        // lane e holds this wave's offset for slot e
+        const uint32_t off_l = l < kFiltRegs ? static_cast<uint32_t>(sh.foff[par][l * kSelWaves + wv]) : 0u;
+        const int chunk_total = sh.ftot[par];
+        if (base + chunk_total <= cap) {
+#pragma unroll
+            for (int e = 0; e < kFiltRegs; ++e) {
+                const uint64_t km = ballot(keep[e]);
+                if (keep[e]) {
+                    const int slot = base + static_cast<int>(lane_value(off_l, e)) + mbcnt(km);
+                    store_as<kLds>(out_v, slot, v[e]);
+                    store_as<kLds>(out_p, slot, j0 + e * kSelThreads + tid);
+                }
+            }
+        }
+        base += chunk_total;
+        par ^= 1;
+    };
+    fetch(0);
+    int j0 = 0;
+    for (; j0 + CH <= n; j0 += CH) chunk(j0, std::false_type{});
+    if (j0 < n) chunk(j0, std::true_type{});
+    __syncthreads();  // the compacted entries are visible to the block
+    return base;
+}
+
+// Walk sc[0..n) in order (AS: the address space of sc and pos) and call
+// emit(slot, position, score) for every entry selected by s, where position
+// is pos[j] (or j when pos is null); slots are dense and ascending. One
+// block prefix per chunk counts both the entries above kth and those equal
+// to it: an entry's slot is (entries above before it) + min(equal entries
+// before it, quota).
+template <int AS, class F>
+__device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, BlockShared &sh, F &&emit)
+{
+    constexpr int CH = kVec * kSelThreads;
+    const int tid = threadIdx.x;
+    int ab_seen = 0, eq_seen = 0;
     // the next chunk's loads are issued before the current chunk is processed
     float vn[kVec];
     int32_t pn[kVec];
@@ -1158,60 +1508,53 @@ template <class F> __device__ int block_emit(const float *sc, const int32_t *pos
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
             const int j = j0 + kVec * tid + e;
-            vn[e] = j < n ? sc[j] : 0.0f;
-            pn[e] = j < n ? (pos ? pos[j] : j) : 0;
+            const int jc = j < n ? j : n - 1;
+            vn[e] = load_as<AS>(sc, jc);
+            pn[e] = pos ? load_as<AS>(pos, jc) : j;
         }
     };
-    fetch(0);
-    for (int j0 = 0; j0 < n; j0 += kVec * kSelThreads) {
+    if (n > 0) fetch(0);
+    for (int j0 = 0; j0 < n; j0 += CH) {
         float v[kVec];
         int32_t p[kVec];
-        bool take[kVec], eq[kVec];
-        int neq = 0;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
             v[e] = vn[e];
             p[e] = pn[e];
         }
-        if (j0 + kVec * kSelThreads < n) fetch(j0 + kVec * kSelThreads);
+        if (j0 + CH < n) fetch(j0 + CH);
+        bool ab[kVec], eq[kVec];
+        int nab = 0, neq = 0;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            const int j = j0 + kVec * tid + e;
-            const bool in = j < n;
+            const bool in = j0 + kVec * tid + e < n;
             const uint32_t key = ord_key(v[e]);
+            ab[e] = in && (s.all || key > s.kth);
             eq[e] = in && !s.all && key == s.kth;
-            take[e] = in && (s.all || key > s.kth);
+            nab += ab[e];
             neq += eq[e];
         }
-        // ranks among equal keys, in position order
-        int rank, dummy, eq_tot, dummy_t;
-        block_prefix2(neq, 0, &rank, &dummy, &eq_tot, &dummy_t, sh);
-        rank += eq_seen;
-        eq_seen += eq_tot;
+        int pab, peq, tab, teq;
+        block_prefix2(nab, neq, &pab, &peq, &tab, &teq, sh);
+        int a_ = ab_seen + pab, q_ = eq_seen + peq;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            if (eq[e]) {
-                take[e] = rank < s.quota;
-                ++rank;
+            if (ab[e]) {
+                emit(a_ + (q_ < s.quota ? q_ : s.quota), p[e], v[e]);
+                ++a_;
+            } else if (eq[e]) {
+                if (q_ < s.quota) emit(a_ + q_, p[e], v[e]);
+                ++q_;
             }
         }
-        int nt = 0;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) nt += take[e];
-        int slot, d2, t_tot, d3;
-        block_prefix2(nt, 0, &slot, &d2, &t_tot, &d3, sh);
-        slot += out;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            if (take[e]) emit(slot++, p[e], v[e]);
-        }
-        out += t_tot;
+        ab_seen += tab;
+        eq_seen += teq;
     }
-    return out;
+    return ab_seen + (eq_seen < s.quota ? eq_seen : s.quota);
 }
 
 constexpr int kSurvivors = 12288;  // LDS capacity of the prefilter (entries)
-constexpr int kSampleMax = 8192;   // sampled scores held in LDS
+constexpr int kSampleMax = 8192;   // sampled scores (held in registers)
 
 __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
 {
@@ -1225,50 +1568,54 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         const int64_t b = gid / geo.G, m = gid % geo.G;
         const int64_t tl1 = geo.t_last(b, m) + 1;
         int n = static_cast<int>(tl1 > 0 ? tl1 : 0);
-        const float *sc = a.rows + gid * geo.Lk;
-        const int32_t *pos = nullptr;
+        const float *row = a.rows + gid * geo.Lk;
 
         // Sampled prefilter: tau from every stride-th score, then a stable
         // compaction of the scores > tau into LDS, where the exact select
         // runs. Falls back to the full row when the survivors overflow LDS
         // or are fewer than K (a sample that overshoots).
+        uint32_t key[kSelRegs];
+        bool in_lds = false, in_regs = false;
         if (n > 4 * a.K && 3 * a.K <= kSurvivors) {
             const int stride = n / kSampleMax + 1 > 16 ? n / kSampleMax + 1 : 16;
-            const int ns = (n + stride - 1) / stride;
-            float *smp = sel_scores;
-            for (int i = tid; i < ns; i += kSelThreads) smp[i] = sc[static_cast<int64_t>(i) * stride];
-            __syncthreads();
+            const int ns = (n + stride - 1) / stride;  // <= kSampleMax
+            float x[kSelRegs];
+#pragma unroll
+            for (int e = 0; e < kSelRegs; ++e) {
+                const int i = e * kSelThreads + tid;
+                x[e] = e * kSelThreads < ns ? load_as<kGlobal>(row, static_cast<int64_t>(i < ns ? i : ns - 1) * stride)
+                                            : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < kSelRegs; ++e) key[e] = e * kSelThreads + tid < ns ? ord_key(x[e]) : 0u;
             const float expect = static_cast<float>(a.K) * static_cast<float>(ns) / static_cast<float>(n);
             const int r = static_cast<int>(ceilf(expect + kSampleSigmas * sqrtf(expect) + 8.0f));
             if (r < ns) {
-                const Sel ts = block_select(smp, ns, r, sh);
-                Sel above;
-                above.all = false;
-                above.kth = ts.kth;  // keep keys strictly above the r-th sampled key
-                above.quota = 0;
-                __syncthreads();
-                const int kept = block_emit(sc, nullptr, n, above, sh, [&](int slot, int32_t p, float v) {
-                    if (slot < kSurvivors) {
-                        sel_scores[slot] = v;
-                        sel_pos[slot] = p;
-                    }
-                });
-                __syncthreads();
+                // keep keys strictly above the r-th sampled key
+                const Sel ts = block_select_regs(key, ns, r, sh);
+                const int kept = block_filter_above(row, n, key_float(ts.kth), sel_scores, sel_pos, kSurvivors, sh);
                 if (kept >= a.K && kept <= kSurvivors) {
                     n = kept;
-                    sc = sel_scores;
-                    pos = sel_pos;
+                    in_lds = true;
+                    block_load_keys<kLds>(sel_scores, n, key);
+                    in_regs = true;
                 }
             }
         }
-        const Sel s = block_select(sc, n, a.K, sh);
+        if (!in_regs && n <= kSelRegs * kSelThreads) {
+            block_load_keys<kGlobal>(row, n, key);
+            in_regs = true;
+        }
+        const Sel s = in_regs ? block_select_regs(key, n, a.K, sh) : block_select(row, n, a.K, sh);
         if (a.to_candidates) {
             int32_t *ci = a.out_idx + gid * a.out_stride;
             float *cs = a.out_sc ? a.out_sc + gid * a.out_stride : nullptr;
-            const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float v) {
+            auto emit = [&](int slot, int32_t p, float v) {
                 ci[slot] = p;
                 if (cs) cs[slot] = v;
-            });
+            };
+            const int got = in_lds ? block_emit<kLds>(sel_scores, sel_pos, n, s, sh, emit)
+                                   : block_emit<kGlobal>(row, nullptr, n, s, sh, emit);
             for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
                 ci[t] = -1;
                 if (cs) cs[t] = -INFINITY;
@@ -1278,12 +1625,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         }
         const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
         const int64_t stride = a.out_stride;
-        const int got = block_emit(sc, pos, n, s, sh, [&](int slot, int32_t p, float v) {
+        auto emit = [&](int slot, int32_t p, float v) {
             for (int64_t r = r0; r < r1; ++r) {
                 a.out_idx[(b * geo.Lq + r) * stride + slot] = p;
                 if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + slot] = v;
             }
-        });
+        };
+        const int got = in_lds ? block_emit<kLds>(sel_scores, sel_pos, n, s, sh, emit)
+                               : block_emit<kGlobal>(row, nullptr, n, s, sh, emit);
         for (int64_t r = r0; r < r1; ++r) {
             for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
                 a.out_idx[(b * geo.Lq + r) * stride + t] = -1;
@@ -1307,17 +1656,23 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         const int j = j0 + tid;
         cnt_le += (j < nc && C[j] <= t) ? 1 : 0;
     }
-    for (int o = 32; o > 0; o >>= 1) cnt_le += __shfl_xor(cnt_le, o);
+    cnt_le = static_cast<int>(wave_sum(static_cast<uint32_t>(cnt_le)));
     if ((tid & 63) == 0) sh.wave_sum[0][tid >> 6] = cnt_le;
     __syncthreads();
-    int nvalid = 0;
-    for (int i = 0; i < kSelWaves; ++i) nvalid += sh.wave_sum[0][i];
+    const int nvalid = static_cast<int>(row0_sum(static_cast<uint32_t>(sh.wave_sum[0][tid & (kSelWaves - 1)])));
     __syncthreads();
     const float *sc = a.rows + (gid * geo.g + mi) * static_cast<int64_t>(a.c);
-    const Sel s = block_select(sc, nvalid, a.K, sh);
+    Sel s;
+    if (nvalid <= kSelRegs * kSelThreads) {
+        uint32_t key[kSelRegs];
+        block_load_keys<kGlobal>(sc, nvalid, key);
+        s = block_select_regs(key, nvalid, a.K, sh);
+    } else {
+        s = block_select(sc, nvalid, a.K, sh);
+    }
     int32_t *oi = a.out_idx + row * a.out_stride;
     float *os = a.out_sc ? a.out_sc + row * a.out_stride : nullptr;
-    const int got = block_emit(sc, C, nvalid, s, sh, [&](int slot, int32_t p, float v) {
+    const int got = block_emit<kGlobal>(sc, C, nvalid, s, sh, [&](int slot, int32_t p, float v) {
         oi[slot] = p;
         if (os) os[slot] = v;
     });
@@ -1374,22 +1729,31 @@ __device__ __forceinline__ int count_ge(const uint32_t (&kv)[N], uint32_t x)
     return n;
 }
 
+// Wave-uniform max / min: the prefix-scan pattern of wave_incl_sum, read
+// from the last lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t x = __shfl_xor(v, o);
-        v = x > v ? x : v;
-    }
-    return v;
+    uint32_t t;
+    t = dpp_move<0x111>(v, 0u), v = t > v ? t : v;
+    t = dpp_move<0x112>(v, 0u), v = t > v ? t : v;
+    t = dpp_move<0x114>(v, 0u), v = t > v ? t : v;
+    t = dpp_move<0x118>(v, 0u), v = t > v ? t : v;
+    t = dpp_move<0x142, 0xA>(v, 0u), v = t > v ? t : v;
+    t = dpp_move<0x143, 0xC>(v, 0u), v = t > v ? t : v;
+    return lane_value(v, kWave - 1);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t x = __shfl_xor(v, o);
-        v = x < v ? x : v;
-    }
-    return v;
+    constexpr uint32_t kTop = 0xFFFFFFFFu;
+    uint32_t t;
+    t = dpp_move<0x111>(v, kTop), v = t < v ? t : v;
+    t = dpp_move<0x112>(v, kTop), v = t < v ? t : v;
+    t = dpp_move<0x114>(v, kTop), v = t < v ? t : v;
+    t = dpp_move<0x118>(v, kTop), v = t < v ? t : v;
+    t = dpp_move<0x142, 0xA>(v, kTop), v = t < v ? t : v;
+    t = dpp_move<0x143, 0xC>(v, kTop), v = t < v ? t : v;
+    return lane_value(v, kWave - 1);
 }
 
 // The best K of n entries (score desc, then lower entry index), emitted in
@@ -1454,11 +1818,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             // lane l holds bins 4l .. 4l+3; suffix counts run from the top bin
             const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
             const uint32_t tot = c0 + c1 + c2 + c3;
-            uint32_t suf = tot;
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t t = __shfl_down(suf, o);
-                if (l + o < kWave) suf += t;
-            }
+            const uint32_t suf = wave_suffix_sum(tot);
             const uint32_t above_lane = suf - tot;
             const bool here = above_lane < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= suf;
             const int src = __ffsll(static_cast<long long>(ballot(here))) - 1;
@@ -1478,9 +1838,9 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
                 }
                 abv = cum;
             }
-            bb = __shfl(bb, src);
-            abv = __shfl(abv, src);
-            cnt = __shfl(cnt, src);
+            bb = static_cast<int>(lane_value(static_cast<uint32_t>(bb), src));
+            abv = lane_value(abv, src);
+            cnt = lane_value(cnt, src);
             wave_fence();
             if (cnt <= static_cast<uint32_t>(kMsMid)) {
                 const uint32_t blo = lo + (static_cast<uint32_t>(bb) << shift);
@@ -1885,7 +2245,7 @@ __device__ __forceinline__ int64_t xcd_unit(int64_t i, int64_t n)
 // ahead, and the scoring is the scan's pipelined tile_step. Groups are
 // ordered per XCD, so neighbouring groups (whose candidate sets overlap)
 // share an L2.
-template <int H, int D, int NW>
+template <int H, int D, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
@@ -1923,7 +2283,11 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
 
     // positions of the key rows this lane gathers for a tile (slices
     // wv + nwaves j, tile rows slice_row(slice, l)), loaded a tile ahead and
-    // consumed raw by the DMA issue, so the loads never stall the MFMAs
+    // consumed raw by the DMA issue, so the loads never stall the MFMAs.
+    // Paged keys add a step: positions are loaded two tiles ahead, and one
+    // tile ahead become page offsets plus table entries (loaded), which the
+    // issue combines; every array is written once per tile, so no loaded
+    // value is copied (a copy would wait for the loads in flight).
     auto load_pos = [&](int tile_idx, int32_t (&pos)[kMaxSlices]) {
 #pragma unroll
         for (int j = 0; j < kMaxSlices; ++j) {
@@ -1931,12 +2295,28 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
             pos[j] = cj < nc ? C[cj] : 0;  // row 0: any valid key (masked)
         }
     };
-    auto issue_tile = [&](int buf, const int32_t (&pos)[kMaxSlices]) {
+    auto load_entries = [&](const int32_t (&pos)[kMaxSlices], int32_t (&off)[kMaxSlices],
+                            int32_t (&ent)[kMaxSlices]) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int j = 0; j < kMaxSlices; ++j) {
+                const uint32_t sp = static_cast<uint32_t>(pos[j]);
+                off[j] = static_cast<int32_t>(a.keys.page_offset(sp));
+                // computed here, not sunk below the reload of pos (which
+                // would then need other registers and a waited copy)
+                asm volatile("" : "+v"(off[j]));
+                ent[j] = a.keys.entry(b, sp);
+            }
+        }
+    };
+    // key = positions (contiguous) or page offsets (paged)
+    auto issue_tile = [&](int buf, const int32_t (&key)[kMaxSlices], const int32_t (&ent)[kMaxSlices]) {
         uint16_t *dst = buf ? tile1 : tile0;
 #pragma unroll
         for (int j = 0; j < kMaxSlices; ++j) {
             const int slice = wv + nwaves * j;
-            const uint16_t *src = kbase + a.keys.row(b, pos[j]) * D + slice_col(slice, l);
+            const int64_t r = PAGED ? a.keys.paged_row(ent[j], static_cast<uint32_t>(key[j])) : a.keys.flat(b, key[j]);
+            const uint16_t *src = kbase + r * D + slice_col(slice, l);
             __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(dst + slice * 512), 16, 0, 0);
         }
     };
@@ -1953,10 +2333,20 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
         load_a<H>(static_cast<const uint16_t *>(a.q) + (b * geo.Lq + r) * H * D, l, afr);
         load_w<H>(a.w + (b * geo.Lq + r) * H, l, wr);
 
-        int32_t pos[kMaxSlices];
+        int32_t pos[kMaxSlices], off[kMaxSlices] = {}, ent[kMaxSlices] = {};
         load_pos(tile_lo, pos);
-        issue_tile(0, pos);
-        if (ntiles > 1) load_pos(tile_lo + 1, pos);
+        if constexpr (PAGED) {
+            load_entries(pos, off, ent);
+            issue_tile(0, off, ent);
+            if (ntiles > 1) {
+                load_pos(tile_lo + 1, pos);
+                load_entries(pos, off, ent);
+            }
+            if (ntiles > 2) load_pos(tile_lo + 2, pos);
+        } else {
+            issue_tile(0, pos, ent);
+            if (ntiles > 1) load_pos(tile_lo + 1, pos);
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         tile_barrier();
 
@@ -1973,8 +2363,18 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
             // the buffer of tile it + 1 held tile it - 1, which every wave
             // finished reading before the last barrier
             if (it + 1 < ntiles) {
-                issue_tile(cur ^ 1, pos);
-                if (it + 2 < ntiles) load_pos(tile_lo + it + 2, pos);
+                if constexpr (PAGED) {
+                    issue_tile(cur ^ 1, off, ent);
+                    if (it + 2 < ntiles) {
+                        load_entries(pos, off, ent);
+                        // the positions are read before they are reloaded
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (it + 3 < ntiles) load_pos(tile_lo + it + 3, pos);
+                    }
+                } else {
+                    issue_tile(cur ^ 1, pos, ent);
+                    if (it + 2 < ntiles) load_pos(tile_lo + it + 2, pos);
+                }
             }
             const int ti = tile_lo + it;
             auto emit = [&](int qt, float score) {
@@ -2121,10 +2521,15 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * a.splits));
     if (mfma_shape(sh)) {
         // 4 or 8 member waves; more members loop in rounds
-        if (L.g <= 4)
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4>), grid, dim3(64 * 4), 0, st, a);
+        const bool paged = sh.pages.table != nullptr;
+        if (L.g <= 4 && paged)
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4, true>), grid, dim3(64 * 4), 0, st, a);
+        else if (L.g <= 4)
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4, false>), grid, dim3(64 * 4), 0, st, a);
+        else if (paged)
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8, true>), grid, dim3(64 * 8), 0, st, a);
         else
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8>), grid, dim3(64 * 8), 0, st, a);
+            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8, false>), grid, dim3(64 * 8), 0, st, a);
     } else if (sh.bf16) {
         hipLaunchKernelGGL(k_refine_exact<uint16_t>, grid, dim3(256), 0, st, a);
     } else {
@@ -2149,7 +2554,10 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.D = sh.D;
     a.rows = L.rows;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
-    hipLaunchKernelGGL((k_scan_split<64, 128>), grid, dim3(256), 0, st, a, splits);
+    if (sh.pages.table)
+        hipLaunchKernelGGL((k_scan_split<64, 128, true>), grid, dim3(256), 0, st, a, splits);
+    else
+        hipLaunchKernelGGL((k_scan_split<64, 128, false>), grid, dim3(256), 0, st, a, splits);
     return hipGetLastError();
 }
 

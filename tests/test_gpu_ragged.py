@@ -79,7 +79,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("variant", ["dense", "reuse", "refine"])
-@pytest.mark.parametrize("page", [0, 16, 64])
+@pytest.mark.parametrize("page", [0, 16, 48, 64])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_ragged_and_paged_match_oracle_bitwise(case, page, variant):
     name, B, Lq, Lk, H, d, g, topk, c, dt = case
