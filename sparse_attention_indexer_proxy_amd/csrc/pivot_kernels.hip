@@ -1129,7 +1129,8 @@ struct BlockShared {
     alignas(16) uint32_t hist[kSelWaves][256];  // one histogram per wave (no inter-wave atomic contention)
     int wave_sum[2][kSelWaves];
     uint32_t bcast[4];
-    uint32_t key_and[kSelWaves], key_or[kSelWaves];  // block_select_regs
+    uint32_t key_and[kSelWaves], key_or[kSelWaves];  // block_select_keys
+    uint32_t small[4 * kWave];                        // block_select_keys: the last bin's keys
     // block_filter_above: per-chunk survivor counts and their offsets, in
     // (slot e, wave) order, double-buffered over chunks
     alignas(16) int fcnt[2][kSelWaves * kSelWaves];
@@ -1296,7 +1297,15 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v)
     return lane_value(v, kWave - 1);
 }
 
-__device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, BlockShared &sh)
+// Generic form: N keys per thread, valid(e) this lane's key e is an entry,
+// any(e) a wave-uniform "slot e may hold entries" (false skips the slot); n
+// is the number of entries. Once the chosen digit's bin holds at most
+// kSmall keys, they are compacted into LDS and wave 0 resolves the remaining
+// bits by bisection over them (two barriers instead of further digits).
+constexpr int kSmall = 4 * kWave;
+
+template <int N, class Valid, class Any>
+__device__ Sel block_select_keys(const uint32_t (&key)[N], Valid &&valid, Any &&any, int n, int K, BlockShared &sh)
 {
     Sel r;
     if (n <= K) {
@@ -1310,9 +1319,9 @@ __device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, 
     // bits shared by every valid key
     uint32_t kand = ~0u, kor = 0u;
 #pragma unroll
-    for (int e = 0; e < kSelRegs; ++e) {
-        if (e * kSelThreads < n) {
-            const bool in = e * kSelThreads + tid < n;
+    for (int e = 0; e < N; ++e) {
+        if (any(e)) {
+            const bool in = valid(e);
             kand &= in ? key[e] : ~0u;
             kor |= in ? key[e] : 0u;
         }
@@ -1346,8 +1355,8 @@ __device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, 
         for (int i = l; i < 256; i += kWave) own[i] = 0u;
         wave_fence();
 #pragma unroll
-        for (int e = 0; e < kSelRegs; ++e)
-            if (e * kSelThreads < n) hist_add_peel(e * kSelThreads + tid < n, key[e], prefix, pmask, shift, own, l);
+        for (int e = 0; e < N; ++e)
+            if (any(e)) hist_add_peel(valid(e), key[e], prefix, pmask, shift, own, l);
         __syncthreads();
         if (tid < kWave) {
             uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
@@ -1363,25 +1372,27 @@ __device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, 
             const uint32_t suf = wave_suffix_sum(tot);
             const uint32_t above = suf - tot;
             if (above < remaining && remaining <= suf) {
-                uint32_t cum = above, dig;
+                uint32_t cum = above, dig, cnt;
                 if (cum + c3 >= remaining) {
-                    dig = 4 * l + 3;
+                    dig = 4 * l + 3, cnt = c3;
                 } else {
                     cum += c3;
                     if (cum + c2 >= remaining) {
-                        dig = 4 * l + 2;
+                        dig = 4 * l + 2, cnt = c2;
                     } else {
                         cum += c2;
                         if (cum + c1 >= remaining) {
-                            dig = 4 * l + 1;
+                            dig = 4 * l + 1, cnt = c1;
                         } else {
                             cum += c1;
-                            dig = 4 * l;
+                            dig = 4 * l, cnt = c0;
                         }
                     }
                 }
                 sh.bcast[0] = dig;
                 sh.bcast[1] = cum;
+                sh.bcast[2] = cnt;
+                sh.bcast[3] = 0u;  // compaction counter of the small path
             }
         }
         __syncthreads();
@@ -1389,10 +1400,64 @@ __device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, 
         prefix |= sh.bcast[0] << shift;
         pmask |= 0xFFu << shift;
         if (shift == 0) break;
+        if (sh.bcast[2] <= static_cast<uint32_t>(kSmall)) {
+            // few keys left in the bin: compact them, wave 0 bisects the
+            // bits below this digit
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                if (any(e)) {
+                    const bool m = valid(e) && (key[e] & pmask) == prefix;
+                    const uint64_t mm = ballot(m);
+                    if (mm != 0) {
+                        const int first = __ffsll(static_cast<long long>(mm)) - 1;
+                        uint32_t base = 0;
+                        if (l == first) base = atomicAdd(&sh.bcast[3], static_cast<uint32_t>(popc(mm)));
+                        base = lane_value(base, first);
+                        if (m) sh.small[base + mbcnt(mm)] = key[e];
+                    }
+                }
+            }
+            __syncthreads();
+            if (tid < kWave) {
+                const int ns = static_cast<int>(sh.bcast[2]);
+                uint32_t v[kSmall / kWave];
+#pragma unroll
+                for (int q = 0; q < kSmall / kWave; ++q) v[q] = kWave * q + l < ns ? sh.small[kWave * q + l] : 0u;
+                auto count_ge_small = [&](uint32_t x) {
+                    int c = 0;
+#pragma unroll
+                    for (int q = 0; q < kSmall / kWave; ++q) c += popc(ballot(v[q] >= x));
+                    return c;
+                };
+                // the largest x with #{v >= x} >= remaining (bits below shift)
+                uint32_t x = prefix;
+                for (int bit = shift - 1; bit >= 0; --bit) {
+                    const uint32_t t = x | (1u << bit);
+                    if (count_ge_small(t) >= static_cast<int>(remaining)) x = t;
+                }
+                const int gt = x == 0xFFFFFFFFu ? 0 : count_ge_small(x + 1u);
+                if (l == 0) {
+                    sh.bcast[0] = x;
+                    sh.bcast[1] = remaining - static_cast<uint32_t>(gt);
+                }
+            }
+            __syncthreads();
+            r.kth = sh.bcast[0];
+            r.quota = static_cast<int>(sh.bcast[1]);
+            __syncthreads();  // bcast read before a next call rewrites it
+            return r;
+        }
     }
     r.kth = prefix;
     r.quota = static_cast<int>(remaining);
     return r;
+}
+
+__device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, BlockShared &sh)
+{
+    const int tid = threadIdx.x;
+    return block_select_keys(
+        key, [&](int e) { return e * kSelThreads + tid < n; }, [&](int e) { return e * kSelThreads < n; }, n, K, sh);
 }
 
 // Keys of entries j = e * kSelThreads + tid of sc[0, n) (n <= kSelRegs *
@@ -1650,32 +1715,86 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
     const int64_t t = geo.pos(b, r);
     const int nc = a.cand_n[gid];
     const int32_t *C = a.cand + gid * a.c;
-    // candidates s <= t are a prefix of C (ascending): count them
-    int cnt_le = 0;
-    for (int j0 = 0; j0 < nc; j0 += kSelThreads) {
-        const int j = j0 + tid;
-        cnt_le += (j < nc && C[j] <= t) ? 1 : 0;
-    }
-    cnt_le = static_cast<int>(wave_sum(static_cast<uint32_t>(cnt_le)));
-    if ((tid & 63) == 0) sh.wave_sum[0][tid >> 6] = cnt_le;
-    __syncthreads();
-    const int nvalid = static_cast<int>(row0_sum(static_cast<uint32_t>(sh.wave_sum[0][tid & (kSelWaves - 1)])));
-    __syncthreads();
     const float *sc = a.rows + (gid * geo.g + mi) * static_cast<int64_t>(a.c);
-    Sel s;
-    if (nvalid <= kSelRegs * kSelThreads) {
-        uint32_t key[kSelRegs];
-        block_load_keys<kGlobal>(sc, nvalid, key);
-        s = block_select_regs(key, nvalid, a.K, sh);
-    } else {
-        s = block_select(sc, nvalid, a.K, sh);
-    }
     int32_t *oi = a.out_idx + row * a.out_stride;
     float *os = a.out_sc ? a.out_sc + row * a.out_stride : nullptr;
-    const int got = block_emit<kGlobal>(sc, C, nvalid, s, sh, [&](int slot, int32_t p, float v) {
-        oi[slot] = p;
-        if (os) os[slot] = v;
-    });
+    int got;
+    if (a.c <= kVec * kSelThreads) {
+        // the whole row in registers, entries 4 tid .. 4 tid + 3: loaded
+        // once, counted, selected and emitted without another pass
+        int32_t cp[kVec];
+        float cv[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const int j = kVec * tid + e;
+            const int jc = j < a.c ? j : a.c - 1;
+            cp[e] = load_as<kGlobal>(C, jc);
+            cv[e] = load_as<kGlobal>(sc, jc);
+        }
+        // candidates s <= t are a prefix of C (ascending): count them
+        int cnt_le = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) cnt_le += (kVec * tid + e < nc && cp[e] <= t) ? 1 : 0;
+        cnt_le = static_cast<int>(wave_sum(static_cast<uint32_t>(cnt_le)));
+        if ((tid & 63) == 0) sh.wave_sum[0][tid >> 6] = cnt_le;
+        __syncthreads();
+        const int nvalid =
+            static_cast<int>(row0_sum(static_cast<uint32_t>(sh.wave_sum[0][tid & (kSelWaves - 1)])));
+        __syncthreads();
+        uint32_t key[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) key[e] = ord_key(cv[e]);
+        const Sel s = block_select_keys(
+            key, [&](int e) { return kVec * tid + e < nvalid; }, [](int) { return true; }, nvalid, a.K, sh);
+        bool ab[kVec], eq[kVec];
+        int nab = 0, neq = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const bool in = kVec * tid + e < nvalid;
+            ab[e] = in && (s.all || key[e] > s.kth);
+            eq[e] = in && !s.all && key[e] == s.kth;
+            nab += ab[e];
+            neq += eq[e];
+        }
+        int pab, peq, tab, teq;
+        block_prefix2(nab, neq, &pab, &peq, &tab, &teq, sh);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            int slot = -1;
+            if (ab[e]) slot = pab + (peq < s.quota ? peq : s.quota), ++pab;
+            else if (eq[e]) slot = peq < s.quota ? pab + peq : -1, ++peq;
+            if (slot >= 0) {
+                oi[slot] = cp[e];
+                if (os) os[slot] = cv[e];
+            }
+        }
+        got = tab + (teq < s.quota ? teq : s.quota);
+    } else {
+        // candidates s <= t are a prefix of C (ascending): count them
+        int cnt_le = 0;
+        for (int j0 = 0; j0 < nc; j0 += kSelThreads) {
+            const int j = j0 + tid;
+            cnt_le += (j < nc && C[j] <= t) ? 1 : 0;
+        }
+        cnt_le = static_cast<int>(wave_sum(static_cast<uint32_t>(cnt_le)));
+        if ((tid & 63) == 0) sh.wave_sum[0][tid >> 6] = cnt_le;
+        __syncthreads();
+        const int nvalid =
+            static_cast<int>(row0_sum(static_cast<uint32_t>(sh.wave_sum[0][tid & (kSelWaves - 1)])));
+        __syncthreads();
+        Sel s;
+        if (nvalid <= kSelRegs * kSelThreads) {
+            uint32_t key[kSelRegs];
+            block_load_keys<kGlobal>(sc, nvalid, key);
+            s = block_select_regs(key, nvalid, a.K, sh);
+        } else {
+            s = block_select(sc, nvalid, a.K, sh);
+        }
+        got = block_emit<kGlobal>(sc, C, nvalid, s, sh, [&](int slot, int32_t p, float v) {
+            oi[slot] = p;
+            if (os) os[slot] = v;
+        });
+    }
     for (int x = got + tid; x < a.out_stride; x += kSelThreads) {
         oi[x] = -1;
         if (os) os[x] = -INFINITY;
