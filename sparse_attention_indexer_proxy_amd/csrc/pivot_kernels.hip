@@ -766,16 +766,17 @@ constexpr int kSampleStride = 32;     // tiles between sampled tiles (>= this)
 constexpr float kSampleSigmas = 6.0f;
 
 // Fused-scan workgroup shape: kScanWaves groups (one per wave) share each
-// 128-key tile; kScanBufs tiles are in LDS or in flight at once. The kernel
-// needs about 240 VGPRs, so a CU holds eight of its waves: one workgroup of
-// eight waves with two buffers measured faster than two workgroups of four
-// (each key tile is fetched once per eight groups instead of four) and than
-// a third buffer (L=128K, g=8: 16.4 ms vs 20.8 and 16.8).
+// 256-key tile (64 KiB); kScanBufs tiles are in LDS or in flight at once.
+// The kernel needs about 220 VGPRs, so a CU holds eight of its waves: one
+// workgroup of eight waves with two buffers measured faster than two
+// workgroups of four (each key tile is fetched once per eight groups instead
+// of four) and than a third buffer (L=128K, g=8: 16.4 ms vs 20.8 and 16.8);
+// 256-key tiles (half the barriers) beat 128-key ones by 1.5% (13.6 vs 13.8 ms).
 #ifndef PIVOT_SCAN_WAVES
 #define PIVOT_SCAN_WAVES 8
 #endif
 #ifndef PIVOT_SCAN_TILE
-#define PIVOT_SCAN_TILE 128
+#define PIVOT_SCAN_TILE 256
 #endif
 #ifndef PIVOT_SCAN_BUFS
 #define PIVOT_SCAN_BUFS 2
