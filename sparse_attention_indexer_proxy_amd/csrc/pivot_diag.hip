@@ -4,11 +4,14 @@
 // indexer-score mass saturates. Rows are the indexer's outputs: the selected
 // positions in ascending order, then -1.
 //
-//   k_row_overlap   one wave per row t: |T_t ∩ T_{t+d}|; the partner row sits
-//                   in LDS and every entry of T_t is found by a branch-free
-//                   binary search over it.
-//   k_group_sets    one workgroup per group: its rows merged pairwise in LDS
-//                   into one sorted multiset; distinct values = union, values
+//   k_row_overlap   one wave per row t: |T_t ∩ T_{t+d}|; the partner row is
+//                   a bitmap in LDS (positions below 2^17) probed once per
+//                   entry of T_t, else a sorted array searched by bisection.
+//   k_group_bits    one workgroup per group whose positions are below 2^17:
+//                   the union is the OR of the rows' bitmaps, the
+//                   intersection their AND.
+//   k_group_sets    the other groups: rows merged pairwise in LDS into one
+//                   sorted multiset; distinct values = union, values
 //                   occurring in every row = intersection.
 //   k_row_mass      one wave per row: the row's scores as ordered keys in
 //                   registers; the j-th largest (three j at once) by bisection
@@ -28,9 +31,54 @@ constexpr int kW = 64;            // wavefront
 constexpr int kRowMax = 4096;     // row width limit (LDS / registers)
 constexpr int kGroupMax = 16384;  // padded g * k limit of the group kernel (LDS)
 constexpr int kDiagWaves = 4;
+constexpr int kBitWords = 4096;   // bitmaps of positions below 32 * 4096 = 2^17
+constexpr int32_t kNotHere = -2;  // group result left to the merge kernel
 
 __device__ __forceinline__ int lane() { return threadIdx.x & (kW - 1); }
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+// Wave reductions on DPP lane moves (gfx9: row_shr:n = 0x110 + n,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143; lanes without a source take
+// `fill`): a Hillis-Steele scan whose last lane holds the result.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ int32_t dpp_move(int32_t v, int32_t fill)
+{
+    return __builtin_amdgcn_update_dpp(fill, v, Ctrl, RowMask, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ int32_t wave_reduce(int32_t v, int32_t fill, Op op)
+{
+    v = op(v, dpp_move<0x111>(v, fill));
+    v = op(v, dpp_move<0x112>(v, fill));
+    v = op(v, dpp_move<0x114>(v, fill));
+    v = op(v, dpp_move<0x118>(v, fill));
+    v = op(v, dpp_move<0x142, 0xA>(v, fill));
+    v = op(v, dpp_move<0x143, 0xC>(v, fill));
+    return __builtin_amdgcn_readlane(v, kW - 1);
+}
+
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v)
+{
+    return wave_reduce(v, INT32_MAX, [](int32_t x, int32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v)
+{
+    return wave_reduce(v, INT32_MIN, [](int32_t x, int32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(
+        wave_reduce(static_cast<int32_t>(v), 0, [](int32_t x, int32_t y) { return static_cast<int32_t>(static_cast<uint32_t>(x) + static_cast<uint32_t>(y)); }));
+}
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(wave_reduce(static_cast<int32_t>(v), -1, [](int32_t x, int32_t y) { return x & y; }));
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(wave_reduce(static_cast<int32_t>(v), 0, [](int32_t x, int32_t y) { return x | y; }));
+}
 
 // A row's entries, lane l holding entries 64 i + l (all loads issued at once;
 // past k reads as -1), and its valid length: the prefix before the first -1.
@@ -43,11 +91,7 @@ __device__ __forceinline__ int load_row(const int32_t *row, int k, int32_t (&v)[
     int n = NV * kW < k ? NV * kW : k;
 #pragma unroll
     for (int i = NV - 1; i >= 0; --i) n = v[i] < 0 ? kW * i + l : n;  // this lane's first pad
-    for (int o = kW / 2; o > 0; o >>= 1) {
-        const int x = __shfl_xor(n, o);
-        n = x < n ? x : n;
-    }
-    return n;
+    return wave_min_i32(n);
 }
 
 // Whether x is among the n ascending entries p[0..n).
@@ -62,7 +106,9 @@ __device__ __forceinline__ bool sorted_has(const int32_t *p, int n, int32_t x)
 template <int NV>
 __global__ __launch_bounds__(kDiagWaves * kW) void k_row_overlap(StatsArgs a)
 {
-    extern __shared__ int32_t dyn[];  // kDiagWaves rows of a.k entries
+    // per wave: the partner row as a bitmap (positions < 32 * kBitWords) or
+    // as a sorted array (k <= kRowMax = kBitWords entries)
+    __shared__ uint32_t lds[kDiagWaves][kBitWords];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane();
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kDiagWaves + wv;
@@ -75,20 +121,135 @@ __global__ __launch_bounds__(kDiagWaves * kW) void k_row_overlap(StatsArgs a)
     int32_t v0[NV], v1[NV];
     const int n0 = load_row(a.idx + row * a.k, a.k, v0);
     const int n1 = load_row(a.idx + (row + a.d) * a.k, a.k, v1);
-    int32_t *p = dyn + wv * a.k;
+    uint32_t *bm = lds[wv];
+    int32_t mx = INT32_MIN;  // the partner row's largest entry (its last valid one)
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-        if (kW * i + l < n1) p[kW * i + l] = v1[i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = 0; i < NV; ++i) mx = kW * i + l < n1 && v1[i] > mx ? v1[i] : mx;
+    mx = wave_max_i32(mx);
     int cnt = 0;
+    if (mx < 32 * kBitWords) {
+        // bitmap: clear the words in use, set the partner's bits, probe
+        const int words = mx < 0 ? 0 : (mx >> 5) + 1;
+        for (int w = l; w < words; w += kW) bm[w] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int j = kW * i + l;
-        cnt += popc64(__ballot(j < n0 && sorted_has(p, n1, v0[i])));
+        for (int i = 0; i < NV; ++i)
+            if (kW * i + l < n1) atomicOr(&bm[v1[i] >> 5], 1u << (v1[i] & 31));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int32_t x = v0[i];
+            const bool in = kW * i + l < n0 && x <= mx;  // valid entries are >= 0
+            const bool hit = in && ((bm[in ? x >> 5 : 0] >> (x & 31)) & 1u);
+            cnt += popc64(__ballot(hit));
+        }
+    } else {
+        int32_t *p = reinterpret_cast<int32_t *>(bm);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (kW * i + l < n1) p[kW * i + l] = v1[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int j = kW * i + l;
+            cnt += popc64(__ballot(j < n0 && sorted_has(p, n1, v0[i])));
+        }
     }
     if (l == 0) a.overlap[row] = cnt;
+}
+
+// Groups whose positions are all below 32 * kBitWords: the union is the OR
+// of the rows' bitmaps, the intersection their AND, built row by row in LDS
+// (rows are sets; each thread holds up to kSeg of the group's entries). A
+// group with a larger position is marked kNotHere in its first requested
+// output for k_group_sets.
+constexpr int kSetThreads = 512;
+constexpr int kSeg = kGroupMax / kSetThreads;  // entries per thread (32)
+
+__global__ __launch_bounds__(kSetThreads) void k_group_bits(StatsArgs a)
+{
+    __shared__ uint32_t U[kBitWords], A[kBitWords], T[kBitWords];
+    __shared__ int32_t red[kSetThreads / kW][2];
+    const int64_t gid = blockIdx.x;
+    const int64_t b = gid / a.G, m = gid - b * a.G;
+    const int64_t t0 = m * a.g;
+    const int gm = static_cast<int>((t0 + a.g < a.Lq ? t0 + a.g : a.Lq) - t0);
+    const int N = gm * a.k;  // <= kGroupMax (checked by the caller)
+    const int tid = threadIdx.x, l = lane(), wv = tid >> 6;
+    const int32_t *g0 = a.idx + (b * a.Lq + t0) * a.k;
+    int32_t ld[kSeg];
+    int32_t mx = INT32_MIN;
+#pragma unroll
+    for (int q = 0; q < kSeg; ++q) {
+        const int e = tid + q * kSetThreads;
+        ld[q] = e < N ? g0[e] : -1;  // -1: padding (rows are their valid prefix, then -1)
+        mx = ld[q] > mx ? ld[q] : mx;
+    }
+    mx = wave_max_i32(mx);
+    if (l == 0) red[wv][0] = mx;
+    __syncthreads();
+    mx = wave_max_i32(red[l & (kSetThreads / kW - 1)][0]);
+    if (mx >= 32 * kBitWords) {
+        if (tid == 0) {
+            if (a.group_union) a.group_union[gid] = kNotHere;
+            else a.group_inter[gid] = kNotHere;
+        }
+        return;  // uniform
+    }
+    const int words = mx < 0 ? 0 : (mx >> 5) + 1;
+    for (int w = tid; w < words; w += kSetThreads) U[w] = A[w] = T[w] = 0u;
+    __syncthreads();
+    // every row into U, row 0 into A
+#pragma unroll
+    for (int q = 0; q < kSeg; ++q) {
+        const int e = tid + q * kSetThreads;
+        if (ld[q] >= 0) {
+            const uint32_t bit = 1u << (ld[q] & 31);
+            atomicOr(&U[ld[q] >> 5], bit);
+            if (e < a.k) atomicOr(&A[ld[q] >> 5], bit);
+        }
+    }
+    __syncthreads();
+    for (int r = 1; r < gm; ++r) {
+#pragma unroll
+        for (int q = 0; q < kSeg; ++q) {
+            const int e = tid + q * kSetThreads;
+            if (ld[q] >= 0 && e >= r * a.k && e < (r + 1) * a.k) atomicOr(&T[ld[q] >> 5], 1u << (ld[q] & 31));
+        }
+        __syncthreads();
+        for (int w = tid; w < words; w += kSetThreads) {
+            A[w] &= T[w];
+            T[w] = 0u;
+        }
+        __syncthreads();
+    }
+    uint32_t nu = 0, ni = 0;
+    for (int w = tid; w < words; w += kSetThreads) {
+        nu += __popc(U[w]);
+        ni += __popc(A[w]);
+    }
+    nu = wave_sum_u32(nu);
+    ni = wave_sum_u32(ni);
+    if (l == 0) {
+        red[wv][0] = static_cast<int32_t>(nu);
+        red[wv][1] = static_cast<int32_t>(ni);
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const int i = l & (kSetThreads / kW - 1);
+        const uint32_t su = wave_sum_u32(l < kSetThreads / kW ? static_cast<uint32_t>(red[i][0]) : 0u);
+        const uint32_t si = wave_sum_u32(l < kSetThreads / kW ? static_cast<uint32_t>(red[i][1]) : 0u);
+        if (l == 0) {
+            if (a.group_union) a.group_union[gid] = static_cast<int32_t>(su);
+            if (a.group_inter) a.group_inter[gid] = static_cast<int32_t>(si);
+        }
+    }
 }
 
 // A group's rows are merged into one sorted multiset (rows are sets, so a
@@ -98,8 +259,6 @@ __global__ __launch_bounds__(kDiagWaves * kW) void k_row_overlap(StatsArgs a)
 // (a multiple of the per-thread segment) and to a power-of-two count P,
 // are merged pairwise in LDS, log2 P levels, each output segment found by a
 // merge-path search (equal values: the left run first).
-constexpr int kSetThreads = 512;
-constexpr int kSeg = kGroupMax / kSetThreads;  // outputs per thread per level (32)
 constexpr int32_t kSentinel = 0x7FFFFFFF;
 
 __global__ __launch_bounds__(kSetThreads) void k_group_sets(StatsArgs a)
@@ -107,6 +266,8 @@ __global__ __launch_bounds__(kSetThreads) void k_group_sets(StatsArgs a)
     __shared__ int32_t buf[2][kGroupMax];
     __shared__ int32_t cnt[2];
     const int64_t gid = blockIdx.x;
+    // only the groups k_group_bits left (uniform)
+    if ((a.group_union ? a.group_union[gid] : a.group_inter[gid]) != kNotHere) return;
     const int64_t b = gid / a.G, m = gid - b * a.G;
     const int64_t t0 = m * a.g;
     const int gm = static_cast<int>((t0 + a.g < a.Lq ? t0 + a.g : a.Lq) - t0);
@@ -188,8 +349,9 @@ __device__ __forceinline__ uint32_t okey(float f)
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-    for (int o = kW / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return __int_as_float(wave_reduce(__float_as_int(v), 0, [](int32_t x, int32_t y) {
+        return __float_as_int(__int_as_float(x) + __int_as_float(y));
+    }));
 }
 
 template <int NV>
@@ -235,20 +397,31 @@ __global__ __launch_bounds__(kDiagWaves * kW) void k_row_mass(StatsArgs a)
     // floor(f k) for f = 1/4, 1/2, 3/4 (exact integer arithmetic)
     const int jsel[3] = {a.k / 4, a.k / 2, 3 * a.k / 4};
     // the jsel-th largest key of each: the largest T with #{key >= T} >= jsel;
-    // the three searches share each pass over the keys
-    uint32_t T[3] = {0u, 0u, 0u};
-    for (int bit = 31; bit >= 0; --bit) {
+    // the three searches share each pass over the keys, which starts below
+    // the leading bits every valid key shares (each answer is a valid key)
+    uint32_t kand = ~0u, kor = 0u;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        kand &= kv[i] != 0u ? kv[i] : ~0u;
+        kor |= kv[i];
+    }
+    kand = wave_and_u32(kand);
+    kor = wave_or_u32(kor);
+    const uint32_t diff = kand ^ kor;
+    const int topbit = diff == 0u ? -1 : 31 - __builtin_clz(diff);
+    const uint32_t shared = topbit < 0 ? kand : (topbit == 31 ? 0u : (kand & ~((2u << topbit) - 1u)));
+    uint32_t T[3] = {shared, shared, shared};
+    for (int bit = topbit; bit >= 0; --bit) {
         const uint32_t x0 = T[0] | (1u << bit), x1 = T[1] | (1u << bit), x2 = T[2] | (1u << bit);
-        // per-lane counts, packed 3 x 10 bits (<= NV <= 64 each), then one
-        // butterfly sum over the wave (totals <= 4096 fit 13 bits: widen first)
+        // per-lane counts, packed 3 x 10 bits (<= NV <= 64 each), summed over
+        // the wave as two 16-bit pairs and one word (totals <= 4096)
         uint32_t c = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             c += (kv[i] >= x0 ? 1u : 0u) | (kv[i] >= x1 ? 1u << 10 : 0u) | (kv[i] >= x2 ? 1u << 20 : 0u);
-        uint64_t cw = (c & 0x3FFu) | (uint64_t((c >> 10) & 0x3FFu) << 21) | (uint64_t(c >> 20) << 42);
-        for (int o = kW / 2; o > 0; o >>= 1) cw += __shfl_xor(cw, o);
-        const int c0 = static_cast<int>(cw & 0x1FFFFF), c1 = static_cast<int>((cw >> 21) & 0x1FFFFF),
-                  c2 = static_cast<int>(cw >> 42);
+        const uint32_t s01 = wave_sum_u32((c & 0x3FFu) | (((c >> 10) & 0x3FFu) << 16));
+        const int c0 = static_cast<int>(s01 & 0xFFFFu), c1 = static_cast<int>(s01 >> 16),
+                  c2 = static_cast<int>(wave_sum_u32(c >> 20));
         T[0] = c0 >= jsel[0] ? x0 : T[0];
         T[1] = c1 >= jsel[1] ? x1 : T[1];
         T[2] = c2 >= jsel[2] ? x2 : T[2];
@@ -280,17 +453,23 @@ hipError_t launch_stats(const StatsArgs &a, hipStream_t st)
     const dim3 block(kDiagWaves * kW);
     const dim3 rgrid(static_cast<uint32_t>((rows + kDiagWaves - 1) / kDiagWaves));
     if (a.overlap) {
-        const size_t lds = static_cast<size_t>(kDiagWaves) * a.k * sizeof(int32_t);
         if (a.k <= 1024)
-            hipLaunchKernelGGL(k_row_overlap<16>, rgrid, block, lds, st, a);
+            hipLaunchKernelGGL(k_row_overlap<16>, rgrid, block, 0, st, a);
+        else if (a.k <= 2048)
+            hipLaunchKernelGGL(k_row_overlap<32>, rgrid, block, 0, st, a);
         else
-            hipLaunchKernelGGL(k_row_overlap<64>, rgrid, block, lds, st, a);
+            hipLaunchKernelGGL(k_row_overlap<64>, rgrid, block, 0, st, a);
     }
-    if (a.group_union || a.group_inter)
-        hipLaunchKernelGGL(k_group_sets, dim3(static_cast<uint32_t>(a.B * a.G)), dim3(kSetThreads), 0, st, a);
+    if (a.group_union || a.group_inter) {
+        const dim3 ggrid(static_cast<uint32_t>(a.B * a.G));
+        hipLaunchKernelGGL(k_group_bits, ggrid, dim3(kSetThreads), 0, st, a);
+        hipLaunchKernelGGL(k_group_sets, ggrid, dim3(kSetThreads), 0, st, a);
+    }
     if (a.mass) {
         if (a.k <= 1024)
             hipLaunchKernelGGL(k_row_mass<16>, rgrid, block, 0, st, a);
+        else if (a.k <= 2048)
+            hipLaunchKernelGGL(k_row_mass<32>, rgrid, block, 0, st, a);
         else
             hipLaunchKernelGGL(k_row_mass<64>, rgrid, block, 0, st, a);
     }

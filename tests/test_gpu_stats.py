@@ -84,3 +84,37 @@ def test_stats_on_gaussian_refine_rows():
     torch.cuda.synchronize()
     idx, sc = i.cpu().numpy(), s.cpu().numpy()
     _check(idx, np.where(idx >= 0, sc, 0.0).astype(np.float32), g)
+
+
+@pytest.mark.parametrize("span", [1 << 16, 1 << 17, (1 << 17) + 1, 1 << 24])
+def test_stats_positions_around_the_bitmap_limit(span):
+    """Rows and groups whose positions stay below 2^17 take the bitmap kernels,
+    the others the sorted-array search and the merge kernel; a call mixes
+    both, and some rows hold position span - 1 (2^17 itself for the third
+    case: the first value past the bitmaps)."""
+    k, g = 512, 8
+    B, Lq = 2, 3 * g + 5
+    r = np.random.default_rng(span % 1009)
+    idx = np.full((B, Lq, k), -1, dtype=np.int32)
+    sc = np.zeros((B, Lq, k), dtype=np.float32)
+    for b in range(B):
+        for t in range(Lq):
+            hi = span if (t // g) % 2 == 0 else min(span, 1 << 12)  # alternate groups: wide, narrow
+            n = int(r.integers(1, k + 1)) if t % 4 else k
+            pos = r.choice(hi, size=n, replace=False)
+            if t % 3 == 0:
+                pos[0] = hi - 1
+            pos = np.unique(pos).astype(np.int32)
+            idx[b, t, :pos.size] = pos
+            sc[b, t, :pos.size] = r.random(pos.size).astype(np.float32)
+    # neighbouring rows share about half their entries, so overlaps are not all zero
+    idx[:, 1::2] = np.where(r.random(idx[:, 1::2].shape) < 0.5, idx[:, 0:-1:2][:, : idx[:, 1::2].shape[1]], idx[:, 1::2])
+    for b in range(B):
+        for t in range(Lq):
+            row = idx[b, t]
+            v = np.unique(row[row >= 0])
+            idx[b, t] = -1
+            idx[b, t, :v.size] = v
+            sc[b, t, v.size:] = 0.0
+    _check(idx, sc, g, 1)
+    _check(idx, sc, g, 3)
