@@ -58,6 +58,18 @@ __device__ __forceinline__ int32_t wave_reduce(int32_t v, int32_t fill, Op op)
     return __builtin_amdgcn_readlane(v, kW - 1);
 }
 
+// Inclusive prefix sum over the lanes (every lane's own result).
+__device__ __forceinline__ int32_t wave_reduce_scan(int32_t v)
+{
+    v += dpp_move<0x111>(v, 0);
+    v += dpp_move<0x112>(v, 0);
+    v += dpp_move<0x114>(v, 0);
+    v += dpp_move<0x118>(v, 0);
+    v += dpp_move<0x142, 0xA>(v, 0);
+    v += dpp_move<0x143, 0xC>(v, 0);
+    return v;
+}
+
 __device__ __forceinline__ int32_t wave_min_i32(int32_t v)
 {
     return wave_reduce(v, INT32_MAX, [](int32_t x, int32_t y) { return x < y ? x : y; });
@@ -411,7 +423,114 @@ __global__ __launch_bounds__(kDiagWaves * kW) void k_row_mass(StatsArgs a)
     const int topbit = diff == 0u ? -1 : 31 - __builtin_clz(diff);
     const uint32_t shared = topbit < 0 ? kand : (topbit == 31 ? 0u : (kand & ~((2u << topbit) - 1u)));
     uint32_t T[3] = {shared, shared, shared};
-    for (int bit = topbit; bit >= 0; --bit) {
+    // One pass of the 8 bits below the shared ones into 256 bins (LDS) gives
+    // each search its bin, and with it 8 more bits of T; the bisection then
+    // covers the bits below the bin only: over the bins' own keys, compacted
+    // to LDS, when each of the three bins holds at most kMassSmall keys, else
+    // over all keys.
+    constexpr int kMassSmall = 2 * kW;
+    int lowbit = topbit;
+    bool small = false;
+    uint32_t need[3] = {0u, 0u, 0u};  // small path: the rank sought within each bin
+    uint32_t sv[3][kMassSmall / kW];  // small path: each bin's keys, 0 = empty
+    if (topbit >= 0) {
+        __shared__ uint32_t hist_all[kDiagWaves][256];
+        uint32_t *hist = hist_all[wv];
+        const int shift = topbit >= 7 ? topbit - 7 : 0;
+        for (int j = l; j < 256; j += kW) hist[j] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (kv[i] != 0u) atomicAdd(&hist[(kv[i] >> shift) & 0xFFu], 1u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l holds bins 4l .. 4l + 3; counts of the keys in higher bins
+        const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+        const uint32_t tot = c0 + c1 + c2 + c3;
+        const uint32_t incl = static_cast<uint32_t>(
+            wave_reduce_scan(static_cast<int32_t>(tot)));  // inclusive prefix over lanes
+        const uint32_t all = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int32_t>(incl), kW - 1));
+        const uint32_t above_lane = all - incl;  // keys in the bins of higher lanes
+#pragma unroll
+        for (int f = 0; f < 3; ++f) {
+            const uint32_t j = static_cast<uint32_t>(jsel[f]);
+            if (jsel[f] == 0 || jsel[f] >= n) continue;  // uniform; T unused
+            const bool here = above_lane < j && j <= above_lane + tot;
+            const int src = __ffsll(static_cast<long long>(__ballot(here))) - 1;
+            uint32_t dig = 0;
+            if (here) {
+                uint32_t cum = above_lane;
+                if (cum + c3 >= j) {
+                    dig = 4 * l + 3;
+                } else if ((cum += c3) + c2 >= j) {
+                    dig = 4 * l + 2;
+                } else if ((cum += c2) + c1 >= j) {
+                    dig = 4 * l + 1;
+                } else {
+                    dig = 4 * l;
+                }
+            }
+            dig = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int32_t>(dig), src));
+            T[f] = (T[f] & ~(0xFFu << shift)) | (dig << shift);
+        }
+        lowbit = shift - 1;
+        // whether every searched bin is small
+        bool fits = lowbit >= 0;
+#pragma unroll
+        for (int f = 0; f < 3; ++f) {
+            if (jsel[f] == 0 || jsel[f] >= n) continue;
+            fits = fits && hist[(T[f] >> shift) & 0xFFu] <= static_cast<uint32_t>(kMassSmall);
+        }
+        if (fits) {
+            small = true;
+            // compact each bin's keys into LDS, then into registers
+            __shared__ uint32_t lists[kDiagWaves][3][kMassSmall];
+#pragma unroll
+            for (int f = 0; f < 3; ++f) {
+                if (jsel[f] == 0 || jsel[f] >= n) continue;
+                const uint32_t lo = T[f], hi = T[f] | ((1u << shift) - 1u);  // the bin's keys
+                int base = 0;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const bool in = kv[i] >= lo && kv[i] <= hi;
+                    const uint64_t bm = __ballot(in);
+                    if (in) lists[wv][f][base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bm >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bm), 0u))] = kv[i];
+                    base += popc64(bm);
+                }
+                // the rank sought within the bin: jsel minus the keys above it
+                int above = 0;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) above += popc64(__ballot(kv[i] > hi));
+                need[f] = static_cast<uint32_t>(jsel[f] - above);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int q = 0; q < kMassSmall / kW; ++q) sv[f][q] = kW * q + l < base ? lists[wv][f][kW * q + l] : 0u;
+            }
+        }
+    }
+    if (small) {
+        // each search over its bin's keys alone: the largest T with
+        // #{bin key >= T} >= the rank left
+#pragma unroll
+        for (int f = 0; f < 3; ++f) {
+            if (jsel[f] == 0 || jsel[f] >= n) continue;
+            for (int bit = lowbit; bit >= 0; --bit) {
+                const uint32_t x = T[f] | (1u << bit);
+                int c = 0;
+#pragma unroll
+                for (int q = 0; q < kMassSmall / kW; ++q) c += popc64(__ballot(sv[f][q] >= x));
+                T[f] = c >= static_cast<int>(need[f]) ? x : T[f];
+            }
+        }
+        lowbit = -1;  // done
+    }
+    for (int bit = lowbit; bit >= 0; --bit) {
         const uint32_t x0 = T[0] | (1u << bit), x1 = T[1] | (1u << bit), x2 = T[2] | (1u << bit);
         // per-lane counts, packed 3 x 10 bits (<= NV <= 64 each), summed over
         // the wave as two 16-bit pairs and one word (totals <= 4096)

@@ -118,3 +118,21 @@ def test_stats_positions_around_the_bitmap_limit(span):
             sc[b, t, v.size:] = 0.0
     _check(idx, sc, g, 1)
     _check(idx, sc, g, 3)
+
+
+def test_mass_with_crowded_and_sparse_bins():
+    """Score mass where the bin of a sought rank holds many equal keys (the
+    search falls back to all keys) next to rows whose bins are small (the
+    search runs over the compacted bin)."""
+    k, g = 2048, 8
+    B, Lq = 1, 16
+    r = np.random.default_rng(77)
+    idx = np.tile(np.arange(k, dtype=np.int32), (B, Lq, 1))
+    sc = np.zeros((B, Lq, k), dtype=np.float32)
+    for t in range(Lq):
+        if t % 2 == 0:  # crowded: most scores equal, a few far above
+            sc[0, t] = 1.0
+            sc[0, t, r.choice(k, size=40, replace=False)] = 100.0 + r.random(40).astype(np.float32)
+        else:           # spread: log-uniform over six decades
+            sc[0, t] = np.exp(r.uniform(-7, 7, size=k)).astype(np.float32)
+    _check(idx, sc, g, 1)
