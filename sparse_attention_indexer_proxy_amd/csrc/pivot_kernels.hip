@@ -2395,6 +2395,18 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
     const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
     // this workgroup's tiles of C: [tile_lo, tile_hi)
     const int ntiles_all = (nc + NT - 1) / NT;
+    if (ntiles_all == 0) {
+        // an empty C (every member precedes its sequence's keys): each
+        // member row still gets its causal count (0) or its -1 padding
+        if (split == 0) {
+            for (int mi = wv; mi < gm; mi += nwaves) {
+                const int64_t r = r0 + mi;
+                if (a.row_nvalid && l == 0) a.row_nvalid[b * geo.Lq + r] = 0;
+                if (a.finish) finish_member(a, b, r, C, a.scratch + (gid * geo.g + mi) * a.c, 0, hist[wv]);
+            }
+        }
+        return;  // uniform over the workgroup
+    }
     const int per_split = (ntiles_all + a.splits - 1) / a.splits;
     const int tile_lo = split * per_split;
     const int tile_hi = tile_lo + per_split < ntiles_all ? tile_lo + per_split : ntiles_all;

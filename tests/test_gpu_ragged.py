@@ -145,3 +145,71 @@ def test_lengths_below_the_query_count_select_nothing_for_early_rows():
     ref = oracle.dense(q[:1, 3:], w[:1, 3:], k[:1, :5], topk)["indices"]
     np.testing.assert_array_equal(got[0, 3:], ref[0])
     np.testing.assert_array_equal(got[1], oracle.dense(q[1:], w[1:], k[1:], topk)["indices"][0])
+
+
+def test_out_of_range_page_entries_read_the_clamped_page():
+    """Table entries outside the pool are clamped into it (first or last
+    page), so a malformed table cannot address outside the storage; the
+    oracle runs on the keys those clamped pages hold."""
+    B, Lq, Lk, g, topk, c, page = 3, 4, 700, 4, 16, 32, 64
+    q, w, k = exact_random(51, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([700, 513, 290], dtype=np.int32)
+    pool, table = _paged(k, page, 51)
+    table = table.copy()
+    table[0, 2] = -7
+    table[1, 5] = pool.shape[0] + 5
+    table[2, 0] = -1
+    clamped = np.clip(table, 0, pool.shape[0] - 1)
+    kl = np.zeros_like(k)
+    for b in range(B):
+        for s in range(Lk):
+            kl[b, s] = pool[clamped[b, s // page], s % page]
+    for variant, v in (("refine", pv.REFINE), ("dense", pv.DENSE)):
+        i, s = pv.index_kv(_dev(q), _dev(w), _dev(pool), torch.from_numpy(lens).cuda(), torch.from_numpy(table).cuda(),
+                           page_size=page, lk=Lk, return_scores=True, variant=v, g=g, topk=topk, c=c)
+        torch.cuda.synchronize()
+        ref_i, ref_s = _oracle_ragged(variant, q, w, kl, lens, g, topk, c)
+        np.testing.assert_array_equal(i.cpu().numpy(), ref_i)
+        np.testing.assert_array_equal(s.cpu().numpy(), ref_s)
+
+
+def test_lengths_outside_the_capacity_are_clamped():
+    """seq_lens above Lk act as Lk and negative ones as 0 (no keys: every row
+    of that sequence is empty)."""
+    B, Lq, Lk, g, topk, c = 3, 4, 400, 4, 16, 32
+    q, w, k = exact_random(52, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([Lk + 100, -3, 250], dtype=np.int32)
+    i, s = pv.index_kv(_dev(q), _dev(w), _dev(k), torch.from_numpy(lens).cuda(), return_scores=True,
+                       variant=pv.REFINE, g=g, topk=topk, c=c)
+    torch.cuda.synchronize()
+    got_i, got_s = i.cpu().numpy(), s.cpu().numpy()
+    assert np.all(got_i[1] == -1) and np.all(np.isneginf(got_s[1]))
+    for b, n in ((0, Lk), (2, 250)):
+        ref_i, ref_s = _oracle_ragged("refine", q[b:b + 1], w[b:b + 1], k[b:b + 1], np.array([n]), g, topk, c)
+        np.testing.assert_array_equal(got_i[b], ref_i[0])
+        np.testing.assert_array_equal(got_s[b], ref_s[0])
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_groups_before_their_sequence_start_are_empty(path, monkeypatch):
+    """A sequence shorter than the query block: whole groups sit before its
+    first key (empty candidate sets; the member rows are all -1), the rest
+    equal the oracle's prefill on that sequence. Lq - len is a multiple of g,
+    so the groups that see keys form a prefill problem of their own."""
+    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if path == "fused" else str(1 << 40))
+    B, Lq, Lk, g, topk, c = 2, 1100, 1100, 4, 16, 32
+    q, w, k = exact_random(53, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([1100, 300], dtype=np.int32)
+    r0 = Lq - 300
+    for variant, v in (("refine", pv.REFINE), ("reuse", pv.REUSE)):
+        i, s = pv.index_kv(_dev(q), _dev(w), _dev(k), torch.from_numpy(lens).cuda(), return_scores=True,
+                           variant=v, g=g, topk=topk, c=c)
+        torch.cuda.synchronize()
+        got_i, got_s = i.cpu().numpy(), s.cpu().numpy()
+        assert np.all(got_i[1, :r0] == -1) and np.all(np.isneginf(got_s[1, :r0]))
+        ref_i, ref_s = _oracle_ragged(variant, q[1:, r0:], w[1:, r0:], k[1:, :300], np.array([300]), g, topk, c)
+        np.testing.assert_array_equal(got_i[1, r0:], ref_i[0])
+        np.testing.assert_array_equal(got_s[1, r0:], ref_s[0])
+        ref_i, ref_s = _oracle_ragged(variant, q[:1], w[:1], k[:1], np.array([Lk]), g, topk, c)
+        np.testing.assert_array_equal(got_i[0], ref_i[0])
+        np.testing.assert_array_equal(got_s[0], ref_s[0])
