@@ -213,3 +213,33 @@ def test_groups_before_their_sequence_start_are_empty(path, monkeypatch):
         ref_i, ref_s = _oracle_ragged(variant, q[:1], w[:1], k[:1], np.array([Lk]), g, topk, c)
         np.testing.assert_array_equal(got_i[0], ref_i[0])
         np.testing.assert_array_equal(got_s[0], ref_s[0])
+
+
+@pytest.mark.parametrize("agg,causal", [("first", False), ("last", False), ("mean", True)])
+@pytest.mark.parametrize("page", [0, 64])
+def test_ragged_aggregation_and_member_causal_reuse(agg, causal, page):
+    """The first / last-member proxies and member-causal Reuse over ragged
+    (and paged) keys, against the oracle run sequence by sequence."""
+    B, Lq, Lk, g, topk, c = 3, 8, 900, 4, 24, 48
+    q, w, k = exact_random(54, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([900, 611, 97], dtype=np.int32)
+    variant = "reuse" if causal else "refine"
+    cfg = pv.make_config(variant=pv.REUSE if causal else pv.REFINE, g=g, topk=topk, c=c, aggregation=agg,
+                         member_causal=causal)
+    tl = torch.from_numpy(lens).cuda()
+    if page:
+        pool, table = _paged(k, page, 54)
+        i, s = pv.index_kv(_dev(q), _dev(w), _dev(pool), tl, torch.from_numpy(table).cuda(), page_size=page, lk=Lk,
+                           cfg=cfg, return_scores=True)
+    else:
+        i, s = pv.index_kv(_dev(q), _dev(w), _dev(k), tl, cfg=cfg, return_scores=True)
+    torch.cuda.synchronize()
+    got_i, got_s = i.cpu().numpy(), s.cpu().numpy()
+    for b in range(B):
+        qb, wb, kb = q[b:b + 1], w[b:b + 1], k[b:b + 1, :lens[b]]
+        if causal:
+            r = oracle.reuse(qb, wb, kb, g, topk, agg=agg, member_causal=True)
+        else:
+            r = oracle.refine(qb, wb, kb, g, topk, c, agg=agg)
+        np.testing.assert_array_equal(got_i[b], r["indices"][0], err_msg=f"{variant} {agg} b={b}")
+        np.testing.assert_array_equal(got_s[b], r["scores"][0], err_msg=f"{variant} {agg} b={b}")
