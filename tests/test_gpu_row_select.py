@@ -44,8 +44,8 @@ def _check_refine_and_reuse(q, w, k, g, topk, c):
 
 
 # name, B, Lk, c, topk: member rows in registers (c <= 4096) or streamed
-# (c > 4096); group rows selected in registers (prefix <= 16384) or through
-# the sampled prefilter (prefix > 4c)
+# (c > 4096); group rows selected in registers (prefix <= 16384), through
+# the sampled prefilter (prefix > 4c, 3c <= 12288) or streamed (the rest)
 CASES = [
     ("c4095_regs", 2, 9000, 4095, 1000),
     ("c4096_regs", 2, 9000, 4096, 2048),
@@ -53,6 +53,8 @@ CASES = [
     ("c5000_streamed", 1, 12000, 5000, 3000),
     ("prefilter_c4096", 2, 20000, 4096, 2048),
     ("prefilter_c1024", 2, 30000, 1024, 256),
+    ("streamed_row_c5000", 1, 20000, 5000, 2048),  # no prefilter (3c > LDS), row > 16384: streamed select
+    ("k1_c1", 2, 3000, 1, 1),
 ]
 
 
