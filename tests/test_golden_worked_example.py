@@ -1,0 +1,237 @@
+"""The hand-worked example in tests/golden/hand_worked_L6_H2_g2.txt.
+
+Every expected value there was derived by hand from eqs. (1) and (4)-(9) of
+the PIVOT paper summary page (picx.dev) and the aggregation ablation on the
+same page; the file shows the arithmetic beside each block. The CPU tests pin
+the oracle to it (in f32 and bf16 storage); the GPU tests run the library on
+the same example, embedded in wider shapes by zero padding (extra dims of q
+and k are 0, extra heads have q = 0 and w = 0, which adds nothing to any
+score), once on the exact-order kernels and once on the MFMA shape
+(H = 64, d = 128, bf16).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import diagnostics
+from tests.test_oracle_exact_and_mutations import _SRC, MUTATIONS
+from workloads import BF16, F32, to_storage
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked_L6_H2_g2.txt")
+L, H, D, G_SIZE, K = 6, 2, 2, 2, 2
+
+
+def _value(tok: str) -> float:
+    if tok in ("-inf", "inf"):
+        return float(tok)
+    return float(Fraction(tok))
+
+
+def load_golden(path: str = GOLDEN) -> dict:
+    """name -> list of rows (each a float64 array)."""
+    rows: dict = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            name, *vals = line.split()
+            rows.setdefault(name, []).append(np.array([_value(v) for v in vals], dtype=np.float64))
+    return rows
+
+
+@pytest.fixture(scope="module")
+def gold():
+    return load_golden()
+
+
+def _matrix(gold, name, width=None):
+    rows = gold[name]
+    width = width or max(len(r) for r in rows)
+    out = np.full((len(rows), width), np.nan)
+    for i, r in enumerate(rows):
+        out[i, :len(r)] = r
+    return out
+
+
+def _inputs(gold):
+    k = gold["k"][0].reshape(L, D)
+    q = np.stack(gold["q"]).reshape(L, H, D)
+    w = np.stack(gold["w"]).reshape(L, H)
+    return q, w, k
+
+
+def _storage(gold, dtype):
+    q, w, k = _inputs(gold)
+    return (to_storage(q[None], dtype), w[None].astype(np.float32), to_storage(k[None], dtype))
+
+
+def _idx(gold, name):
+    return _matrix(gold, name).astype(np.int32)
+
+
+def _check_rows(idx, sc, gold, name):
+    np.testing.assert_array_equal(np.asarray(idx).reshape(L, -1), _idx(gold, name + ".idx"), err_msg=name)
+    np.testing.assert_array_equal(np.asarray(sc).reshape(L, -1).astype(np.float64), _matrix(gold, name + ".sc"),
+                                  err_msg=name)
+
+
+def test_golden_inputs_are_exact_in_bf16(gold):
+    q, w, k = _inputs(gold)
+    for x in (q, k):
+        bits = to_storage(x, BF16)
+        back = (bits.astype(np.uint32) << 16).view(np.float32)
+        np.testing.assert_array_equal(back.astype(np.float64), x)
+    np.testing.assert_array_equal(w.astype(np.float32).astype(np.float64), w)
+
+
+def _check_oracle(gold, dtype, lib=None):
+    q, w, k = _storage(gold, dtype)
+    kw = {"lib_path": lib}
+
+    r = oracle.dense(q, w, k, L, **kw)
+    full = _matrix(gold, "dense_all.sc", L)
+    for t in range(L):
+        np.testing.assert_array_equal(r["indices"][0, t, :t + 1], np.arange(t + 1))
+        np.testing.assert_array_equal(r["indices"][0, t, t + 1:], -1)
+        np.testing.assert_array_equal(r["scores"][0, t, :t + 1], full[t, :t + 1])
+    assert r["counters"][2] == gold["cost.dense"][0][0]
+
+    r = oracle.dense(q, w, k, K, **kw)
+    _check_rows(r["indices"], r["scores"], gold, "dense_k2")
+
+    qbar, wbar = oracle.pool(q, w, G_SIZE, **kw)
+    np.testing.assert_array_equal(qbar[0].reshape(3, -1), _matrix(gold, "qbar"))
+    np.testing.assert_array_equal(wbar[0], _matrix(gold, "wbar"))
+    for m in range(3):
+        np.testing.assert_array_equal(oracle.proxy_row(q, w, k, G_SIZE, 0, m, **kw), gold["proxy.sc"][m])
+
+    r = oracle.reuse(q, w, k, G_SIZE, K, **kw)
+    _check_rows(r["indices"], r["scores"], gold, "reuse_k2")
+    assert r["counters"][0] == gold["cost.proxy"][0][0]
+    r = oracle.reuse(q, w, k, G_SIZE, K, member_causal=True, **kw)
+    _check_rows(r["indices"], r["scores"], gold, "reuse_causal_k2")
+    for agg in ("first", "last"):
+        r = oracle.reuse(q, w, k, G_SIZE, K, agg=agg, **kw)
+        _check_rows(r["indices"], r["scores"], gold, f"reuse_{agg}_k2")
+
+    for c in (3, 2):
+        r = oracle.refine(q, w, k, G_SIZE, K, c, **kw)
+        _check_rows(r["indices"], r["scores"], gold, f"refine_c{c}")
+        np.testing.assert_array_equal(r["cand"][0], _idx(gold, f"refine_c{c}.cand"))
+        np.testing.assert_array_equal(r["cand_n"][0], gold[f"refine_c{c}.cand_n"][0].astype(np.int32))
+        assert r["counters"][1] == gold[f"cost.refine_c{c}"][0][0]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_oracle_reproduces_the_worked_example(gold, dtype):
+    _check_oracle(gold, dtype)
+
+
+# Planted mistakes of the oracle (the same source edits as the pin battery's)
+# that the worked example must expose on its own. Two are out of its reach:
+# it has no short last group, and its proxies need no bf16 rounding.
+HAND_CATCHES = sorted(set(MUTATIONS) - {"short_group_divides_by_g", "proxy_not_rounded_to_bf16"})
+
+
+@pytest.mark.parametrize("name", HAND_CATCHES)
+def test_worked_example_exposes_planted_mistake(gold, name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(_SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / f"mut_{name}.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, str(path), "-o", lib, "-lm"], check=True)
+    with pytest.raises(AssertionError):
+        _check_oracle(gold, BF16, lib)
+
+
+def test_oracle_diagnostics_reproduce_the_worked_example(gold):
+    idx = _idx(gold, "dense_k2.idx")[None]
+    sc = _matrix(gold, "dense_k2.sc")[None]
+    np.testing.assert_array_equal(diagnostics.overlap(idx, 1)[0], gold["stats.overlap_d1"][0])
+    union, inter = diagnostics.group_sets(idx, G_SIZE)
+    np.testing.assert_array_equal(union[0], gold["stats.union_g2"][0])
+    np.testing.assert_array_equal(inter[0], gold["stats.inter_g2"][0])
+    np.testing.assert_array_equal(diagnostics.mass(idx, sc)[0], _matrix(gold, "stats.mass"))
+
+
+# ------------------------------------------------------------------ GPU
+
+def _padded(gold, dtype, heads, dim):
+    """The example with dims zero-padded to ``dim`` and extra heads silent."""
+    q, w, k = _inputs(gold)
+    qp = np.zeros((1, L, heads, dim))
+    qp[0, :, :H, :D] = q
+    wp = np.zeros((1, L, heads))
+    wp[0, :, :H] = w
+    kp = np.zeros((1, L, dim))
+    kp[0, :, :D] = k
+    return to_storage(qp, dtype), wp.astype(np.float32), to_storage(kp, dtype)
+
+
+GPU_SHAPES = [(F32, 2, 4), (BF16, 2, 8), (BF16, 64, 128)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", GPU_SHAPES, ids=[f"{s[0]}_H{s[1]}_d{s[2]}" for s in GPU_SHAPES])
+def test_library_reproduces_the_worked_example(gold, shape, pivot_lib):
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_proxy_amd as pv
+    from tests.parity import to_device
+
+    dtype, heads, dim = shape
+    tq, tw, tk = to_device(*_padded(gold, dtype, heads, dim))
+    host = lambda t: t.cpu().numpy()  # noqa: E731
+
+    i, s = pv.index_dense(tq, tw, tk, L, return_scores=True)
+    i, s = host(i)[0], host(s)[0]
+    full = _matrix(gold, "dense_all.sc", L)
+    for t in range(L):
+        np.testing.assert_array_equal(i[t, :t + 1], np.arange(t + 1))
+        np.testing.assert_array_equal(i[t, t + 1:], -1)
+        np.testing.assert_array_equal(s[t, :t + 1], full[t, :t + 1])
+
+    i, s = pv.index_dense(tq, tw, tk, K, return_scores=True)
+    _check_rows(host(i), host(s), gold, "dense_k2")
+
+    qbar, wbar = pv.pool(tq, tw, G_SIZE)
+    qbar = host(qbar.float())[0]
+    np.testing.assert_array_equal(qbar[:, :H, :D].reshape(3, -1), _matrix(gold, "qbar"))
+    assert not qbar[:, H:].any() and not qbar[:, :, D:].any()
+    np.testing.assert_array_equal(host(wbar)[0][:, :H], _matrix(gold, "wbar"))
+    rows = host(pv.proxy_scores(*pv.pool(tq, tw, G_SIZE), tk, G_SIZE, L))[0]
+    for m in range(3):
+        n = len(gold["proxy.sc"][m])
+        np.testing.assert_array_equal(rows[m, :n], gold["proxy.sc"][m])
+        assert np.all(np.isneginf(rows[m, n:]))
+
+    i, s = pv.index_reuse(tq, tw, tk, G_SIZE, K, return_scores=True)
+    _check_rows(host(i), host(s), gold, "reuse_k2")
+    i, s = pv.index(tq, tw, tk, variant=pv.REUSE, g=G_SIZE, topk=K, member_causal=True, return_scores=True)
+    _check_rows(host(i), host(s), gold, "reuse_causal_k2")
+    for agg in ("first", "last"):
+        i, s = pv.index(tq, tw, tk, variant=pv.REUSE, g=G_SIZE, topk=K, aggregation=agg, return_scores=True)
+        _check_rows(host(i), host(s), gold, f"reuse_{agg}_k2")
+
+    for c in (3, 2):
+        i, s, cand, cand_n = pv.index_refine(tq, tw, tk, G_SIZE, K, c, return_scores=True, return_candidates=True)
+        _check_rows(host(i), host(s), gold, f"refine_c{c}")
+        np.testing.assert_array_equal(host(cand)[0], _idx(gold, f"refine_c{c}.cand"))
+        np.testing.assert_array_equal(host(cand_n)[0], gold[f"refine_c{c}.cand_n"][0].astype(np.int32))
+
+    i, s = pv.index_dense(tq, tw, tk, K, return_scores=True)
+    st = pv.index_stats(i, s, d=1, g=G_SIZE)
+    np.testing.assert_array_equal(host(st["overlap"])[0], gold["stats.overlap_d1"][0])
+    np.testing.assert_array_equal(host(st["union"])[0], gold["stats.union_g2"][0])
+    np.testing.assert_array_equal(host(st["inter"])[0], gold["stats.inter_g2"][0])
+    np.testing.assert_allclose(host(st["mass"])[0], _matrix(gold, "stats.mass"), rtol=1e-6, atol=0)
