@@ -121,6 +121,14 @@ struct Layout {
 // key axis is split over workgroups instead (decode shapes). The environment
 // variable PIVOT_FEW_GROUPS overrides the threshold (0 disables the split
 // path, a huge value forces it); tests use it to cover both paths.
+#ifndef PIVOT_SPLIT_SCAN_WGS
+#define PIVOT_SPLIT_SCAN_WGS 512
+#endif
+// Workgroups of the split scan over all groups: two per CU, the waves of
+// which stay resident for the whole launch (its key streams are one quarter
+// deep per wave, so long-lived waves keep HBM busy).
+constexpr int64_t kSplitScanWorkgroups = PIVOT_SPLIT_SCAN_WGS;
+
 int64_t few_groups_threshold()
 {
     const char *v = getenv("PIVOT_FEW_GROUPS");
@@ -213,9 +221,12 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
     l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
     l.few = pivot::mfma_shape(sh) && (paged || static_cast<int64_t>(groups) < few_groups_threshold());
     if (l.few) {
-        const int64_t tiles = (p->lk + 63) / 64;
-        int64_t ss = (2048 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
-        l.scan_splits = static_cast<int>(ss < tiles ? ss : tiles);
+        // split scan: about kSplitScanWorkgroups workgroups of four waves
+        // over all groups, each wave streaming at least one 64-key quarter
+        const int64_t quarters = (p->lk + 63) / 64;
+        const int64_t most = (quarters + 3) / 4;
+        int64_t ss = (kSplitScanWorkgroups + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
+        l.scan_splits = static_cast<int>(ss < most ? ss : most);
         const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 127) / 128;  // refine tiles of 128
         int64_t rs = (512 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.refine_splits = static_cast<int>(rs < ctiles ? rs : ctiles);
