@@ -144,6 +144,7 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
                                              want_cand=False)}[variant]
     # probe: one thread-batch of mid-sequence units gives the time per unit
     probe = np.linspace(per_seq // 2, per_seq // 2 + threads - 1, threads).astype(np.int64) % per_seq
+    run(probe)  # untimed: thread start-up and first touches would inflate the estimate
     t0 = time.perf_counter()
     run(probe)
     per_unit = max((time.perf_counter() - t0) / len(probe), 1e-6)
