@@ -19,8 +19,9 @@
 //   k_scan_exact<T, Mode>   the same for any shape/dtype, in the exact fp32
 //                           order of the definition (heads, then dims ascending)
 //   k_select_groups<NV>     the final top-K of each group's survivors (eqs. 6-7)
-//   k_scan_split            eq. (5) with the key axis split over workgroups
-//                           (few groups: decode), score rows to HBM
+//   k_scan_split            eq. (5) with the key axis split over many waves
+//                           (few groups: decode), keys streamed from HBM
+//                           straight into MFMA operands, score rows to HBM
 //   k_select_rows           block-wide selects of those rows (eqs. 6-7, 9)
 //   k_refine_mfma           eq. (8) over gathered candidate tiles
 //   k_select_members<NV>    eq. (9): each member's top-k of its re-scored C
@@ -1945,6 +1946,47 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 // repeated key (many exact zeros), which ends the search. emit(slot,
 // position, score) is called for every selected entry, slots dense and
 // ascending; positions are loaded a chunk ahead. Returns the count.
+// The K-th largest key when it lies in a bin [lo, hi] whose n keys are in
+// mid (LDS) and `above` keys exceed the bin: the largest x in [lo, hi] with
+// above + #{bin keys >= x} >= K, plus the keys above it and equal to it
+// (counted over the bin alone), with the bin held R keys per lane.
+struct BinKth {
+    uint32_t kth;
+    int n_gt, n_eq;
+};
+
+template <int R>
+__device__ __forceinline__ BinKth bisect_bin(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above, int K)
+{
+    const int l = lane_id();
+    uint32_t mv[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int j = kWave * q + l;
+        mv[q] = j < n ? mid[j] : 0u;
+    }
+    while (lo < hi) {
+        const uint32_t x = lo + (hi - lo) / 2u + 1u;
+        if (above + count_ge(mv, x) >= K)
+            lo = x;
+        else
+            hi = x - 1u;
+    }
+    BinKth r;
+    r.kth = lo;
+    r.n_gt = above + (lo == 0xFFFFFFFFu ? 0 : count_ge(mv, lo + 1u));
+    r.n_eq = above + count_ge(mv, lo) - r.n_gt;
+    return r;
+}
+
+__device__ __forceinline__ BinKth bisect_bin_any(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above,
+                                                 int K)
+{
+    if (n <= kWave) return bisect_bin<1>(mid, n, lo, hi, above, K);
+    if (n <= 4 * kWave) return bisect_bin<4>(mid, n, lo, hi, above, K);
+    return bisect_bin<kMsMid / kWave>(mid, n, lo, hi, above, K);
+}
+
 template <int NV, class Emit>
 __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rc, int n, int K,
                                               uint32_t *mid, Emit &&emit)
@@ -1968,6 +2010,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
     if (n > K) {
         uint32_t T = 0;
         bool found = false;
+        BinKth bin{};
         {
             // One pass into kHistBins bins of equal width 2^shift over the
             // keys' range [lo, hi] (LDS atomics) finds the bin holding the
@@ -2032,22 +2075,9 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
                     nm += popc(im);
                 }
                 wave_fence();
-                uint32_t mv[kMsMid / kWave];
-#pragma unroll
-                for (int q = 0; q < kMsMid / kWave; ++q) {
-                    const int j = kWave * q + l;
-                    mv[q] = j < nm ? mid[j] : 0u;
-                }
-                // the largest x in [blo, bhi] with abv + #{bin key >= x} >= K
-                uint32_t a_lo = blo, a_hi = bhi;
-                while (a_lo < a_hi) {
-                    const uint32_t x = a_lo + (a_hi - a_lo) / 2u + 1u;
-                    if (static_cast<int>(abv) + count_ge(mv, x) >= K)
-                        a_lo = x;
-                    else
-                        a_hi = x - 1u;
-                }
-                T = a_lo;
+                // counted over as few registers as the bin needs
+                bin = bisect_bin_any(mid, nm, blo, bhi, static_cast<int>(abv), K);
+                T = bin.kth;
                 found = true;
             }
             wave_fence();
@@ -2108,8 +2138,10 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             }
         }
         kth = T;
-        const int n_gt = T == 0xFFFFFFFFu ? 0 : count_ge(kv, T + 1u);
-        const int n_eq = count_ge(kv, T) - n_gt;
+        // found in a bin: every key above the bin exceeds T, every key
+        // below it is less, so the bin's counts are the row's
+        const int n_gt = found ? bin.n_gt : (T == 0xFFFFFFFFu ? 0 : count_ge(kv, T + 1u));
+        const int n_eq = found ? bin.n_eq : count_ge(kv, T) - n_gt;
         quota = K - n_gt;
         ties_all = quota == n_eq;
     }
