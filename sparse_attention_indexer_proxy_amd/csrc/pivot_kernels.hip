@@ -1895,7 +1895,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *p, int 
 constexpr int kMsWaves = 4;     // rows (one per wave) per workgroup
 constexpr int kMsMid = 1024;    // LDS keys per wave for the final bits
 constexpr int kMsChunk = 16;    // slabs of positions loaded at a time
-constexpr int kHistBins = 256;  // value-range bins of the one-pass histogram
+#ifndef PIVOT_HIST_BINS
+#define PIVOT_HIST_BINS 512
+#endif
+constexpr int kHistBins = PIVOT_HIST_BINS;  // value-range bins of the one-pass histogram
+static_assert(kHistBins % kWave == 0, "whole bins per lane");
 
 // Number of keys in kv[] that are >= x (a wave-uniform count).
 template <int N>
@@ -2035,9 +2039,16 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             for (int i = 0; i < NV; ++i)
                 if (kv[i] != 0u) atomicAdd(&hist[(kv[i] - lo) >> shift], 1u);
             wave_fence();
-            // lane l holds bins 4l .. 4l+3; suffix counts run from the top bin
-            const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-            const uint32_t tot = c0 + c1 + c2 + c3;
+            // lane l holds bins BPL l .. BPL l + BPL - 1; suffix counts run
+            // from the top bin
+            constexpr int BPL = kHistBins / kWave;
+            uint32_t cb[BPL];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                cb[j] = hist[BPL * l + j];
+                tot += cb[j];
+            }
             const uint32_t suf = wave_suffix_sum(tot);
             const uint32_t above_lane = suf - tot;
             const bool here = above_lane < static_cast<uint32_t>(K) && static_cast<uint32_t>(K) <= suf;
@@ -2045,18 +2056,19 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             int bb = 0;
             uint32_t abv = 0, cnt = 0;
             if (here) {
+                // the highest of this lane's bins whose count reaches K
                 uint32_t cum = above_lane;
-                if (cum + c3 >= static_cast<uint32_t>(K)) {
-                    bb = 4 * l + 3; cnt = c3;
-                } else if ((cum += c3) + c2 >= static_cast<uint32_t>(K)) {
-                    bb = 4 * l + 2; cnt = c2;
-                } else if ((cum += c2) + c1 >= static_cast<uint32_t>(K)) {
-                    bb = 4 * l + 1; cnt = c1;
-                } else {
-                    cum += c1;
-                    bb = 4 * l; cnt = c0;
+                bool done = false;
+#pragma unroll
+                for (int j = BPL - 1; j >= 0; --j) {
+                    if (!done && cum + cb[j] >= static_cast<uint32_t>(K)) {
+                        bb = BPL * l + j;
+                        cnt = cb[j];
+                        abv = cum;
+                        done = true;
+                    }
+                    if (!done) cum += cb[j];
                 }
-                abv = cum;
             }
             bb = static_cast<int>(lane_value(static_cast<uint32_t>(bb), src));
             abv = lane_value(abv, src);
@@ -2222,10 +2234,15 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
     }
     int32_t *oi = a.out_idx + row * a.topk;
     float *os = a.out_sc ? a.out_sc + row * a.topk : nullptr;
+    // the row's outputs as buffer resources: a store is one offset, not a
+    // 64-bit address computation
+    const __amdgpu_buffer_rsrc_t ri = row_buffer(oi, a.topk), rsc = row_buffer(os, os ? a.topk : 0);
     const int out = wave_topk_emit<NV>(row_buffer(sc, a.c), row_buffer(C, a.c), nvalid, a.topk, mid_all[wv],
                                        [&](int slot, int32_t pos, float v) {
-                                           oi[slot] = pos;
-                                           if (os) os[slot] = v;
+                                           __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(pos), ri,
+                                                                                 slot * 4, 0, 0);
+                                           if (os) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsc,
+                                                                                          slot * 4, 0, 0);
                                        });
     for (int x = out + l; x < a.topk; x += kWave) {
         oi[x] = -1;
@@ -2277,9 +2294,10 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectA
     if (o.to_candidates) {
         int32_t *ci = o.idx + gid * o.stride;
         float *cs = o.sc ? o.sc + gid * o.stride : nullptr;
+        const __amdgpu_buffer_rsrc_t rci = row_buffer(ci, o.stride), rcs = row_buffer(cs, cs ? o.stride : 0);
         const int got = wave_topk_emit<(NV > 0 ? NV : 1)>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
-            ci[slot] = p;
-            if (cs) cs[slot] = v;
+            __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), rci, slot * 4, 0, 0);
+            if (cs) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rcs, slot * 4, 0, 0);
         });
         for (int t = got + l; t < o.stride; t += kWave) {
             ci[t] = -1;
