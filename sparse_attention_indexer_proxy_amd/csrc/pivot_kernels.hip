@@ -1991,7 +1991,11 @@ __device__ __forceinline__ BinKth bisect_bin_any(const uint32_t *mid, int n, uin
     return bisect_bin<kMsMid / kWave>(mid, n, lo, hi, above, K);
 }
 
-template <int NV, class Emit>
+// Slot passed for the entries not selected when the emitter drops
+// out-of-range slots (its stores go through a buffer resource of the row).
+constexpr int kNoSlot = 0x1FFFFFFF;  // times 4 bytes: past any row, still a positive int
+
+template <int NV, bool DROPS = false, class Emit>
 __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rc, int n, int K,
                                               uint32_t *mid, Emit &&emit)
 {
@@ -2022,13 +2026,15 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             // compacted into `mid` and the key is resolved by bisection over
             // the bin's values. A bin too crowded (many equal keys) falls
             // back to the bisection over all keys below.
-            uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+            // the smallest non-empty key: empty (0) wraps to the largest
+            // value under key - 1, so one unsigned min covers both
+            uint32_t lo1 = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                lo = kv[i] != 0u && kv[i] < lo ? kv[i] : lo;
-                hi = kv[i] > hi ? kv[i] : hi;
+                lo1 = min(lo1, kv[i] - 1u);
+                hi = max(hi, kv[i]);
             }
-            lo = wave_min_u32(lo);
+            uint32_t lo = wave_min_u32(lo1) + 1u;
             hi = wave_max_u32(hi);
             int shift = 0;
             while (((hi - lo) >> shift) >= static_cast<uint32_t>(kHistBins)) ++shift;
@@ -2037,7 +2043,9 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             wave_fence();
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                if (kv[i] != 0u) atomicAdd(&hist[(kv[i] - lo) >> shift], 1u);
+                // empty slots count into this lane's spare word past the bins
+                // (no branch around the atomic)
+                atomicAdd(&hist[kv[i] != 0u ? (kv[i] - lo) >> shift : kHistBins + l], 1u);
             wave_fence();
             // lane l holds bins BPL l .. BPL l + BPL - 1; suffix counts run
             // from the top bin
@@ -2083,7 +2091,8 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
                 for (int i = 0; i < NV; ++i) {
                     const bool in = kv[i] >= blo && kv[i] <= bhi;
                     const uint64_t im = ballot(in);
-                    if (in) mid[nm + mbcnt(im)] = kv[i];
+                    // lanes outside the bin write their spare word past the bins
+                    mid[in ? nm + mbcnt(im) : kMsMid + kHistBins + l] = kv[i];
                     nm += popc(im);
                 }
                 wave_fence();
@@ -2186,7 +2195,10 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
                 take = key > kth || (eq && rank < quota);
             }
             const uint64_t tm = ballot(take);
-            if (take) emit(out + mbcnt(tm), cv[e], key_float(key));
+            if constexpr (DROPS)
+                emit(take ? out + mbcnt(tm) : kNoSlot, cv[e], key_float(key));
+            else if (take)
+                emit(out + mbcnt(tm), cv[e], key_float(key));
             out += popc(tm);
         }
         if (i0 + CH < NV) {
@@ -2200,7 +2212,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
 template <int NV>
 __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelectArgs a)
 {
-    __shared__ uint32_t mid_all[kMsWaves][kMsMid + kHistBins];
+    __shared__ uint32_t mid_all[kMsWaves][kMsMid + kHistBins + kWave];
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row addressing
     const int l = threadIdx.x & 63;
@@ -2237,7 +2249,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
     // the row's outputs as buffer resources: a store is one offset, not a
     // 64-bit address computation
     const __amdgpu_buffer_rsrc_t ri = row_buffer(oi, a.topk), rsc = row_buffer(os, os ? a.topk : 0);
-    const int out = wave_topk_emit<NV>(row_buffer(sc, a.c), row_buffer(C, a.c), nvalid, a.topk, mid_all[wv],
+    const int out = wave_topk_emit<NV, true>(row_buffer(sc, a.c), row_buffer(C, a.c), nvalid, a.topk, mid_all[wv],
                                        [&](int slot, int32_t pos, float v) {
                                            __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(pos), ri,
                                                                                  slot * 4, 0, 0);
@@ -2267,7 +2279,7 @@ struct GroupSelectArgs {
 template <int NV>
 __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectArgs a)
 {
-    __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid + kHistBins : 256];
+    __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid + kHistBins + kWave : 256];
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -2295,7 +2307,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectA
         int32_t *ci = o.idx + gid * o.stride;
         float *cs = o.sc ? o.sc + gid * o.stride : nullptr;
         const __amdgpu_buffer_rsrc_t rci = row_buffer(ci, o.stride), rcs = row_buffer(cs, cs ? o.stride : 0);
-        const int got = wave_topk_emit<(NV > 0 ? NV : 1)>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
+        const int got = wave_topk_emit<(NV > 0 ? NV : 1), true>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
             __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), rci, slot * 4, 0, 0);
             if (cs) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rcs, slot * 4, 0, 0);
         });
