@@ -552,15 +552,30 @@ __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const flo
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) {
-        const T *src = q + ((b * geo.Lq + r) * H + h) * D + ch * VEC;
-        union {
-            uint4 v;
-            T e[VEC];
-        } u;
-        u.v = *reinterpret_cast<const uint4 *>(src);
+    // eight member rows are requested before the first is added (a short
+    // batch repeats its last row and skips the repeats); the sum still runs
+    // in member order
+    constexpr int kRows = 8;
+    for (int64_t r = r0; r < r1; r += kRows) {
+        uint4 v[kRows];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + widen<T>(u.e[e]);
+        for (int j = 0; j < kRows; ++j) {
+            const int64_t rr = r + j < r1 ? r + j : r1 - 1;
+            v[j] = *reinterpret_cast<const uint4 *>(q + ((b * geo.Lq + rr) * H + h) * D + ch * VEC);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+            if (r + j < r1) {
+                union {
+                    uint4 v;
+                    T e[VEC];
+                } u;
+                u.v = v[j];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + widen<T>(u.e[e]);
+            }
+        }
     }
     union {
         uint4 v;
