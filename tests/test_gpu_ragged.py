@@ -243,3 +243,21 @@ def test_ragged_aggregation_and_member_causal_reuse(agg, causal, page):
             r = oracle.refine(qb, wb, kb, g, topk, c, agg=agg)
         np.testing.assert_array_equal(got_i[b], r["indices"][0], err_msg=f"{variant} {agg} b={b}")
         np.testing.assert_array_equal(got_s[b], r["scores"][0], err_msg=f"{variant} {agg} b={b}")
+
+
+@pytest.mark.parametrize("variant", ["refine", "reuse"])
+def test_paged_prefill_with_many_groups(variant):
+    """Paged keys always take the split-key scan; with 512+ groups each group
+    gets a single workgroup (four waves sweeping its quarters from a
+    staggered start), the longest case of that kernel's per-wave loop."""
+    B, Lq, Lk, g, topk, c, page = 2, 2000, 2300, 4, 16, 32, 96  # 1000 groups
+    q, w, k = exact_random(57, B, Lq, Lk, 64, 128, BF16)
+    lens = np.array([2300, 2011], dtype=np.int32)
+    pool, table = _paged(k, page, 58)
+    v = {"refine": pv.REFINE, "reuse": pv.REUSE}[variant]
+    i, s = pv.index_kv(_dev(q), _dev(w), _dev(pool), torch.from_numpy(lens).cuda(), torch.from_numpy(table).cuda(),
+                       page_size=page, lk=Lk, return_scores=True, variant=v, g=g, topk=topk, c=c)
+    torch.cuda.synchronize()
+    ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
+    np.testing.assert_array_equal(i.cpu().numpy(), ref_i)
+    np.testing.assert_array_equal(s.cpu().numpy(), ref_s)
