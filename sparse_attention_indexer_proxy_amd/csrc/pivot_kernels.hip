@@ -2010,7 +2010,10 @@ __device__ __forceinline__ BinKth bisect_bin_any(const uint32_t *mid, int n, uin
 // out-of-range slots (its stores go through a buffer resource of the row).
 constexpr int kNoSlot = 0x1FFFFFFF;  // times 4 bytes: past any row, still a positive int
 
-template <int NV, bool DROPS = false, class Emit>
+// SKIP: rows often fill only part of the NV slabs (the scan's survivor
+// buffers), so the passes stop at the last non-empty slab, checked once per
+// kMsChunk slabs; full rows (member scores) leave the checks out.
+template <int NV, bool DROPS = false, bool SKIP = false, class Emit>
 __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rc, int n, int K,
                                               uint32_t *mid, Emit &&emit)
 {
@@ -2046,6 +2049,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             uint32_t lo1 = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
+                if (SKIP && i % kMsChunk == 0 && kWave * i >= n) break;
                 lo1 = min(lo1, kv[i] - 1u);
                 hi = max(hi, kv[i]);
             }
@@ -2057,10 +2061,12 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
             for (int j = l; j < kHistBins; j += kWave) hist[j] = 0u;
             wave_fence();
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
+            for (int i = 0; i < NV; ++i) {
+                if (SKIP && i % kMsChunk == 0 && kWave * i >= n) break;
                 // empty slots count into this lane's spare word past the bins
                 // (no branch around the atomic)
                 atomicAdd(&hist[kv[i] != 0u ? (kv[i] - lo) >> shift : kHistBins + l], 1u);
+            }
             wave_fence();
             // lane l holds bins BPL l .. BPL l + BPL - 1; suffix counts run
             // from the top bin
@@ -2104,6 +2110,7 @@ __device__ __forceinline__ int wave_topk_emit(__amdgpu_buffer_rsrc_t rs, __amdgp
                 int nm = 0;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) {
+                    if (SKIP && i % kMsChunk == 0 && kWave * i >= n) break;
                     const bool in = kv[i] >= blo && kv[i] <= bhi;
                     const uint64_t im = ballot(in);
                     // lanes outside the bin write their spare word past the bins
@@ -2322,7 +2329,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectA
         int32_t *ci = o.idx + gid * o.stride;
         float *cs = o.sc ? o.sc + gid * o.stride : nullptr;
         const __amdgpu_buffer_rsrc_t rci = row_buffer(ci, o.stride), rcs = row_buffer(cs, cs ? o.stride : 0);
-        const int got = wave_topk_emit<(NV > 0 ? NV : 1), true>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
+        const int got = wave_topk_emit<(NV > 0 ? NV : 1), true, true>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
             __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), rci, slot * 4, 0, 0);
             if (cs) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rcs, slot * 4, 0, 0);
         });
@@ -2335,7 +2342,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectA
     }
     const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
     const int64_t stride = o.stride;
-    const int got = wave_topk_emit<(NV > 0 ? NV : 1)>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
+    const int got = wave_topk_emit<(NV > 0 ? NV : 1), false, true>(rs, rp, n, a.K, lds[wv], [&](int slot, int32_t p, float v) {
         for (int64_t r = r0; r < r1; ++r) {
             const int64_t off = (b * geo.Lq + r) * stride + slot;
             o.idx[off] = p;
