@@ -44,10 +44,20 @@
  * then describes it (thread-local). Calls are re-entrant; calls that share a
  * workspace must not overlap on different streams.
  *
- * Fast path: bf16 with heads == 64 and dim == 128 runs on bf16 MFMA with fp32
- * accumulation. Every other shape, and f32 inputs, runs the general kernels,
- * whose scores follow the exact fp32 order of the definition above (heads
- * ascending, dims ascending, one rounding per product and per sum).
+ * Kernels: bf16 with heads == 64 and dim == 128 runs on bf16 MFMA with fp32
+ * accumulation, at any size. Every other shape, and f32 inputs, runs the exact-order kernels:
+ * one lane per key, fp32 in the definition's order (heads ascending, dims
+ * ascending, one rounding per product and per sum), so their results equal
+ * a plain CPU evaluation bit for bit. They are meant for small problems: a
+ * call whose scan and refine need more than 2^36 multiply-adds, estimated
+ * as (batch * G * lk + batch * lq * min(c, lk)) * heads * dim, returns
+ * PIVOT_ERR_UNSUPPORTED instead of running slowly.
+ *
+ * Departure from a score-ordered TopK: rows list positions in ascending
+ * order, not by descending score. T_t is a set in the pages' definitions;
+ * the kernels' selections are stable compactions in position order, and a
+ * sort by score would add a k-entry sort per row that sparse attention does
+ * not need. Callers that want score order sort (scores, indices) per row.
  */
 #ifndef PIVOT_H
 #define PIVOT_H
@@ -59,7 +69,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 5
+#define PIVOT_ABI_VERSION 6
 
 typedef enum {
     PIVOT_OK = 0,
@@ -80,6 +90,20 @@ typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2, PIVOT_AUTO = 
  * section "Ablation Studies"): the per-head mean of eq. (4), or the first or
  * the last member's own q and w taken unchanged. */
 typedef enum { PIVOT_AGG_MEAN = 0, PIVOT_AGG_FIRST = 1, PIVOT_AGG_LAST = 2 } pivot_aggregation;
+
+/* Which proxy-scan kernel family runs on the MFMA shape (bf16, 64 heads,
+ * 128 dims); the results are the same either way:
+ *   PIVOT_PATH_FUSED  one wave per group streams the group's key prefix
+ *                     through LDS tiles shared by 8 groups and keeps only the
+ *                     entries above a running threshold (no score row is
+ *                     written); fills the GPU from 256 groups up;
+ *   PIVOT_PATH_SPLIT  each group's key range is split over many workgroups,
+ *                     which write the group's full score row [lk] to the
+ *                     workspace for a block-wide select (decode: few groups,
+ *                     long prefixes); the workspace grows with groups * lk;
+ *   PIVOT_PATH_AUTO   SPLIT below 256 groups (batch * ceil(lq / g)), else
+ *                     FUSED. */
+typedef enum { PIVOT_PATH_AUTO = 0, PIVOT_PATH_FUSED = 1, PIVOT_PATH_SPLIT = 2 } pivot_scan_path;
 
 /* Default guardrail of PIVOT_AUTO: the key count below which dense (g = 1) is
  * faster than PIVOT-Refine (g = 8, k = 2048, c = 4096) on MI355X, measured on
@@ -134,12 +158,12 @@ typedef struct {
                               where it applies when the call resolves to Reuse; an error with an
                               explicit dense or Refine variant (Refine members already drop s > t) */
     int32_t auto_variant;  /* PIVOT_AUTO: PIVOT_REUSE or PIVOT_REFINE above the guardrail */
-    int32_t reserved;      /* 0 */
+    int32_t scan_path;     /* pivot_scan_path; 0 = PIVOT_PATH_AUTO */
     int64_t dense_below;   /* PIVOT_AUTO: dense when lk < dense_below; 0 = PIVOT_DENSE_BELOW_DEFAULT */
 } pivot_config;
 
 /* Defaults: Refine, g = 8, topk = 2048, c = 4096, mean proxy, group rows,
- * auto_variant = Refine, default guardrail. */
+ * auto_variant = Refine, automatic scan path, default guardrail. */
 pivot_status pivot_config_init(pivot_config *cfg);
 
 /* The variant a pivot_index call with this config runs (resolves PIVOT_AUTO). */
@@ -183,8 +207,8 @@ typedef struct {
 } pivot_keys;
 
 /* pivot_index over a ragged / paged batch (p->lk is the key capacity per
- * sequence). With paged keys the bf16 64-head / 128-dim shape takes the
- * split-key scan (the decode path) whatever the number of groups. */
+ * sequence). Every kernel reads keys through the page table, so paged keys
+ * take the same scan path as contiguous ones. */
 pivot_status pivot_index_kv(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
                             const pivot_keys *keys, int32_t *indices, float *scores, int32_t *candidates,
                             int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);

@@ -22,11 +22,12 @@ import torch
 __all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "index_kv", "resolve_variant", "pool",
            "index_stats",
            "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
-           "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "DENSE_BELOW_DEFAULT",
+           "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "SCAN_PATHS", "DENSE_BELOW_DEFAULT",
            "STAGES"]
 
 DENSE, REUSE, REFINE, AUTO = 0, 1, 2, 3
 AGGREGATIONS = {"mean": 0, "first": 1, "last": 2}
+SCAN_PATHS = {"auto": 0, "fused": 1, "split": 2}  # pivot_scan_path of the header
 DENSE_BELOW_DEFAULT = 8192  # PIVOT_DENSE_BELOW_DEFAULT of the header
 _F32, _BF16 = 0, 1
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -57,7 +58,7 @@ class Config(ctypes.Structure):
     """pivot_config of the header."""
     _fields_ = [("variant", ctypes.c_int32), ("g", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("c", ctypes.c_int32), ("aggregation", ctypes.c_int32), ("member_causal", ctypes.c_int32),
-                ("auto_variant", ctypes.c_int32), ("reserved", ctypes.c_int32), ("dense_below", ctypes.c_int64)]
+                ("auto_variant", ctypes.c_int32), ("scan_path", ctypes.c_int32), ("dense_below", ctypes.c_int64)]
 
 
 class Keys(ctypes.Structure):
@@ -188,8 +189,13 @@ def _finish(squeeze, *ts):
     return out if len(out) > 1 else out[0]
 
 
-def index_dense(q, w, k, topk: int, *, return_scores: bool = False, workspace=None, stream=None):
-    """eq. (1): every query keeps the top-k of its prefix s <= t."""
+def index_dense(q, w, k, topk: int, *, return_scores: bool = False, workspace=None, stream=None,
+                scan_path: str = "auto"):
+    """eq. (1): every query keeps the top-k of its prefix s <= t. scan_path
+    ("auto", "fused", "split") picks the scan kernels (pivot_scan_path)."""
+    if scan_path != "auto":
+        return index(q, w, k, make_config(variant=DENSE, g=1, topk=topk, scan_path=scan_path),
+                     return_scores=return_scores, workspace=workspace, stream=stream)
     prob, q, w, k, sq = _prepare(q, w, k)
     ws, wsb = _workspace(prob, DENSE, 1, topk, 0, q.device, workspace)
     idx, sc = _outputs(prob, topk, q.device, return_scores)
@@ -198,9 +204,13 @@ def index_dense(q, w, k, topk: int, *, return_scores: bool = False, workspace=No
     return _finish(sq, idx, sc) if return_scores else _finish(sq, idx)
 
 
-def index_reuse(q, w, k, g: int, topk: int, *, return_scores: bool = False, workspace=None, stream=None):
+def index_reuse(q, w, k, g: int, topk: int, *, return_scores: bool = False, workspace=None, stream=None,
+                scan_path: str = "auto"):
     """eqs. (4)-(6): one proxy scan per group of g rows; its top-k is every
     member's row."""
+    if scan_path != "auto":
+        return index(q, w, k, make_config(variant=REUSE, g=g, topk=topk, scan_path=scan_path),
+                     return_scores=return_scores, workspace=workspace, stream=stream)
     prob, q, w, k, sq = _prepare(q, w, k)
     ws, wsb = _workspace(prob, REUSE, g, topk, 0, q.device, workspace)
     idx, sc = _outputs(prob, topk, q.device, return_scores)
@@ -210,12 +220,16 @@ def index_reuse(q, w, k, g: int, topk: int, *, return_scores: bool = False, work
 
 
 def index_refine(q, w, k, g: int, topk: int, c: int | None = None, *, return_scores: bool = False,
-                 return_candidates: bool = False, workspace=None, stream=None):
+                 return_candidates: bool = False, workspace=None, stream=None, scan_path: str = "auto"):
     """eqs. (4)-(5), (7)-(9): one proxy scan per group keeps c candidates
     (default 2k); each member re-scores them and keeps its own top-k.
     With return_candidates, also returns C [B, G, c] (ascending, -1 pad) and
     |C| [B, G]."""
     c = 2 * topk if c is None else c
+    if scan_path != "auto":
+        return index(q, w, k, make_config(variant=REFINE, g=g, topk=topk, c=c, scan_path=scan_path),
+                     return_scores=return_scores, return_candidates=return_candidates, workspace=workspace,
+                     stream=stream)
     prob, q, w, k, sq = _prepare(q, w, k)
     ws, wsb = _workspace(prob, REFINE, g, topk, c, q.device, workspace)
     idx, sc = _outputs(prob, topk, q.device, return_scores)
@@ -237,11 +251,13 @@ def index_refine(q, w, k, g: int, topk: int, c: int | None = None, *, return_sco
 
 def make_config(variant: int = REFINE, g: int = 8, topk: int = 2048, c: int | None = None,
                 aggregation: str = "mean", member_causal: bool = False, auto_variant: int = REFINE,
-                dense_below: int = 0) -> Config:
+                dense_below: int = 0, scan_path: str = "auto") -> Config:
     """A pivot_config (c defaults to 2k; dense_below 0 = the library's
-    guardrail)."""
+    guardrail; scan_path "auto", "fused" or "split")."""
     if aggregation not in AGGREGATIONS:
         raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}")
+    if scan_path not in SCAN_PATHS:
+        raise ValueError(f"scan_path must be one of {sorted(SCAN_PATHS)}")
     cfg = Config()
     _check(load_library().pivot_config_init(ctypes.byref(cfg)))
     cfg.variant, cfg.g, cfg.topk = variant, g, topk
@@ -249,6 +265,7 @@ def make_config(variant: int = REFINE, g: int = 8, topk: int = 2048, c: int | No
     cfg.aggregation = AGGREGATIONS[aggregation]
     cfg.member_causal = 1 if member_causal else 0
     cfg.auto_variant, cfg.dense_below = auto_variant, dense_below
+    cfg.scan_path = SCAN_PATHS[scan_path]
     return cfg
 
 

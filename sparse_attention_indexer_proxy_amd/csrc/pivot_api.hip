@@ -106,6 +106,7 @@ struct Cfg {
     int32_t g, topk, c;
     int agg;      // pivot_aggregation
     bool causal;  // member-causal Reuse
+    int path;     // pivot_scan_path
 };
 
 struct Layout {
@@ -118,9 +119,9 @@ struct Layout {
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
-// key axis is split over workgroups instead (decode shapes). The environment
-// variable PIVOT_FEW_GROUPS overrides the threshold (0 disables the split
-// path, a huge value forces it); tests use it to cover both paths.
+// key axis is split over workgroups instead (decode shapes). A config's
+// scan_path can name either path explicitly.
+constexpr int64_t kFewGroups = 256;
 #ifndef PIVOT_SPLIT_SCAN_WGS
 #define PIVOT_SPLIT_SCAN_WGS 512
 #endif
@@ -129,11 +130,25 @@ struct Layout {
 // deep per wave, so long-lived waves keep HBM busy).
 constexpr int64_t kSplitScanWorkgroups = PIVOT_SPLIT_SCAN_WGS;
 
-int64_t few_groups_threshold()
+// Shapes without an MFMA kernel (f32, or bf16 with heads != 64 or dim !=
+// 128) run the exact-order kernels: one lane per key, fp32 in the
+// definition's order. They are meant for small problems (and for bit-exact
+// checks); a call whose scan and refine need more multiply-adds than this is
+// refused rather than run slowly.
+constexpr double kExactMaxMacs = 68719476736.0;  // 2^36
+
+pivot_status check_exact_work(const pivot_problem *p, int64_t G, int64_t c)
 {
-    const char *v = getenv("PIVOT_FEW_GROUPS");
-    if (v && *v) return strtoll(v, nullptr, 10);
-    return 256;
+    if (pivot::mfma_shape(shape_of(p))) return PIVOT_OK;
+    const double pairs = double(p->batch) * double(G) * double(p->lk) +
+                         double(p->batch) * double(p->lq) * double(c < p->lk ? c : p->lk);
+    const double macs = pairs * double(p->heads) * double(p->dim);
+    if (macs > kExactMaxMacs)
+        return fail(PIVOT_ERR_UNSUPPORTED,
+                    "no MFMA kernel for %s with %d heads and dim %d (MFMA: bf16, 64 heads, dim 128); the exact-order "
+                    "kernels take at most 2^36 multiply-adds per call, this one needs about %.3g",
+                    p->dtype == PIVOT_BF16 ? "bf16" : "f32", p->heads, p->dim, macs);
+    return PIVOT_OK;
 }
 
 // The short-context guardrail of PIVOT_AUTO: dense below this many keys.
@@ -168,12 +183,15 @@ pivot_status resolve(const pivot_problem *p, const pivot_config *cfg, Cfg *out)
     c.c = c.variant == PIVOT_REFINE ? cfg->c : 0;
     c.agg = c.variant == PIVOT_DENSE ? PIVOT_AGG_MEAN : cfg->aggregation;
     c.causal = c.variant == PIVOT_REUSE && cfg->member_causal != 0;
+    if (cfg->scan_path < PIVOT_PATH_AUTO || cfg->scan_path > PIVOT_PATH_SPLIT)
+        return fail(PIVOT_ERR_INVALID_ARG, "unknown scan_path %d", cfg->scan_path);
+    c.path = cfg->scan_path;
     *out = c;
     return PIVOT_OK;
 }
 
-// paged: keys in pages (the MFMA shape then takes the split scan, which
-// translates every key row it reads).
+// paged: keys in pages (every kernel translates the key rows it reads;
+// the layout does not depend on it).
 pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
 {
     pivot_status st = check_problem(p);
@@ -192,6 +210,8 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
     Layout l{};
     l.g = g;
     l.G = (p->lq + g - 1) / g;
+    st = check_exact_work(p, l.G, variant == PIVOT_REFINE ? c : 0);
+    if (st != PIVOT_OK) return st;
     // scan selection size: c (Refine), k (Reuse, dense) or k + g - 1
     // (member-causal Reuse: every member's top-k over s <= t lies in the
     // group's top-(k + g - 1) over s <= t_last, since at most g - 1
@@ -219,7 +239,8 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
     };
     l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
-    l.few = pivot::mfma_shape(sh) && (paged || static_cast<int64_t>(groups) < few_groups_threshold());
+    l.few = pivot::mfma_shape(sh) &&
+            (cfg.path == PIVOT_PATH_SPLIT || (cfg.path == PIVOT_PATH_AUTO && static_cast<int64_t>(groups) < kFewGroups));
     if (l.few) {
         // split scan: about kSplitScanWorkgroups workgroups of four waves
         // over all groups, each wave streaming at least one 64-key quarter
@@ -474,6 +495,7 @@ Cfg basic(int variant, int32_t g, int32_t topk, int32_t c)
     cfg.c = variant == PIVOT_REFINE ? c : 0;
     cfg.agg = PIVOT_AGG_MEAN;
     cfg.causal = false;
+    cfg.path = PIVOT_PATH_AUTO;
     return cfg;
 }
 
@@ -527,6 +549,7 @@ pivot_status pivot_config_init(pivot_config *cfg)
     cfg->aggregation = PIVOT_AGG_MEAN;
     cfg->member_causal = 0;
     cfg->auto_variant = PIVOT_REFINE;
+    cfg->scan_path = PIVOT_PATH_AUTO;
     cfg->dense_below = 0;
     return PIVOT_OK;
 }
@@ -659,6 +682,8 @@ pivot_status pivot_proxy_scores(const pivot_problem *p, int32_t g, const void *q
     if (!qbar || !wbar || !k || !out) return fail(PIVOT_ERR_INVALID_ARG, "qbar, wbar, k and out must be non-NULL");
     if (reinterpret_cast<uintptr_t>(qbar) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0)
         return fail(PIVOT_ERR_INVALID_ARG, "qbar and k must be 16-byte aligned");
+    st = check_exact_work(p, (p->lq + g - 1) / g, 0);
+    if (st != PIVOT_OK) return st;
     pivot::ScanLaunch sl{};
     sl.qsrc = qbar;
     sl.wsrc = wbar;

@@ -23,6 +23,7 @@
 #include <cstdint>
 
 #include "pivot_kernels.h"
+#include "pivot_launch.h"
 
 namespace pivot {
 namespace {
@@ -571,28 +572,32 @@ hipError_t launch_stats(const StatsArgs &a, hipStream_t st)
     const int64_t rows = a.B * a.Lq;
     const dim3 block(kDiagWaves * kW);
     const dim3 rgrid(static_cast<uint32_t>((rows + kDiagWaves - 1) / kDiagWaves));
+    hipError_t e = hipSuccess;
     if (a.overlap) {
         if (a.k <= 1024)
-            hipLaunchKernelGGL(k_row_overlap<16>, rgrid, block, 0, st, a);
+            e = launch(&k_row_overlap<16>, rgrid, block, st, a);
         else if (a.k <= 2048)
-            hipLaunchKernelGGL(k_row_overlap<32>, rgrid, block, 0, st, a);
+            e = launch(&k_row_overlap<32>, rgrid, block, st, a);
         else
-            hipLaunchKernelGGL(k_row_overlap<64>, rgrid, block, 0, st, a);
+            e = launch(&k_row_overlap<64>, rgrid, block, st, a);
+        if (e != hipSuccess) return e;
     }
     if (a.group_union || a.group_inter) {
         const dim3 ggrid(static_cast<uint32_t>(a.B * a.G));
-        hipLaunchKernelGGL(k_group_bits, ggrid, dim3(kSetThreads), 0, st, a);
-        hipLaunchKernelGGL(k_group_sets, ggrid, dim3(kSetThreads), 0, st, a);
+        e = launch(&k_group_bits, ggrid, dim3(kSetThreads), st, a);
+        if (e != hipSuccess) return e;
+        e = launch(&k_group_sets, ggrid, dim3(kSetThreads), st, a);
+        if (e != hipSuccess) return e;
     }
     if (a.mass) {
         if (a.k <= 1024)
-            hipLaunchKernelGGL(k_row_mass<16>, rgrid, block, 0, st, a);
+            e = launch(&k_row_mass<16>, rgrid, block, st, a);
         else if (a.k <= 2048)
-            hipLaunchKernelGGL(k_row_mass<32>, rgrid, block, 0, st, a);
+            e = launch(&k_row_mass<32>, rgrid, block, st, a);
         else
-            hipLaunchKernelGGL(k_row_mass<64>, rgrid, block, 0, st, a);
+            e = launch(&k_row_mass<64>, rgrid, block, st, a);
     }
-    return hipGetLastError();
+    return e;
 }
 
 int stats_row_max() { return kRowMax; }

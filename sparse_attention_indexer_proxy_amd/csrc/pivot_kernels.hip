@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "pivot_kernels.h"
+#include "pivot_launch.h"
 
 namespace pivot {
 namespace {
@@ -851,10 +852,11 @@ __device__ __forceinline__ void tile_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int H, int D, int Mode>
+template <int H, int D, int Mode, bool PAGED>
 __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
+    static_assert(!PAGED || kScanBufs == 2, "paged keys: two tile buffers");
     constexpr int RB = H / 16;
     constexpr int NT = kScanTileKeys;                     // keys per tile
     constexpr int NQ = NT / kWave;                        // 64-key quarters per tile
@@ -885,8 +887,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     const int64_t wg_tlast = geo.t_last(b, m_hi);
     const int64_t my_tlast = active ? geo.t_last(b, m) : -1;
     const int ntiles = static_cast<int>(wg_tlast / NT) + 1;
-    // contiguous keys only (paged calls take the split scan); rows up to the
-    // capacity exist, those past the sequence are masked
+    // contiguous keys: rows up to the capacity exist, those past the
+    // sequence are masked
     const uint16_t *kseq = static_cast<const uint16_t *>(a.keys.base) + b * geo.Lk * D;
     const int64_t gid = b * geo.G + (active ? m : blk * kScanWaves);
 
@@ -915,9 +917,40 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
         const int slice = wv * SLICES_PER_WAVE + j;
         slice_voff[j] = static_cast<uint32_t>((slice_row(slice, l) * D + slice_col(slice, l)) * 2);
     }
+    // Paged keys: lane l's row of slice j of the tile at `base` is key
+    // base + slice_row(slice, l) (clamped to the sequence's last key; those
+    // past t_last are masked), whose page table entry is read one tile
+    // ahead of its DMA, so the DMA issue never waits for a table load.
+    const int64_t lkb = geo.lk(b);
+    int32_t ent[PAGED ? SLICES_PER_WAVE : 1];
+    auto key_of = [&](int64_t base, int j) {
+        const int64_t s = base + slice_row(wv * SLICES_PER_WAVE + j, l);
+        return static_cast<uint32_t>(s < lkb ? s : (lkb > 0 ? lkb - 1 : 0));
+    };
+    auto load_entries = [&](int64_t base) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int j = 0; j < SLICES_PER_WAVE; ++j) {
+                const uint32_t s = key_of(base, j);
+                ent[j] = load_as<kGlobal>(a.keys.pg.table, b * a.keys.pg.max_pages + a.keys.page_index(s));
+            }
+        }
+    };
     auto issue_tile = [&](int buf, int64_t base) {
         uint16_t *dst = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
-        dma_key_tile(kseq, base, geo.Lk, dst + wv * SLICES_PER_WAVE * 512, slice_voff);
+        if constexpr (PAGED) {
+            const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
+#pragma unroll
+            for (int j = 0; j < SLICES_PER_WAVE; ++j) {
+                const int slice = wv * SLICES_PER_WAVE + j;
+                const uint32_t s = key_of(base, j);
+                const int64_t r = a.keys.paged_row(ent[j], a.keys.page_offset(s));
+                __builtin_amdgcn_global_load_lds((global_cptr)(kbase + r * D + slice_col(slice, l)),
+                                                 (lds_ptr)(dst + slice * 512), 16, 0, 0);
+            }
+        } else {
+            dma_key_tile(kseq, base, geo.Lk, dst + wv * SLICES_PER_WAVE * 512, slice_voff);
+        }
     };
 
     // Phases of a pass over the tiles; the per-score work is chosen at run
@@ -947,7 +980,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     auto pass = [&](int phase, int step) {
         const int nt = (ntiles - 1) / step + 1;  // tiles 0, step, 2 step, ...
         const int64_t tstep = static_cast<int64_t>(step) * NT;
+        load_entries(0);
         issue_tile(0, 0);
+        if (PAGED && nt > 1) load_entries(tstep);
         if (NB == 3 && nt > 1) {
             issue_tile(1, tstep);
             __builtin_amdgcn_s_waitcnt(0x0F70 | SLICES_PER_WAVE);  // tile 0 has landed, tile 1 may not
@@ -967,7 +1002,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             // the buffer of tile i + NB - 1 held tile i - 1, which every wave
             // finished reading before the last barrier
             const bool ahead = i + NB - 1 < nt;
-            if (ahead) issue_tile(buf == 0 ? NB - 1 : buf - 1, base + (NB - 1) * tstep);
+            if (ahead) {
+                issue_tile(buf == 0 ? NB - 1 : buf - 1, base + (NB - 1) * tstep);
+                if (PAGED && i + 2 < nt) load_entries(base + 2 * tstep);
+            }
             auto emit = [&](int qt, float score) {
                 if (qt < 0)
                     on_score(phase, prev_it, NQ - 1, static_cast<int64_t>(prev_it) * NT + (NQ - 1) * kWave, score);
@@ -2717,24 +2755,24 @@ __global__ __launch_bounds__(256) void k_refine_exact(RefineArgs a)
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     Geo geo{sh.B, G, sh.Lq, sh.Lk, g, sh.lens};
     const int vec = sh.bf16 ? 8 : 4;
     const int64_t total = sh.B * G * sh.H * (sh.D / vec);
     const int64_t blocks = (total + 255) / 256;
     if (sh.bf16) {
-        hipLaunchKernelGGL(k_pool<uint16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(q), w, static_cast<uint16_t *>(qbar), wbar, geo, sh.H, sh.D, agg);
+        e = launch(&k_pool<uint16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), st, static_cast<const uint16_t *>(q), w, static_cast<uint16_t *>(qbar), wbar, geo, sh.H, sh.D, agg);
     } else {
-        hipLaunchKernelGGL(k_pool<float>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
-                           static_cast<const float *>(q), w, static_cast<float *>(qbar), wbar, geo, sh.H, sh.D, agg);
+        e = launch(&k_pool<float>, dim3(static_cast<uint32_t>(blocks)), dim3(256), st, static_cast<const float *>(q), w, static_cast<float *>(qbar), wbar, geo, sh.H, sh.D, agg);
     }
-    return hipGetLastError();
+    return e;
 }
 
 bool mfma_shape(const LaunchShape &sh) { return sh.bf16 && sh.H == 64 && sh.D == 128; }
 
 hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     ScanArgs a{};
     a.qsrc = L.qsrc;
     a.wsrc = L.wsrc;
@@ -2754,26 +2792,32 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     if (mfma_shape(sh)) {
         const dim3 mgrid(static_cast<uint32_t>(sh.B * ((L.G + kScanWaves - 1) / kScanWaves)));
         const dim3 mblock(kScanWaves * 64);
-        if (rows)
-            hipLaunchKernelGGL((k_scan_mfma<64, 128, kRows>), mgrid, mblock, 0, st, a);
+        const bool paged = sh.pages.table != nullptr;
+        if (rows && paged)
+            e = launch(&k_scan_mfma<64, 128, kRows, true>, mgrid, mblock, st, a);
+        else if (rows)
+            e = launch(&k_scan_mfma<64, 128, kRows, false>, mgrid, mblock, st, a);
+        else if (paged)
+            e = launch(&k_scan_mfma<64, 128, kFilter, true>, mgrid, mblock, st, a);
         else
-            hipLaunchKernelGGL((k_scan_mfma<64, 128, kFilter>), mgrid, mblock, 0, st, a);
+            e = launch(&k_scan_mfma<64, 128, kFilter, false>, mgrid, mblock, st, a);
     } else if (sh.bf16) {
         if (rows)
-            hipLaunchKernelGGL((k_scan_exact<uint16_t, kRows>), grid, block, 0, st, a);
+            e = launch(&k_scan_exact<uint16_t, kRows>, grid, block, st, a);
         else
-            hipLaunchKernelGGL((k_scan_exact<uint16_t, kFilter>), grid, block, 0, st, a);
+            e = launch(&k_scan_exact<uint16_t, kFilter>, grid, block, st, a);
     } else {
         if (rows)
-            hipLaunchKernelGGL((k_scan_exact<float, kRows>), grid, block, 0, st, a);
+            e = launch(&k_scan_exact<float, kRows>, grid, block, st, a);
         else
-            hipLaunchKernelGGL((k_scan_exact<float, kFilter>), grid, block, 0, st, a);
+            e = launch(&k_scan_exact<float, kFilter>, grid, block, st, a);
     }
-    return hipGetLastError();
+    return e;
 }
 
 hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     RefineArgs a{};
     a.q = L.q;
     a.w = L.w;
@@ -2796,19 +2840,19 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
         // 4 or 8 member waves; more members loop in rounds
         const bool paged = sh.pages.table != nullptr;
         if (L.g <= 4 && paged)
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4, true>), grid, dim3(64 * 4), 0, st, a);
+            e = launch(&k_refine_mfma<64, 128, 4, true>, grid, dim3(64 * 4), st, a);
         else if (L.g <= 4)
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 4, false>), grid, dim3(64 * 4), 0, st, a);
+            e = launch(&k_refine_mfma<64, 128, 4, false>, grid, dim3(64 * 4), st, a);
         else if (paged)
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8, true>), grid, dim3(64 * 8), 0, st, a);
+            e = launch(&k_refine_mfma<64, 128, 8, true>, grid, dim3(64 * 8), st, a);
         else
-            hipLaunchKernelGGL((k_refine_mfma<64, 128, 8, false>), grid, dim3(64 * 8), 0, st, a);
+            e = launch(&k_refine_mfma<64, 128, 8, false>, grid, dim3(64 * 8), st, a);
     } else if (sh.bf16) {
-        hipLaunchKernelGGL(k_refine_exact<uint16_t>, grid, dim3(256), 0, st, a);
+        e = launch(&k_refine_exact<uint16_t>, grid, dim3(256), st, a);
     } else {
-        hipLaunchKernelGGL(k_refine_exact<float>, grid, dim3(256), 0, st, a);
+        e = launch(&k_refine_exact<float>, grid, dim3(256), st, a);
     }
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace pivot
@@ -2817,6 +2861,7 @@ namespace pivot {
 
 hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int splits, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     if (!mfma_shape(sh) || !L.rows || splits < 1) return hipErrorInvalidValue;
     ScanArgs a{};
     a.qsrc = L.qsrc;
@@ -2828,10 +2873,10 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.rows = L.rows;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
     if (sh.pages.table)
-        hipLaunchKernelGGL((k_scan_split<64, 128, true>), grid, dim3(kSplitWaves * 64), 0, st, a, splits);
+        e = launch(&k_scan_split<64, 128, true>, grid, dim3(kSplitWaves * 64), st, a, splits);
     else
-        hipLaunchKernelGGL((k_scan_split<64, 128, false>), grid, dim3(kSplitWaves * 64), 0, st, a, splits);
-    return hipGetLastError();
+        e = launch(&k_scan_split<64, 128, false>, grid, dim3(kSplitWaves * 64), st, a, splits);
+    return e;
 }
 
 int group_select_slabs(int cap)
@@ -2843,6 +2888,7 @@ int group_select_slabs(int cap)
 
 hipError_t launch_select_groups(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     if (!mfma_shape(sh) || L.rows || !L.buf_n) return hipErrorInvalidValue;
     GroupSelectArgs a{};
     a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
@@ -2853,14 +2899,14 @@ hipError_t launch_select_groups(const LaunchShape &sh, const ScanLaunch &L, hipS
     a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
     const dim3 grid(static_cast<uint32_t>((sh.B * L.G + kMsWaves - 1) / kMsWaves)), block(kMsWaves * kWave);
     switch (group_select_slabs(L.cap)) {
-    case 8: hipLaunchKernelGGL(k_select_groups<8>, grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL(k_select_groups<16>, grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL(k_select_groups<32>, grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL(k_select_groups<64>, grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL(k_select_groups<128>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(k_select_groups<0>, grid, block, 0, st, a); break;
+    case 8: e = launch(&k_select_groups<8>, grid, block, st, a); break;
+    case 16: e = launch(&k_select_groups<16>, grid, block, st, a); break;
+    case 32: e = launch(&k_select_groups<32>, grid, block, st, a); break;
+    case 64: e = launch(&k_select_groups<64>, grid, block, st, a); break;
+    case 128: e = launch(&k_select_groups<128>, grid, block, st, a); break;
+    default: e = launch(&k_select_groups<0>, grid, block, st, a); break;
     }
-    return hipGetLastError();
+    return e;
 }
 
 int member_select_slabs(int c)
@@ -2872,6 +2918,7 @@ int member_select_slabs(int c)
 
 hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch &L, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     MemberSelectArgs a{};
     a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.topk = L.topk;
@@ -2886,17 +2933,18 @@ hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch
     const int64_t rows = sh.B * sh.Lq;
     const dim3 grid(static_cast<uint32_t>((rows + kMsWaves - 1) / kMsWaves)), block(kMsWaves * kWave);
     switch (member_select_slabs(L.c)) {
-    case 8: hipLaunchKernelGGL(k_select_members<8>, grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL(k_select_members<16>, grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL(k_select_members<32>, grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL(k_select_members<64>, grid, block, 0, st, a); break;
+    case 8: e = launch(&k_select_members<8>, grid, block, st, a); break;
+    case 16: e = launch(&k_select_members<16>, grid, block, st, a); break;
+    case 32: e = launch(&k_select_members<32>, grid, block, st, a); break;
+    case 64: e = launch(&k_select_members<64>, grid, block, st, a); break;
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    return e;
 }
 
 hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     RowSelectArgs a{};
     a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.kind = L.kind;
@@ -2911,8 +2959,8 @@ hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, h
     a.cand_n = L.cand_n;
     a.c = L.c;
     const int64_t jobs = L.kind == 0 ? sh.B * L.G : sh.B * sh.Lq;
-    hipLaunchKernelGGL(k_select_rows, dim3(static_cast<uint32_t>(jobs)), dim3(kSelThreads), 0, st, a);
-    return hipGetLastError();
+    e = launch(&k_select_rows, dim3(static_cast<uint32_t>(jobs)), dim3(kSelThreads), st, a);
+    return e;
 }
 
 }  // namespace pivot

@@ -201,3 +201,30 @@ def test_index_stats_validates_before_launch(pivot_lib):
     assert call(1, 8, 4096, fake, None, 1, 8, None, None, out, None, None) == 2     # g * k > 16384
     assert call(1, 8, 16, fake, None, 1, 1, None, None, None, out, None) == 1       # mass without scores
     assert call(0, 8, 16, fake, None, 1, 1, out, None, None, None, None) == 1
+
+
+@pytest.mark.parametrize("H,D,dt", [(64, 128, 0), (32, 128, 1), (64, 64, 1)])
+def test_shapes_without_mfma_are_refused_above_the_exact_kernel_limit(pivot_lib, H, D, dt):
+    """f32 and bf16 shapes other than (64 heads, dim 128) run the exact-order
+    kernels only up to 2^36 multiply-adds per call: no slow fallback at size."""
+    big = _prob(Lq=131072, Lk=131072, H=H, D=D, dt=dt)
+    st, _ = _ws(pivot_lib, big, pv.REFINE, 8, 2048, 4096)
+    assert st == 2
+    assert "MFMA" in pivot_lib.pivot_last_error().decode()
+    small = _prob(Lq=512, Lk=512, H=4, D=32, dt=0)  # the tiny f32 workload
+    assert _ws(pivot_lib, small, pv.DENSE, 1, 16, 0)[0] == 0
+    mfma = _prob(Lq=131072, Lk=131072)  # bf16, 64 heads, dim 128: any size
+    assert _ws(pivot_lib, mfma, pv.DENSE, 1, 2048, 0)[0] == 0
+
+
+def test_config_scan_path_is_checked(pivot_lib):
+    cfg = pv.make_config(variant=pv.REFINE, g=8, topk=16, c=32)
+    prob = _prob()
+    out = ctypes.c_size_t(0)
+    for path in (0, 1, 2):
+        cfg.scan_path = path
+        assert pivot_lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(out)) == 0
+    cfg.scan_path = 3
+    assert pivot_lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(out)) == 1
+    with pytest.raises(ValueError):
+        pv.make_config(scan_path="elsewhere")

@@ -33,11 +33,12 @@ def _need_gpu(pivot_lib):
         pytest.skip("no GPU")
 
 
-def _gpu_all(q, w, k, g, topk, c):
+def _gpu_all(q, w, k, g, topk, c, path="auto"):
     tq, tw, tk = to_device(q, w, k)
-    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True)
-    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True)
-    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True)
+    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True, scan_path=path)
+    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True, scan_path=path)
+    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True,
+                                         scan_path=path)
     torch.cuda.synchronize()
     cpu = lambda t: t.cpu().numpy()
     return {"dense": (cpu(d_i), cpu(d_s)), "reuse": (cpu(r_i), cpu(r_s)),
@@ -99,10 +100,9 @@ MFMA_EXACT_CASES = [
 
 
 @pytest.fixture(params=["fused", "split"])
-def scan_path(request, monkeypatch):
+def scan_path(request):
     """Run a test on the fused per-group scan ("fused") and on the split-key
     scan + block selects used for few groups ("split")."""
-    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if request.param == "fused" else str(1 << 40))
     return request.param
 
 
@@ -110,14 +110,14 @@ def scan_path(request, monkeypatch):
 def test_mfma_kernels_bitwise_on_exact_inputs(case, scan_path):
     name, B, Lq, Lk, g, topk, c, wl = case
     q, w, k = exact_random(zlib.crc32(name.encode()) % 1000, B, Lq, Lk, 64, 128, BF16, w_levels=wl)
-    _assert_bitwise(_gpu_all(q, w, k, g, topk, c), _oracle_all(q, w, k, g, topk, c))
+    _assert_bitwise(_gpu_all(q, w, k, g, topk, c, scan_path), _oracle_all(q, w, k, g, topk, c))
 
 
 def test_mfma_all_equal_keys_fall_back_to_position(scan_path):
     L, g, topk, c = 200, 8, 16, 32
     q, w, _ = exact_random(5, 1, L, L, 64, 128, BF16)
     k = np.tile(exact_random(6, 1, 1, 1, 1, 128, BF16)[2], (1, L, 1))
-    gpu = _gpu_all(q, w, k, g, topk, c)
+    gpu = _gpu_all(q, w, k, g, topk, c, scan_path)
     for v in ("dense", "refine"):
         idx = gpu[v][0][0]
         for t in range(L):
@@ -130,7 +130,7 @@ def test_mfma_all_equal_keys_fall_back_to_position(scan_path):
 def test_mfma_kernels_float_rule_on_gaussian_inputs(seed, scan_path):
     B, L, g, topk, c = 1, 600, 8, 24, 48
     q, w, k = gauss_random(seed, B, L, L, 64, 128, BF16)
-    gpu = _gpu_all(q, w, k, g, topk, c)
+    gpu = _gpu_all(q, w, k, g, topk, c, scan_path)
     ref = _oracle_all(q, w, k, g, topk, c)
     qf = q.view(np.uint16)
     from workloads import bf16_bits_to_f32
@@ -250,9 +250,10 @@ def test_mfma_sampled_threshold_stays_exact(hot_sampled, stripe, scan_path):
     w = np.ldexp(1.0, r.integers(-3, 1, size=(1, L, 64))).astype(np.float32)
     k = _striped_keys(L, 3, hot_sampled, stripe)
     tq, tw, tk = to_device(q, w, k)
-    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True)
-    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True)
-    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True)
+    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True,
+                                         scan_path=scan_path)
+    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True, scan_path=scan_path)
+    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True, scan_path=scan_path)
     torch.cuda.synchronize()
     ref = oracle.refine(q, w, k, g, topk, c)
     np.testing.assert_array_equal(f_n.cpu().numpy(), ref["cand_n"])

@@ -7,8 +7,8 @@ also equal the contiguous ones bit for bit.
 
 Exact inputs (q, k in {-3..3}/4, w powers of two) make every score exact, so
 indices, scores and candidate sets must match bit for bit on the MFMA
-kernels (split-key scan for paged keys; the fused scan too for contiguous
-ragged keys) and on the exact-order kernels.
+kernels (the fused scan and the split-key scan, contiguous and paged keys)
+and on the exact-order kernels.
 """
 import zlib
 
@@ -78,11 +78,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("variant", ["dense", "reuse", "refine"])
 @pytest.mark.parametrize("page", [0, 16, 48, 64])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_ragged_and_paged_match_oracle_bitwise(case, page, variant):
+def test_ragged_and_paged_match_oracle_bitwise(case, page, variant, path):
     name, B, Lq, Lk, H, d, g, topk, c, dt = case
+    if H != 64 and path == "split":
+        pytest.skip("the exact-order kernels have one scan path")
     seed = zlib.crc32(name.encode()) % 1000
     q, w, k = exact_random(seed, B, Lq, Lk, H, d, dt)
     r = np.random.default_rng(seed)
@@ -90,7 +93,8 @@ def test_ragged_and_paged_match_oracle_bitwise(case, page, variant):
     lens[0] = Lk
     ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
     tq, tw = _dev(q), _dev(w)
-    kw = dict(variant={"dense": pv.DENSE, "reuse": pv.REUSE, "refine": pv.REFINE}[variant], g=g, topk=topk, c=c)
+    kw = dict(variant={"dense": pv.DENSE, "reuse": pv.REUSE, "refine": pv.REFINE}[variant], g=g, topk=topk, c=c,
+              scan_path=path)
     tl = torch.from_numpy(lens).cuda()
     if page:
         pool, table = _paged(k, page, seed)
@@ -104,15 +108,14 @@ def test_ragged_and_paged_match_oracle_bitwise(case, page, variant):
 
 
 @pytest.mark.parametrize("path", ["fused", "split"])
-def test_contiguous_ragged_on_both_scan_paths(path, monkeypatch):
-    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if path == "fused" else str(1 << 40))
+def test_contiguous_ragged_on_both_scan_paths(path):
     B, Lq, Lk, g, topk, c = 3, 500, 1200, 8, 32, 64
     q, w, k = exact_random(41, B, Lq, Lk, 64, 128, BF16)
     lens = np.array([1200, 777, 501], dtype=np.int32)
     tq, tw, tk = _dev(q), _dev(w), _dev(k)
     tl = torch.from_numpy(lens).cuda()
     for variant, v in (("refine", pv.REFINE), ("reuse", pv.REUSE)):
-        i, s = pv.index_kv(tq, tw, tk, tl, return_scores=True, variant=v, g=g, topk=topk, c=c)
+        i, s = pv.index_kv(tq, tw, tk, tl, return_scores=True, variant=v, g=g, topk=topk, c=c, scan_path=path)
         torch.cuda.synchronize()
         ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
         np.testing.assert_array_equal(i.cpu().numpy(), ref_i)
@@ -191,19 +194,18 @@ def test_lengths_outside_the_capacity_are_clamped():
 
 
 @pytest.mark.parametrize("path", ["fused", "split"])
-def test_groups_before_their_sequence_start_are_empty(path, monkeypatch):
+def test_groups_before_their_sequence_start_are_empty(path):
     """A sequence shorter than the query block: whole groups sit before its
     first key (empty candidate sets; the member rows are all -1), the rest
     equal the oracle's prefill on that sequence. Lq - len is a multiple of g,
     so the groups that see keys form a prefill problem of their own."""
-    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if path == "fused" else str(1 << 40))
     B, Lq, Lk, g, topk, c = 2, 1100, 1100, 4, 16, 32
     q, w, k = exact_random(53, B, Lq, Lk, 64, 128, BF16)
     lens = np.array([1100, 300], dtype=np.int32)
     r0 = Lq - 300
     for variant, v in (("refine", pv.REFINE), ("reuse", pv.REUSE)):
         i, s = pv.index_kv(_dev(q), _dev(w), _dev(k), torch.from_numpy(lens).cuda(), return_scores=True,
-                           variant=v, g=g, topk=topk, c=c)
+                           variant=v, g=g, topk=topk, c=c, scan_path=path)
         torch.cuda.synchronize()
         got_i, got_s = i.cpu().numpy(), s.cpu().numpy()
         assert np.all(got_i[1, :r0] == -1) and np.all(np.isneginf(got_s[1, :r0]))
@@ -245,18 +247,21 @@ def test_ragged_aggregation_and_member_causal_reuse(agg, causal, page):
         np.testing.assert_array_equal(got_s[b], r["scores"][0], err_msg=f"{variant} {agg} b={b}")
 
 
+@pytest.mark.parametrize("path", ["auto", "split"])
 @pytest.mark.parametrize("variant", ["refine", "reuse"])
-def test_paged_prefill_with_many_groups(variant):
-    """Paged keys always take the split-key scan; with 512+ groups each group
-    gets a single workgroup (four waves sweeping its quarters from a
-    staggered start), the longest case of that kernel's per-wave loop."""
+def test_paged_prefill_with_many_groups(variant, path):
+    """Paged prefill with 1000 groups: automatically the fused scan (its tile
+    DMA reads every key through the page table); forced onto the split-key
+    scan, each group gets a single workgroup (four waves sweeping its
+    quarters from a staggered start), the longest case of that kernel's
+    per-wave loop."""
     B, Lq, Lk, g, topk, c, page = 2, 2000, 2300, 4, 16, 32, 96  # 1000 groups
     q, w, k = exact_random(57, B, Lq, Lk, 64, 128, BF16)
     lens = np.array([2300, 2011], dtype=np.int32)
     pool, table = _paged(k, page, 58)
     v = {"refine": pv.REFINE, "reuse": pv.REUSE}[variant]
     i, s = pv.index_kv(_dev(q), _dev(w), _dev(pool), torch.from_numpy(lens).cuda(), torch.from_numpy(table).cuda(),
-                       page_size=page, lk=Lk, return_scores=True, variant=v, g=g, topk=topk, c=c)
+                       page_size=page, lk=Lk, return_scores=True, variant=v, g=g, topk=topk, c=c, scan_path=path)
     torch.cuda.synchronize()
     ref_i, ref_s = _oracle_ragged(variant, q, w, k, lens, g, topk, c)
     np.testing.assert_array_equal(i.cpu().numpy(), ref_i)

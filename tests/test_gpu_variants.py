@@ -36,8 +36,9 @@ def _need_gpu(pivot_lib):
 
 
 @pytest.fixture(params=["fused", "split"])
-def scan_path(request, monkeypatch):
-    monkeypatch.setenv("PIVOT_FEW_GROUPS", "0" if request.param == "fused" else str(1 << 40))
+def scan_path(request):
+    """The fused per-group scan or the split-key scan + block selects
+    (pivot_config.scan_path); the exact-order kernels ignore it."""
     return request.param
 
 
@@ -68,9 +69,10 @@ def test_aggregation_bitwise(case, agg, scan_path):
     name, B, Lq, Lk, H, d, g, topk, c, dt = case
     q, w, k = _data(case)
     tq, tw, tk = to_device(q, w, k)
-    r_i, r_s = pv.index(tq, tw, tk, variant=pv.REUSE, g=g, topk=topk, aggregation=agg, return_scores=True)
+    r_i, r_s = pv.index(tq, tw, tk, variant=pv.REUSE, g=g, topk=topk, aggregation=agg, return_scores=True,
+                        scan_path=scan_path)
     f_i, f_s, f_c, f_n = pv.index(tq, tw, tk, variant=pv.REFINE, g=g, topk=topk, c=c, aggregation=agg,
-                                  return_scores=True, return_candidates=True)
+                                  return_scores=True, return_candidates=True, scan_path=scan_path)
     torch.cuda.synchronize()
     ref = oracle.reuse(q, w, k, g, topk, agg=agg)
     np.testing.assert_array_equal(_cpu(r_i), ref["indices"])
@@ -89,7 +91,7 @@ def test_member_causal_reuse_bitwise(case, agg, scan_path):
     q, w, k = _data(case)
     tq, tw, tk = to_device(q, w, k)
     i, s = pv.index(tq, tw, tk, variant=pv.REUSE, g=g, topk=topk, aggregation=agg, member_causal=True,
-                    return_scores=True)
+                    return_scores=True, scan_path=scan_path)
     torch.cuda.synchronize()
     ref = oracle.reuse(q, w, k, g, topk, agg=agg, member_causal=True)
     np.testing.assert_array_equal(_cpu(i), ref["indices"])
@@ -107,9 +109,9 @@ def test_member_causal_reuse_float_inputs_match_plain_reuse_on_last_members(scan
     L, g, topk = 600, 8, 24
     q, w, k = gauss_random(21, 1, L, L, 64, 128, BF16)
     tq, tw, tk = to_device(q, w, k)
-    mc = _cpu(pv.index(tq, tw, tk, variant=pv.REUSE, g=g, topk=topk, member_causal=True))
-    plain = _cpu(pv.index_reuse(tq, tw, tk, g, topk))
-    wide = _cpu(pv.index_reuse(tq, tw, tk, g, topk + g - 1))
+    mc = _cpu(pv.index(tq, tw, tk, variant=pv.REUSE, g=g, topk=topk, member_causal=True, scan_path=scan_path))
+    plain = _cpu(pv.index_reuse(tq, tw, tk, g, topk, scan_path=scan_path))
+    wide = _cpu(pv.index_reuse(tq, tw, tk, g, topk + g - 1, scan_path=scan_path))
     torch.cuda.synchronize()
     for m in range(-(-L // g)):
         last = min((m + 1) * g, L) - 1
