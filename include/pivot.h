@@ -179,6 +179,24 @@ pivot_status pivot_index(const pivot_problem *p, const pivot_config *cfg, const 
                          const void *k, int32_t *indices, float *scores, int32_t *candidates,
                          int32_t *candidate_counts, void *workspace, size_t workspace_bytes, void *stream);
 
+/* pivot_index without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The call allocates nothing: its scratch
+ * is a static device array of PIVOT_STATIC_SCRATCH_BYTES in the library, one
+ * per GPU (the calling thread's current device, which `stream` must belong
+ * to), held until the process ends. Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (other threads, other streams, or
+ * a stream not yet drained of an earlier call) race and must be serialised
+ * by the caller. Nothing in the scratch needs to start at any value: each
+ * call writes every scratch word it reads. A call whose scratch need
+ * (pivot_index_workspace_size) exceeds the array returns PIVOT_ERR_WORKSPACE
+ * before anything is enqueued. Contiguous keys only; timing hooks are not
+ * recorded. Outputs and errors as for pivot_index. */
+#define PIVOT_STATIC_SCRATCH_BYTES (64u << 20)
+pivot_status pivot_index_static(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                                const void *k, int32_t *indices, float *scores, int32_t *candidates,
+                                int32_t *candidate_counts, void *stream);
+
 /* Keys of a ragged and/or paged batch (batched decode with per-sequence
  * prefixes, in the page layout of a serving KV cache). The pages print no
  * batch format; this one is the library's own.

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "index_kv", "resolve_variant", "pool",
+__all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "index_kv", "index_static", "resolve_variant", "pool",
            "index_stats",
            "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
            "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "SCAN_PATHS", "DENSE_BELOW_DEFAULT",
@@ -36,7 +36,7 @@ _lib = None
 
 EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
             "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
-            "pivot_index_kv", "pivot_index_kv_workspace_size",
+            "pivot_index_kv", "pivot_index_kv_workspace_size", "pivot_index_static",
             "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_index_stats", "pivot_timing_enable",
             "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
@@ -91,6 +91,7 @@ def load_library(path: str | None = None):
     lib.pivot_resolve_variant.argtypes = [P, C, ctypes.POINTER(i32)]
     lib.pivot_index_workspace_size.argtypes = [P, C, ctypes.POINTER(sz)]
     lib.pivot_index.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pivot_index_static.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp]
     KP = ctypes.POINTER(Keys)
     lib.pivot_index_kv.argtypes = [P, C, vp, vp, KP, vp, vp, vp, vp, vp, sz, vp]
     lib.pivot_index_kv_workspace_size.argtypes = [P, C, KP, ctypes.POINTER(sz)]
@@ -100,6 +101,7 @@ def load_library(path: str | None = None):
     lib.pivot_index_stats.argtypes = [ctypes.c_int64, ctypes.c_int64, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     for name in ("pivot_index_stats", "pivot_index_kv", "pivot_index_kv_workspace_size","pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "pivot_index_refine",
                  "pivot_config_init", "pivot_resolve_variant", "pivot_index_workspace_size", "pivot_index",
+                 "pivot_index_static",
                  "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pivot_timing_enable.argtypes = [i32]
@@ -307,6 +309,37 @@ def index(q, w, k, cfg: Config | None = None, *, return_scores: bool = False, re
             cand_n = torch.empty((prob.batch, G), dtype=torch.int32, device=q.device)
     _check(lib.pivot_index(ctypes.byref(prob), ctypes.byref(cfg), _ptr(q), _ptr(w), _ptr(k), _ptr(idx), _ptr(sc),
                            _ptr(cand), _ptr(cand_n), _ptr(workspace), wsb, _stream_ptr(stream, q.device)))
+    outs = [idx]
+    if return_scores:
+        outs.append(sc)
+    if return_candidates:
+        outs += [None if cand is None else _finish(sq, cand), None if cand_n is None else _finish(sq, cand_n)]
+    return _finish(sq, *outs) if len(outs) > 1 else _finish(sq, idx)
+
+
+def index_static(q, w, k, cfg: Config | None = None, *, return_scores: bool = False,
+                 return_candidates: bool = False, stream=None, **knobs):
+    """pivot_index_static: the indexer with the library's static device
+    scratch instead of a workspace (allocates nothing but the outputs made
+    here). Same arguments and results as index()."""
+    if cfg is None:
+        cfg = make_config(**knobs)
+    elif knobs:
+        raise TypeError("pass either cfg or keywords")
+    prob, q, w, k, sq = _prepare(q, w, k)
+    lib = load_library()
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    cand = cand_n = None
+    if return_candidates:
+        resolved = ctypes.c_int32(0)
+        _check(lib.pivot_resolve_variant(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(resolved)))
+        if resolved.value == REFINE:
+            G = -(-prob.lq // cfg.g)
+            cand = torch.empty((prob.batch, G, cfg.c), dtype=torch.int32, device=q.device)
+            cand_n = torch.empty((prob.batch, G), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.pivot_index_static(ctypes.byref(prob), ctypes.byref(cfg), _ptr(q), _ptr(w), _ptr(k), _ptr(idx),
+                                      _ptr(sc), _ptr(cand), _ptr(cand_n), _stream_ptr(stream, q.device)))
     outs = [idx]
     if return_scores:
         outs.append(sc)

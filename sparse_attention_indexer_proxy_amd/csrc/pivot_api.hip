@@ -13,6 +13,8 @@
 #include "pivot.h"
 #include "pivot_kernels.h"
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -25,6 +27,7 @@ struct TimedLaunch {
     hipEvent_t start, stop;
 };
 thread_local bool g_timing = false;
+thread_local bool g_timing_off = false;  // set while pivot_index_static runs (it creates no events)
 thread_local std::vector<TimedLaunch> g_timed;
 
 void forget_timing()
@@ -43,7 +46,7 @@ struct StageTimer {
     hipStream_t stream;
     StageTimer(int stage, hipStream_t s) : stream(s)
     {
-        if (!g_timing) return;
+        if (!g_timing || g_timing_off) return;
         rec.stage = stage;
         if (hipEventCreate(&rec.start) != hipSuccess) return;
         if (hipEventCreate(&rec.stop) != hipSuccess) {
@@ -616,6 +619,71 @@ pivot_status pivot_index_kv(const pivot_problem *p, const pivot_config *cfg, con
     st = check_keys(p, keys, &kin);
     if (st != PIVOT_OK) return st;
     return run(p, c, q, w, kin, indices, scores, candidates, candidate_counts, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free entry
+// The scratch of pivot_index_static: one array per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// device array; its device address comes from hipGetSymbolAddress, looked up
+// once per device (with that device current) and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[PIVOT_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+pivot_status static_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(PIVOT_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+            if (!ptr) return fail(PIVOT_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return PIVOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pivot_status pivot_index_static(const pivot_problem *p, const pivot_config *cfg, const void *q, const float *w,
+                                const void *k, int32_t *indices, float *scores, int32_t *candidates,
+                                int32_t *candidate_counts, void *stream)
+{
+    Cfg c;
+    pivot_status st = resolve(p, cfg, &c);
+    if (st != PIVOT_OK) return st;
+    Layout L;
+    st = plan(p, c, false, &L);
+    if (st != PIVOT_OK) return st;
+    if (L.total > PIVOT_STATIC_SCRATCH_BYTES)
+        return fail(PIVOT_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; pivot_index_static holds %zu (use pivot_index with a "
+                    "workspace)",
+                    L.total, static_cast<size_t>(PIVOT_STATIC_SCRATCH_BYTES));
+    void *ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != PIVOT_OK) return st;
+    g_timing_off = true;
+    st = run(p, c, q, w, contiguous(k), indices, scores, candidates, candidate_counts, ws,
+             PIVOT_STATIC_SCRATCH_BYTES, stream);
+    g_timing_off = false;
+    return st;
 }
 
 pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32_t *indices, const float *scores,
