@@ -65,6 +65,8 @@ def load(path: str | None = None):
     lib.oracle_proxy_row.restype = ctypes.c_int
     lib.oracle_proxy_row2.argtypes = [P, i32, i32, vp, vp, vp, i64, i64, vp]
     lib.oracle_proxy_row2.restype = ctypes.c_int
+    lib.oracle_scores_at.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, i64, vp, i64, vp]
+    lib.oracle_scores_at.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
@@ -188,4 +190,23 @@ def proxy_row(q, w, k, g, b, m, lib_path=None, agg="mean"):
                                           _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_proxy_row failed with code {rc}")
+    return out
+
+
+def scores_at(q, w, k, units, pos, g=None, lib_path=None, agg="mean"):
+    """Scores of chosen units at chosen key positions, with the oracle's own
+    fp32 arithmetic: eq. (1) of query rows (g None; units are flat rows
+    b*Lq + r) or eq. (5) of group proxies (g given; units are flat groups
+    b*G + m). ``pos`` [len(units), P] int key positions (negative: skipped);
+    returns float32 [len(units), P], NaN at skipped positions."""
+    q, w, k = _c(q), _c(w), _c(k)
+    prob = _problem(q, w, k)
+    u = np.ascontiguousarray(units, dtype=np.int64).reshape(-1)
+    p = np.ascontiguousarray(pos, dtype=np.int32).reshape(len(u), -1)
+    out = np.empty(p.shape, dtype=np.float32)
+    rc = load(lib_path).oracle_scores_at(ctypes.byref(prob), 0 if g is None else 1, 1 if g is None else g,
+                                         _agg(agg), _ptr(q), _ptr(w), _ptr(k), _ptr(u), len(u), _ptr(p),
+                                         p.shape[1], _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_scores_at failed with code {rc}")
     return out

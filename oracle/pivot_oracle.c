@@ -443,6 +443,64 @@ int oracle_run(const oracle_problem *p, int32_t variant, int32_t g, int32_t topk
                        cand_in, cand_in_n, counters);
 }
 
+/* ------------------------------------------ scores at chosen positions */
+/*
+ * oracle_scores_at: eq. (1) scores of chosen query rows (proxy = 0; unit =
+ * flat row b*Lq + r, scored with its own q and w) or eq. (5) scores of
+ * chosen group proxies (proxy = 1; unit = flat group b*G + m, its proxy from
+ * g and agg as in oracle_run2), at chosen key positions:
+ *   out[i * npos + j] = score of units[i] at key pos[i * npos + j],
+ * NaN where that position is negative or not below Lk. No causal bound is
+ * applied: this is the score function itself, for checking the scores (and
+ * the near-boundary positions) another implementation selected.
+ */
+int oracle_scores_at(const oracle_problem *p, int32_t proxy, int32_t g, int32_t agg, const void *q, const float *w,
+                     const void *k, const int64_t *units, int64_t n_units, const int32_t *pos, int64_t npos,
+                     float *out)
+{
+    if (!check_problem(p) || !q || !w || !k || !units || !pos || !out || n_units < 0 || npos < 0) return OR_BAD_ARG;
+    if (proxy != 0 && proxy != 1) return OR_BAD_ARG;
+    if (proxy && (g < 1 || agg < AGG_MEAN || agg > AGG_LAST)) return OR_BAD_ARG;
+    const int64_t per_seq = proxy ? n_groups(p, g) : p->Lq;
+    for (int64_t u = 0; u < n_units; ++u)
+        if (units[u] < 0 || units[u] >= p->B * per_seq) return OR_BAD_ARG;
+    const int64_t hd = (int64_t)p->H * p->d;
+    int rc = OR_OK;
+#pragma omp parallel
+    {
+        float *qv = malloc(sizeof(float) * (size_t)hd);
+        float *wv = malloc(sizeof(float) * (size_t)p->H);
+        float *ks = malloc(sizeof(float) * (size_t)p->d);
+        int local_ok = qv && wv && ks;
+        if (!local_ok) {
+#pragma omp atomic write
+            rc = OR_NO_MEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < n_units; ++u) {
+            if (!local_ok) continue;
+            const int64_t b = units[u] / per_seq, local = units[u] % per_seq;
+            if (proxy)
+                proxy_of_group(p, g, agg, q, w, b, local, qv, wv);
+            else
+                widen_query_row(p, q, w, b, local, qv, wv);
+            for (int64_t j = 0; j < npos; ++j) {
+                const int64_t s = pos[u * npos + j];
+                if (s < 0 || s >= p->Lk) {
+                    out[u * npos + j] = NAN;
+                    continue;
+                }
+                for (int i = 0; i < p->d; ++i) ks[i] = widen(k, p->dtype, (b * p->Lk + s) * p->d + i);
+                out[u * npos + j] = index_score(p->H, p->d, qv, wv, ks);
+            }
+        }
+        free(qv);
+        free(wv);
+        free(ks);
+    }
+    return rc;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

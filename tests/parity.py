@@ -88,60 +88,110 @@ def member_scores(q, w, k, b, r, positions):
     return (w[b, r].astype(np.float64)[:, None] * np.maximum(qv @ kv.T, 0.0)).sum(axis=0)
 
 
-def check_refine_groups(q, w, k, g, topk, c, gpu_idx, gpu_sc, gpu_C, gpu_n, groups):
-    """Float rule on sampled Refine groups: candidate sets against the oracle's
-    proxy scores, member rows against the oracle's member step run on the
-    GPU's own candidate sets. Returns the total symmetric-difference size."""
+def _padded(lists, fill=-1):
+    n = max([len(x) for x in lists] + [1])
+    out = np.full((len(lists), n), fill, dtype=np.int32)
+    for i, x in enumerate(lists):
+        out[i, :len(x)] = x
+    return out
+
+
+def check_rows(q, w, k, units, gpu_idx, gpu_sc, ref_idx, ref_sc, what, g=None):
+    """The float rule on many rows at once. Row i belongs to ``units[i]`` (a
+    flat query row for eq. (1) scores, or, with g, a flat group whose proxy
+    scores (eq. (5)) judge the row). gpu_* and ref_* are [n, K] (ref: the
+    oracle's rows for the same units). Every GPU score must be within RTOL of
+    the oracle's score of the same position (oracle.scores_at), and every
+    position in the symmetric difference of the two sets within the
+    tolerance of the reference boundary. Returns the total difference size."""
+    import oracle
+    n, K = gpu_idx.shape
+    gv, rv = gpu_idx >= 0, ref_idx >= 0
+    ng, nr = gv.sum(axis=1), rv.sum(axis=1)
+    bad = np.flatnonzero(ng != nr)
+    assert not len(bad), f"{what}: valid counts differ at rows {bad[:5]}: {ng[bad[:5]]} vs {nr[bad[:5]]}"
+    assert np.array_equal(gv, np.arange(K)[None, :] < ng[:, None]), f"{what}: -1 not only in the tail"
+    assert np.all(np.diff(gpu_idx, axis=1)[gv[:, 1:]] > 0), f"{what}: valid entries not strictly ascending"
+    rs = np.where(rv, ref_sc, np.nan).astype(np.float64)
+    has = nr > 0
+    boundary = np.where(has, np.nanmin(np.where(has[:, None], rs, 0.0), axis=1), 0.0)
+    row_max = np.where(has, np.nanmax(np.where(has[:, None], rs, 0.0), axis=1), 0.0)
+    t = RTOL * np.abs(boundary) + ATOL_FRAC * np.abs(row_max) + 1e-30
+    if gpu_sc is not None:
+        exp = oracle.scores_at(q, w, k, units, np.where(gv, gpu_idx, -1), g=g).astype(np.float64)
+        err = np.abs(gpu_sc.astype(np.float64) - exp)
+        lim = RTOL * np.abs(exp) + ATOL_FRAC * np.abs(row_max)[:, None] + 1e-30
+        badm = gv & ~(err <= lim)
+        if badm.any():
+            i, j = np.argwhere(badm)[0]
+            raise AssertionError(f"{what}: score mismatch in row {i} (unit {units[i]}) at position "
+                                 f"{gpu_idx[i, j]}: gpu {gpu_sc[i, j]} oracle {exp[i, j]}")
+    diffs = [np.setxor1d(gpu_idx[i, :ng[i]], ref_idx[i, :nr[i]]) for i in range(n)]
+    total = int(sum(len(d) for d in diffs))
+    if total:
+        D = _padded(diffs)
+        ds = oracle.scores_at(q, w, k, units, D, g=g).astype(np.float64)
+        far = (D >= 0) & (np.abs(ds - boundary[:, None]) > t[:, None])
+        if far.any():
+            i, j = np.argwhere(far)[0]
+            raise AssertionError(f"{what}: row {i} (unit {units[i]}) position {D[i, j]} differs from the oracle's "
+                                 f"set with score {ds[i, j]} vs boundary {boundary[i]}")
+    return total
+
+
+def check_refine_groups(q, w, k, g, topk, c, gpu_idx, gpu_sc, gpu_C, gpu_n, groups=None):
+    """The float rule on Refine groups (all of them when ``groups`` is None):
+    candidate sets against the oracle's proxy scores (eq. (7) at the
+    boundary only), member rows against the oracle's member step (eqs.
+    (8)-(9)) run on the GPU's own candidate sets. Returns the total
+    symmetric-difference size."""
     import oracle
     B, Lq = q.shape[:2]
-    Lk = k.shape[1]
     G = -(-Lq // g)
-    ref = oracle.refine(q, w, k, g, topk, c, groups=groups)
+    groups = np.arange(B * G) if groups is None else np.asarray(groups, dtype=np.int64)
+    ref = oracle.refine(q, w, k, g, topk, c, groups=groups, want_scores=False)
     given = oracle.refine(q, w, k, g, topk, c, groups=groups, cand_in=gpu_C, cand_in_n=gpu_n)
-    diffs = 0
-    for u in groups:
-        b, m = divmod(int(u), G)
-        prow = oracle.proxy_row(q, w, k, g, b, m)
-        n = gpu_n[b, m]
-        diffs += check_candidates(gpu_C[b, m, :n], ref["cand"][b, m, :ref["cand_n"][b, m]], prow,
-                                  f"C of group {b}/{m}")
-        for r in range(m * g, min((m + 1) * g, Lq)):
-            diffs += compare_row(gpu_idx[b, r], None if gpu_sc is None else gpu_sc[b, r],
-                                 given["indices"][b, r], given["scores"][b, r],
-                                 lambda p, b=b, r=r: member_scores(q, w, k, b, r, p), f"refine row {b}/{r}")
+    b_, m_ = np.divmod(groups, G)
+    gC, rC = gpu_C[b_, m_], ref["cand"][b_, m_]
+    # eq. (7): the candidate sets as top-c sets of the proxy scores (the
+    # oracle's own proxy scores of its C give the boundary)
+    rsc = oracle.scores_at(q, w, k, groups, np.where(rC >= 0, rC, -1), g=g)
+    diffs = check_rows(q, w, k, groups, gC, None, rC, rsc, "C", g=g)
+    # eqs. (8)-(9): member rows on the GPU's C
+    rows = np.concatenate([b * Lq + np.arange(m * g, min((m + 1) * g, Lq)) for b, m in zip(b_, m_)])
+    rb, rr = np.divmod(rows, Lq)
+    diffs += check_rows(q, w, k, rows, gpu_idx[rb, rr], None if gpu_sc is None else gpu_sc[rb, rr],
+                        given["indices"][rb, rr], given["scores"][rb, rr], "refine rows")
     return diffs
 
 
-def check_reuse_groups(q, w, k, g, topk, gpu_idx, gpu_sc, groups):
+def check_reuse_groups(q, w, k, g, topk, gpu_idx, gpu_sc, groups=None):
+    """The float rule on Reuse groups (all when ``groups`` is None): each
+    group's row against the oracle's eq. (6) row by the proxy scores; every
+    member row must equal its group's first."""
     import oracle
     B, Lq = q.shape[:2]
     G = -(-Lq // g)
+    groups = np.arange(B * G) if groups is None else np.asarray(groups, dtype=np.int64)
     ref = oracle.reuse(q, w, k, g, topk, groups=groups)
-    diffs = 0
-    for u in groups:
-        b, m = divmod(int(u), G)
-        prow = oracle.proxy_row(q, w, k, g, b, m).astype(np.float64)
-        r0 = m * g
-        diffs += compare_row(gpu_idx[b, r0], None if gpu_sc is None else gpu_sc[b, r0], ref["indices"][b, r0],
-                             ref["scores"][b, r0], lambda p: prow[p], f"reuse group {b}/{m}")
-        rows = gpu_idx[b, r0:min(r0 + g, Lq)]
-        assert np.all(rows == rows[0]), f"reuse group {b}/{m}: member rows differ"
-    return diffs
+    b_, m_ = np.divmod(groups, G)
+    r0 = m_ * g
+    for j in range(1, g):
+        r = np.minimum(r0 + j, Lq - 1)
+        assert np.array_equal(gpu_idx[b_, r], gpu_idx[b_, r0]), "reuse: member rows differ within a group"
+    return check_rows(q, w, k, groups, gpu_idx[b_, r0], None if gpu_sc is None else gpu_sc[b_, r0],
+                      ref["indices"][b_, r0], ref["scores"][b_, r0], "reuse groups", g=g)
 
 
-def check_dense_rows(q, w, k, topk, gpu_idx, gpu_sc, rows):
+def check_dense_rows(q, w, k, topk, gpu_idx, gpu_sc, rows=None):
+    """The float rule on dense rows (all when ``rows`` is None; flat b*Lq+r)."""
     import oracle
     B, Lq = q.shape[:2]
-    Lk = k.shape[1]
+    rows = np.arange(B * Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     ref = oracle.dense(q, w, k, topk, rows=rows)
-    diffs = 0
-    for u in rows:
-        b, r = divmod(int(u), Lq)
-        t = Lk - Lq + r
-        diffs += compare_row(gpu_idx[b, r], None if gpu_sc is None else gpu_sc[b, r], ref["indices"][b, r],
-                             ref["scores"][b, r], lambda p, b=b, r=r: member_scores(q, w, k, b, r, p),
-                             f"dense row {b}/{r}")
-    return diffs
+    rb, rr = np.divmod(rows, Lq)
+    return check_rows(q, w, k, rows, gpu_idx[rb, rr], None if gpu_sc is None else gpu_sc[rb, rr],
+                      ref["indices"][rb, rr], ref["scores"][rb, rr], "dense rows")
 
 
 def structure_all_rows(idx, Lq, Lk, topk, g=None, counts=None):

@@ -2,15 +2,22 @@
 configuration the benchmark times.
 
   exact_prefill_L8192   bit for bit with the oracle (every sum is exact):
-                        Reuse and Refine on every group, dense on sampled rows
-  prefill_L32768        float rule on sampled groups/rows + every-row structure
-  prefill_L131072       Refine and Reuse for g in {4, 8, 16} and dense (g = 1),
-                        float rule on sampled groups/rows + every-row structure
-  mtp_decode            Refine, float rule on every group (32 sequences)
+                        Reuse, Refine and dense on every group / row
+  prefill_L32768        float rule on every group (Refine, Reuse) and every
+                        row (dense) + every-row structure
+  prefill_L131072       Refine and Reuse for g in {4, 8, 16} and dense (g = 1):
+                        float rule on 512 evenly spaced groups for Refine g=8,
+                        on sampled groups/rows otherwise + every-row structure;
+                        repeated calls bit-identical
+  mtp_decode            Refine, float rule on every group (32 sequences);
+                        repeated calls bit-identical
   mtp_decode_ragged     Refine over ragged lengths and 64-key pages (the
                         benchmark's layout), float rule on every sequence
                         against the oracle run on that sequence's own prefix
   tiny_prefill_L512     covered bit for bit in test_gpu_parity.py
+
+The float rule (tests/parity.py) scores the GPU's selected positions with
+the oracle's own fp32 arithmetic (oracle.scores_at).
 """
 import numpy as np
 import pytest
@@ -79,10 +86,10 @@ def test_exact_workload_dense_bitwise(exact_data):
     d_i, d_s = _np(d_i), _np(d_s)
     parity.structure_all_rows(d_i, W.Lq, W.Lk, W.topk,
                               counts=np.minimum(W.topk, np.arange(W.Lq) + 1)[None])
-    rows = np.unique(np.r_[0:300, 4090:4100, np.linspace(0, W.Lq - 1, 200).astype(np.int64), W.Lq - 64:W.Lq])
-    ref = oracle.dense(q, w, k, W.topk, rows=rows)
-    np.testing.assert_array_equal(d_i[0, rows], ref["indices"][0, rows])
-    np.testing.assert_array_equal(d_s[0, rows], ref["scores"][0, rows])
+    _say("[exact] oracle dense, every row")
+    ref = oracle.dense(q, w, k, W.topk)
+    np.testing.assert_array_equal(d_i, ref["indices"])
+    np.testing.assert_array_equal(d_s, ref["scores"])
 
 
 # ------------------------------------------------------------ float prefill
@@ -107,7 +114,7 @@ def _refine_case(data, W, g, n_groups):
     tl = np.minimum((np.arange(G) + 1) * g, W.Lq) - 1
     np.testing.assert_array_equal(f_n[0], np.minimum(W.c, tl + 1))
     parity.structure_all_rows(f_i, W.Lq, W.Lk, W.topk)
-    groups = _sample_groups(G, n_groups)
+    groups = np.arange(G) if n_groups is None else _sample_groups(G, n_groups)
     d = parity.check_refine_groups(q, w, k, g, W.topk, W.c, f_i, f_s, f_c, f_n, groups)
     _say(f"[{W.name} refine g={g}] {len(groups)} groups checked, {d} boundary swaps")
 
@@ -121,7 +128,7 @@ def _reuse_case(data, W, g, n_groups):
     tl = np.minimum((np.arange(G) + 1) * g, W.Lq) - 1
     parity.structure_all_rows(r_i, W.Lq, W.Lk, W.topk, g=g,
                               counts=np.minimum(W.topk, tl[np.arange(W.Lq) // g] + 1)[None])
-    groups = _sample_groups(G, n_groups)
+    groups = np.arange(G) if n_groups is None else _sample_groups(G, n_groups)
     d = parity.check_reuse_groups(q, w, k, g, W.topk, r_i, r_s, groups)
     _say(f"[{W.name} reuse g={g}] {len(groups)} groups checked, {d} boundary swaps")
 
@@ -132,26 +139,39 @@ def _dense_case(data, W, n_rows):
     torch.cuda.synchronize()
     d_i, d_s = _np(d_i), _np(d_s)
     parity.structure_all_rows(d_i, W.Lq, W.Lk, W.topk, counts=np.minimum(W.topk, np.arange(W.Lq) + 1)[None])
-    rows = np.unique(np.r_[0, 1, 2047, 2048, 2049, np.linspace(0, W.Lq - 1, n_rows).astype(np.int64), W.Lq - 1])
+    rows = (np.arange(W.Lq) if n_rows is None else
+            np.unique(np.r_[0, 1, 2047, 2048, 2049, np.linspace(0, W.Lq - 1, n_rows).astype(np.int64), W.Lq - 1]))
     d = parity.check_dense_rows(q, w, k, W.topk, d_i, d_s, rows)
     _say(f"[{W.name} dense] {len(rows)} rows checked, {d} boundary swaps")
 
 
 def test_prefill_32k_refine(prefill32k):
-    _refine_case(prefill32k, PREFILL_32K, PREFILL_32K.g, 24)
+    _refine_case(prefill32k, PREFILL_32K, PREFILL_32K.g, None)
 
 
 def test_prefill_32k_reuse(prefill32k):
-    _reuse_case(prefill32k, PREFILL_32K, PREFILL_32K.g, 24)
+    _reuse_case(prefill32k, PREFILL_32K, PREFILL_32K.g, None)
 
 
 def test_prefill_32k_dense(prefill32k):
-    _dense_case(prefill32k, PREFILL_32K, 12)
+    _dense_case(prefill32k, PREFILL_32K, None)
 
 
 @pytest.mark.parametrize("g", [8, 4, 16])
 def test_long_128k_refine(prefill128k, g):
-    _refine_case(prefill128k, LONG_128K, g, 10)
+    _refine_case(prefill128k, LONG_128K, g, 512 if g == 8 else 10)
+
+
+def test_long_128k_repeat_calls_are_bit_identical(prefill128k):
+    """Refine g=8 at full size twice (the fused scan, the group and member
+    selects): indices, scores and candidate sets identical bit for bit."""
+    _, _, _, (tq, tw, tk) = prefill128k
+    W = LONG_128K
+    a = pv.index_refine(tq, tw, tk, W.g, W.topk, W.c, return_scores=True, return_candidates=True)
+    b = pv.index_refine(tq, tw, tk, W.g, W.topk, W.c, return_scores=True, return_candidates=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("g", [8, 4, 16])
@@ -175,6 +195,10 @@ def test_mtp_decode_refine_every_group():
     parity.structure_all_rows(f_i, W.Lq, W.Lk, W.topk)
     d = parity.check_refine_groups(q, w, k, W.g, W.topk, W.c, f_i, f_s, f_c, f_n, np.arange(W.B))
     _say(f"[decode] {W.B} groups checked, {d} boundary swaps")
+    again = pv.index_refine(tq, tw, tk, W.g, W.topk, W.c, return_scores=True, return_candidates=True)
+    torch.cuda.synchronize()
+    for x, y in zip((f_i, f_s, f_c, f_n), again):
+        np.testing.assert_array_equal(x, _np(y))
 
 
 def test_mtp_decode_ragged_paged_refine_every_sequence():

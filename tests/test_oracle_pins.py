@@ -317,3 +317,54 @@ def test_rejects_bad_arguments():
         oracle.dense(q, w, k[:, :4], 3)       # Lq > Lk
     with pytest.raises(ValueError):
         oracle.dense(q, w, k, 3, rows=[100])  # unit out of range
+
+
+@pytest.mark.parametrize("case", [c for c in EXACT_CASES if _pow2_groups(c[1], c[5])])
+def test_scores_at_equal_the_brute_force_score_matrices(case):
+    """oracle.scores_at (eq. (1) rows and eq. (5) proxies at chosen key
+    positions, used by the full-size GPU checks) against the float64 brute
+    force's whole matrices, on inputs where every sum is exact: bit for bit,
+    every sequence, every row / group, shuffled positions with gaps."""
+    B, Lq, Lk, H, d, g, topk, c, dt = case
+    q, w, k = _exact(case, seed=5)
+    kv = brute._f64(k, dt)
+    r = np.random.default_rng(9)
+    P = min(Lk, 7)
+    rows = np.arange(B * Lq)
+    pos = np.stack([r.permutation(Lk)[:P] for _ in rows]).astype(np.int32)
+    pos[:, -1] = -1                                   # skipped slot
+    got = oracle.scores_at(q, w, k, rows, pos)
+    qf = brute._f64(q, dt)
+    for u in rows:
+        b, t = divmod(int(u), Lq)
+        ref = brute.score_matrix(qf[b, t][None], np.asarray(w[b, t], np.float64)[None], kv[b])[0]
+        np.testing.assert_array_equal(got[u, :-1].astype(np.float64), ref[pos[u, :-1]])
+        assert np.isnan(got[u, -1])
+    qbar, wbar = brute.proxy(q, w, g, dt)
+    G = -(-Lq // g)
+    groups = np.arange(B * G)[::-1]                   # any order
+    gpos = np.stack([r.permutation(Lk)[:P] for _ in groups]).astype(np.int32)
+    got = oracle.scores_at(q, w, k, groups, gpos, g=g)
+    for i, u in enumerate(groups):
+        b, m = divmod(int(u), G)
+        ref = brute.score_matrix(qbar[b, m][None], wbar[b, m][None], kv[b])[0]
+        np.testing.assert_array_equal(got[i].astype(np.float64), ref[gpos[i]])
+
+
+def test_scores_at_agrees_with_the_oracle_rows_on_float_inputs():
+    """On Gaussian inputs the selected entries of the oracle's own dense and
+    Refine rows carry exactly the scores scores_at gives for them."""
+    q, w, k = gauss_random(4, 2, 50, 60, 3, 8, BF16)
+    d = oracle.dense(q, w, k, 6)
+    rows = np.arange(2 * 50)
+    got = oracle.scores_at(q, w, k, rows, d["indices"].reshape(100, 6))
+    ok = d["indices"].reshape(100, 6) >= 0
+    np.testing.assert_array_equal(got[ok], d["scores"].reshape(100, 6)[ok])
+    rf = oracle.refine(q, w, k, 4, 5, 9)
+    G = 13
+    gp = oracle.scores_at(q, w, k, np.arange(2 * G), rf["cand"].reshape(2 * G, 9), g=4)
+    for u in range(2 * G):
+        b, m = divmod(u, G)
+        n = rf["cand_n"][b, m]
+        row = oracle.proxy_row(q, w, k, 4, b, m)
+        np.testing.assert_array_equal(gp[u, :n], row[rf["cand"][b, m, :n]])
