@@ -77,7 +77,9 @@ pivot_status fail(pivot_status s, const char *fmt, ...)
 }
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kMaxSel = int64_t(1) << 28;  // bound on topk and c (keeps buffer indices in int32)
+// bound on topk and c: keeps a group's survivor buffer (2 cap words, cap <=
+// 2 K) addressable by one 32-bit buffer resource and its indices in int32
+constexpr int64_t kMaxSel = int64_t(1) << 27;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -118,7 +120,7 @@ struct Layout {
     bool pool;
     bool few;               // few groups: split scan into score rows + block selects
     int scan_splits, refine_splits;
-    size_t qbar, wbar, buf, buf_n, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
+    size_t qbar, wbar, buf, buf_n, smp, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
@@ -202,10 +204,10 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
     const int variant = cfg.variant;
     const int32_t g = cfg.g, topk = cfg.topk, c = cfg.c;
     if (g < 1) return fail(PIVOT_ERR_INVALID_ARG, "group size g must be >= 1 (got %d)", g);
-    if (topk < 1 || topk > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "topk must be in [1, 2^28] (got %d)", topk);
+    if (topk < 1 || topk > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "topk must be in [1, 2^27] (got %d)", topk);
     if (variant == PIVOT_REFINE) {
         if (c < topk) return fail(PIVOT_ERR_INVALID_ARG, "refine needs c >= topk (c=%d, topk=%d)", c, topk);
-        if (c > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "c must be <= 2^28");
+        if (c > kMaxSel) return fail(PIVOT_ERR_INVALID_ARG, "c must be <= 2^27");
     }
     const pivot::LaunchShape sh = shape_of(p);
     if (variant == PIVOT_REFINE && pivot::mfma_shape(sh) && g > 1024)
@@ -259,6 +261,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
         l.scan_splits = l.refine_splits = 1;
         l.buf = take(groups * 2 * cap * sizeof(float));
         l.buf_n = take(groups * sizeof(int32_t));
+        if (pivot::mfma_shape(sh)) l.smp = take(groups * static_cast<size_t>(pivot::scan_sample_slots()) * sizeof(float));
     }
     if (variant == PIVOT_REFINE || cfg.causal) {
         l.cand = take(groups * static_cast<size_t>(l.K) * sizeof(int32_t));
@@ -364,6 +367,7 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     sl.cap = L.cap;
     sl.buf = L.few ? nullptr : reinterpret_cast<float *>(base + L.buf);
     sl.buf_n = L.few ? nullptr : reinterpret_cast<int32_t *>(base + L.buf_n);
+    sl.smp = (L.few || !pivot::mfma_shape(sh)) ? nullptr : reinterpret_cast<float *>(base + L.smp);
     if (to_cand) {
         sl.out_idx = cand;
         sl.out_sc = cand_sc;

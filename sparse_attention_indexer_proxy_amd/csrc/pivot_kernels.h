@@ -48,6 +48,7 @@ struct ScanLaunch {
     int K, cap;         // selection size and per-group buffer capacity
     float *buf;         // [B*G, 2*cap]: cap scores then cap int32 positions per group
     int32_t *buf_n;     // [B*G] buffered entries (MFMA shape, selection mode)
+    float *smp;         // [B*G, scan_sample_slots()] sampled scores (MFMA shape, selection mode)
     int32_t *out_idx;   // rows [B, Lq, stride] or candidates [B, G, stride]
     float *out_sc;      // rows only, nullable
     int32_t *out_count; // candidates only, nullable
@@ -127,6 +128,8 @@ int stats_row_max();    // largest row width k
 int stats_group_fits(int g, int k);
 
 bool mfma_shape(const LaunchShape &sh);
+// Sampled scores the fused scan keeps per group (its workspace share).
+int scan_sample_slots();
 // agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st);

@@ -426,7 +426,8 @@ template <class F> __device__ int wave_emit(const float *sc, const int32_t *pos,
 // ------------------------------------------------- per-group filter state
 struct Filter {
     float *bs;    // buffered scores (wave-private, ascending position)
-    int32_t *bi;  // buffered positions
+    int32_t *bi;  // buffered positions (bs + cap)
+    __amdgpu_buffer_rsrc_t rs;  // bs as one raw buffer of 2 cap words (appends: one offset per lane)
     int cap;      // buffer capacity (>= K + 64)
     int K;        // entries to keep
     int cnt;      // buffered entries (wave-uniform)
@@ -448,11 +449,20 @@ struct Filter {
             n = popc(pm);
         }
         if (pass) {
+            // score at byte 4 slot, position at byte 4 (cap + slot)
             const int slot = cnt + mbcnt(pm);
-            bs[slot] = score;
-            bi[slot] = pos;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), rs, slot * 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(pos), rs, slot * 4, cap * 4, 0);
         }
         cnt = __builtin_amdgcn_readfirstlane(cnt + n);
+    }
+
+    __device__ __forceinline__ void set_buffer(float *base, int capacity)
+    {
+        bs = base;
+        bi = reinterpret_cast<int32_t *>(base + capacity);
+        cap = capacity;
+        rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<uint32_t>(capacity) * 8u, 0x00020000);
     }
 
     // Keep exactly the best K buffered entries, in order; tau := K-th score.
@@ -622,6 +632,7 @@ struct ScanArgs {
     int K, cap;
     float *buf_s;     // [B*G][2*cap]: cap scores, then cap positions (int32)
     int32_t *buf_n;   // [B*G] entries buffered (MFMA scan; k_select_groups selects them)
+    float *smp;       // [B*G][kSampleSlots] sampled scores (MFMA scan)
     SelectionOut out; // exact-order scan: selected in-kernel
     // kRows
     float *rows;  // [B, G, Lk]
@@ -799,6 +810,7 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
 // so the selection is exact whatever the sample shows.
 constexpr int kSampleStride = 32;     // tiles between sampled tiles (>= this)
 constexpr float kSampleSigmas = 6.0f;
+constexpr int kSampleSlots = 4096;    // sampled scores kept per group (16 tiles of 256 keys)
 
 // Fused-scan workgroup shape: kScanWaves groups (one per wave) share each
 // 256-key tile (64 KiB); kScanBufs tiles are in LDS or in flight at once.
@@ -826,18 +838,17 @@ static_assert(kScanBufs == 2 || kScanBufs == 3, "two or three tile buffers");
 // buffer resource of the bytes that exist, so rows past lk read as zero
 // (their scores are masked) and each 1 KiB slice is one LDS DMA instruction
 // on the lane's fixed byte offset voff[j]; slice j lands at dst + 512 j.
-constexpr int kDmaSlices = kScanTileKeys * 256 / 1024 / kScanWaves;  // 1 KiB slices per wave per tile
-__device__ __forceinline__ void dma_key_tile(const uint16_t *kseq, int64_t base, int64_t lk, uint16_t *dst,
-                                             const uint32_t *voff)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_tile_rsrc(const uint16_t *kseq, int64_t base, int64_t lk)
 {
-    constexpr int NT = kScanTileKeys, D = 128, SLICES = kDmaSlices;
+    constexpr int NT = kScanTileKeys, D = 128;
     const int64_t rows_left = lk - base;
     const uint32_t nbytes = static_cast<uint32_t>(rows_left < NT ? rows_left : NT) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kseq + base * D), 0, nbytes, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < SLICES; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + j * 512), 16, voff[j], 0, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kseq + base * D), 0, nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma_key_slice(__amdgpu_buffer_rsrc_t rs, uint16_t *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, voff, 0, 0, 0);
 }
 
 // Workgroup barrier without a memory fence. LDS tiles are written only by
@@ -903,10 +914,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     f.cnt = 0;
     f.tau = -INFINITY;
     f.hist = hist[wv];
-    if (Mode == kFilter) {
-        f.bs = a.buf_s + gid * 2 * static_cast<int64_t>(a.cap);  // [cap scores | cap positions]
-        f.bi = reinterpret_cast<int32_t *>(f.bs + a.cap);
-    }
+    if (Mode == kFilter) f.set_buffer(a.buf_s + gid * 2 * static_cast<int64_t>(a.cap), a.cap);  // [cap scores | cap positions]
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
     // This lane's byte offset within a tile for each of its DMA slices
@@ -936,20 +944,23 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             }
         }
     };
+    // slice j (of this wave's SLICES_PER_WAVE) of the tile at `base` into
+    // tile buffer `buf`
     auto issue_tile = [&](int buf, int64_t base) {
         uint16_t *dst = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
-        if constexpr (PAGED) {
-            const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
+        const __amdgpu_buffer_rsrc_t rs = key_tile_rsrc(kseq, base, geo.Lk);
 #pragma unroll
-            for (int j = 0; j < SLICES_PER_WAVE; ++j) {
-                const int slice = wv * SLICES_PER_WAVE + j;
+        for (int j = 0; j < SLICES_PER_WAVE; ++j) {
+            const int slice = wv * SLICES_PER_WAVE + j;
+            if constexpr (PAGED) {
+                const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
                 const uint32_t s = key_of(base, j);
                 const int64_t r = a.keys.paged_row(ent[j], a.keys.page_offset(s));
                 __builtin_amdgcn_global_load_lds((global_cptr)(kbase + r * D + slice_col(slice, l)),
                                                  (lds_ptr)(dst + slice * 512), 16, 0, 0);
+            } else {
+                dma_key_slice(rs, dst + slice * 512, slice_voff[j]);
             }
-        } else {
-            dma_key_tile(kseq, base, geo.Lk, dst + wv * SLICES_PER_WAVE * 512, slice_voff);
         }
     };
 
@@ -959,7 +970,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
     int stride = 1;
     int nsv = 0;          // valid sampled keys (phase Sample)
     bool redo = false;    // phase Redo: this wave repeats its selection
-    float *smp = f.bs;    // sample slots (phase Sample; the buffer is empty then)
+    // the group's sampled scores (phase Sample), kept for the filter pass
+    float *smp = Mode == kFilter ? a.smp + gid * static_cast<int64_t>(kSampleSlots) : nullptr;
     auto on_score = [&](int phase, int it, int quarter, int64_t base, float score) {
         const int64_t s = base + l;
         // lanes at or below lim hold keys s <= t_last (wave-uniform; positions
@@ -977,14 +989,36 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             if (redo) f.push(valid, score, static_cast<int32_t>(s));
         }
     };
-    auto pass = [&](int phase, int step) {
-        const int nt = (ntiles - 1) / step + 1;  // tiles 0, step, 2 step, ...
-        const int64_t tstep = static_cast<int64_t>(step) * NT;
-        load_entries(0);
-        issue_tile(0, 0);
-        if (PAGED && nt > 1) load_entries(tstep);
+    // A pass computes tiles tile_of(i), i < nt, in ascending order: every
+    // step-th tile (step > 1: the sample), or, with skip > 0 (the filter
+    // pass after a sample of every skip-th tile), every tile except the
+    // sampled ones, whose scores were stored by the sample pass and are
+    // handed to on_score in their place (so the per-score work still sees
+    // every tile in position order). Sampled tiles are isolated (skip >= 2).
+    auto pass = [&](int phase, int step, int skip) {
+        auto tile_of = [&](int i) { return skip ? i + i / (skip - 1) + 1 : i * step; };
+        const int nt = skip ? ntiles - ((ntiles - 1) / skip + 1) : (ntiles - 1) / step + 1;
+        float gapv[NQ];  // a sampled tile's stored scores, loaded one tile before their turn
+        auto load_gap = [&](int t) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) gapv[q] = load_as<kGlobal>(smp, (t / skip) * NT + q * kWave + l);
+        };
+        auto push_gap = [&](int t) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                on_score(phase, t, q, static_cast<int64_t>(t) * NT + q * kWave, gapv[q]);
+        };
+        if (skip) {  // tile 0 is sampled
+            load_gap(0);
+            push_gap(0);
+        }
+        if (nt == 0) return;  // wave-uniform over the workgroup (ntiles is)
+        const int64_t first = static_cast<int64_t>(tile_of(0)) * NT;
+        load_entries(first);
+        issue_tile(0, first);
+        if (PAGED && nt > 1) load_entries(static_cast<int64_t>(tile_of(1)) * NT);
         if (NB == 3 && nt > 1) {
-            issue_tile(1, tstep);
+            issue_tile(1, static_cast<int64_t>(tile_of(1)) * NT);
             __builtin_amdgcn_s_waitcnt(0x0F70 | SLICES_PER_WAVE);  // tile 0 has landed, tile 1 may not
         } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -996,15 +1030,32 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) carry[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         int prev_it = 0;
+        // the carried last quarter of tile prev_it
+        auto flush = [&]() {
+            const float q4[4] = {pc[0], pc[1], pc[2], relu_weighted<RB>(carry, wr)};
+            on_score(phase, prev_it, NQ - 1, static_cast<int64_t>(prev_it) * NT + (NQ - 1) * kWave,
+                     quarter_transpose_sum(q4));
+        };
         for (int i = 0; i < nt; ++i) {
-            const int it = i * step;
+            const int it = tile_of(i);
             const int64_t base = static_cast<int64_t>(it) * NT;
+            // a stored tile between the previous computed tile and this one:
+            // finish the previous tile, then hand over the stored scores
+            // (without skip the previous tile's last quarter is carried into
+            // this tile's first block, whatever the step)
+            const bool contiguous = i > 0 && (!skip || prev_it == it - 1);
+            if (skip && i > 0 && !contiguous) {
+                flush();
+                push_gap(it - 1);
+            }
+            if (skip && it + 1 < ntiles && (it + 1) % skip == 0) load_gap(it + 1);
             // the buffer of tile i + NB - 1 held tile i - 1, which every wave
-            // finished reading before the last barrier
+            // finished reading before the last barrier (paged keys: the
+            // entries of the tile after it are then read)
             const bool ahead = i + NB - 1 < nt;
             if (ahead) {
-                issue_tile(buf == 0 ? NB - 1 : buf - 1, base + (NB - 1) * tstep);
-                if (PAGED && i + 2 < nt) load_entries(base + 2 * tstep);
+                issue_tile(buf == 0 ? NB - 1 : buf - 1, static_cast<int64_t>(tile_of(i + NB - 1)) * NT);
+                if (PAGED && i + 2 < nt) load_entries(static_cast<int64_t>(tile_of(i + 2)) * NT);
             }
             auto emit = [&](int qt, float score) {
                 if (qt < 0)
@@ -1013,11 +1064,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
                     on_score(phase, it, qt, base + qt * kWave, score);
             };
             if (buf == 0)
-                tile_step<RB, NT / 16>(afr, wr, tile0, l, carry, pc, i > 0, emit);
+                tile_step<RB, NT / 16>(afr, wr, tile0, l, carry, pc, contiguous, emit);
             else if (NB == 2 || buf == 1)
-                tile_step<RB, NT / 16>(afr, wr, tile1, l, carry, pc, i > 0, emit);
+                tile_step<RB, NT / 16>(afr, wr, tile1, l, carry, pc, contiguous, emit);
             else
-                tile_step<RB, NT / 16>(afr, wr, tile2, l, carry, pc, i > 0, emit);
+                tile_step<RB, NT / 16>(afr, wr, tile2, l, carry, pc, contiguous, emit);
             prev_it = it;
             // tile i + 1 must be in LDS; with three buffers tile i + 2's DMAs
             // may stay in flight (vector memory counts complete in issue
@@ -1029,27 +1080,25 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             tile_barrier();
             buf = buf == NB - 1 ? 0 : buf + 1;
         }
-        // the last tile's last quarter
-        const float q4[4] = {pc[0], pc[1], pc[2], relu_weighted<RB>(carry, wr)};
-        on_score(phase, prev_it, NQ - 1, static_cast<int64_t>(prev_it) * NT + (NQ - 1) * kWave,
-                 quarter_transpose_sum(q4));
+        flush();  // the last computed tile's last quarter
+        if (skip && prev_it + 1 < ntiles) push_gap(prev_it + 1);  // a stored tile after it
     };
 
     if (Mode == kRows) {
-        pass(kPhaseRows, 1);
+        pass(kPhaseRows, 1, 0);
         if (!active) return;
         for (int64_t s = static_cast<int64_t>(ntiles) * NT + l; s < geo.Lk; s += kWave) row[s] = -INFINITY;
         return;
     }
 
-    // ---- phase A: sampled threshold (the buffer is empty, use it as scratch)
+    // ---- phase A: sampled threshold, the sampled scores kept in smp
     const int64_t n_valid = my_tlast + 1;
-    const int sample_cap_tiles = (2 * a.cap) / NT;
+    const int sample_cap_tiles = kSampleSlots / NT;
     stride = kSampleStride;
     if ((ntiles + stride - 1) / stride > sample_cap_tiles) stride = (ntiles + sample_cap_tiles - 1) / sample_cap_tiles;
     const bool sample = ntiles * NT > 4 * a.K && sample_cap_tiles > 0;  // short prefixes: plain streaming
     if (sample) {
-        pass(kPhaseSample, stride);
+        pass(kPhaseSample, stride, 0);
         if (active) {
             const int nslots = ((ntiles - 1) / stride + 1) * NT;
             const float expect = static_cast<float>(a.K) * static_cast<float>(nsv) / static_cast<float>(n_valid);
@@ -1062,8 +1111,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
         }
     }
 
-    // ---- phase B: the full pass with the streaming filter
-    pass(kPhaseFilter, 1);
+    // ---- phase B: the full pass with the streaming filter (the sampled
+    // tiles' scores come from smp)
+    pass(kPhaseFilter, 1, sample ? stride : 0);
 
     // exactness guard: a group with fewer than min(K, n_valid) survivors had
     // its sampled tau set too high; the WG repeats the pass for it from -inf
@@ -1075,7 +1125,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
             f.cnt = 0;
             f.tau = -INFINITY;
         }
-        pass(kPhaseRedo, 1);
+        pass(kPhaseRedo, 1, 0);
     }
 
     // the group's survivors (ascending position, at least min(K, n_valid)
@@ -2351,9 +2401,7 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectA
     const int n = a.cnt[gid];
     if (NV == 0) {
         Filter f;
-        f.bs = const_cast<float *>(bs);
-        f.bi = const_cast<int32_t *>(bi);
-        f.cap = a.cap;
+        f.set_buffer(const_cast<float *>(bs), a.cap);
         f.K = a.K;
         f.cnt = n;
         f.tau = -INFINITY;
@@ -2444,10 +2492,7 @@ __global__ __launch_bounds__(256) void k_scan_exact(ScanArgs a)
     f.cnt = 0;
     f.tau = -INFINITY;
     f.hist = hist[wv];
-    if (Mode == kFilter) {
-        f.bs = a.buf_s + gid * 2 * static_cast<int64_t>(a.cap);  // [cap scores | cap positions]
-        f.bi = reinterpret_cast<int32_t *>(f.bs + a.cap);
-    }
+    if (Mode == kFilter) f.set_buffer(a.buf_s + gid * 2 * static_cast<int64_t>(a.cap), a.cap);  // [cap scores | cap positions]
     float *row = (Mode == kRows) ? a.rows + gid * geo.Lk : nullptr;
 
     for (int64_t base = 0; base <= tl; base += kWave) {
@@ -2784,6 +2829,7 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     a.cap = L.cap;
     a.buf_s = L.buf;
     a.buf_n = L.buf_n;
+    a.smp = L.smp;
     a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
     a.rows = L.rows;
     const int64_t blocks = sh.B * ((L.G + 3) / 4);
@@ -2878,6 +2924,8 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
         e = launch(&k_scan_split<64, 128, false>, grid, dim3(kSplitWaves * 64), st, a, splits);
     return e;
 }
+
+int scan_sample_slots() { return kSampleSlots; }
 
 int group_select_slabs(int cap)
 {

@@ -219,36 +219,83 @@ def test_side_stream_and_preallocated_workspace():
         pv.index_refine(tq, tw, tk, 8, 16, 32, workspace=ws[:need // 2])
 
 
+# The fused scan samples 256-key tiles 0, 32, 64, ... (while a group's prefix
+# spans at most 512 tiles); the few-groups row select samples every 16th
+# score. Keys that are hot exactly where a sample looks (or exactly where it
+# does not) make the sampled threshold too high (forcing the exact re-run)
+# or too low (forcing buffer compactions).
+SCAN_TILE, SAMPLE_STRIDE, SAMPLE_SIGMAS = 256, 32, 6.0
+
+
 def _striped_keys(L, seed, hot_sampled, stripe="tile"):
     """Exact keys where the positions a threshold sample looks at are all
     "hot" (hot_sampled=True) or all "cold" (False) relative to the rest: the
-    64-key tiles at multiples of 16 (the fused scan's sample, stripe="tile")
+    256-key tiles at multiples of 32 (the fused scan's sample, stripe="tile")
     or every 16th position (the block select's sample, stripe="pos"). With
     positive queries, hot keys score far above cold ones."""
     r = np.random.default_rng([seed, 7])
     cold = r.integers(-3, 4, size=(1, L, 128)).astype(np.float64) / 4.0
     hot = r.integers(2, 4, size=(1, L, 128)).astype(np.float64) / 4.0
-    unit = np.arange(L) // 64 if stripe == "tile" else np.arange(L)
-    sampled = (unit % 16) == 0
+    unit = np.arange(L) // SCAN_TILE if stripe == "tile" else np.arange(L)
+    sampled = (unit % (SAMPLE_STRIDE if stripe == "tile" else 16)) == 0
     use_hot = sampled if hot_sampled else ~sampled
     k = np.where(use_hot[None, :, None], hot, cold)
     from workloads import to_storage
     return to_storage(k, BF16)
 
 
+def _fused_scan_paths(q, w, k, g, K):
+    """A model of the fused scan's sampled threshold on the oracle's proxy
+    scores (exact inputs, so the same scores): per group, whether the sample
+    sets a threshold that leaves fewer than K survivors (the exact re-run) or
+    more than the buffer holds (compactions). Counts of each."""
+    L = q.shape[1]
+    G = -(-L // g)
+    cap = -(-max(2 * K, K + 64) // 64) * 64
+    redo = compact = 0
+    groups = np.arange(G // 2, G, 16)  # groups whose prefix spans two sampled tiles or more
+    rows = oracle.scores_at(q, w, k, groups, np.tile(np.arange(L, dtype=np.int32), (len(groups), 1)), g=g)
+    for m, full in zip(groups, rows):
+        tl = min((m + 1) * g, L) - 1
+        hi = min((m // 8) * 8 + 7, G - 1)
+        ntiles = (min((hi + 1) * g, L) - 1) // SCAN_TILE + 1
+        if ntiles * SCAN_TILE <= 4 * K or tl + 1 <= 2 * K:
+            continue
+        row = full[:tl + 1]
+        pos = np.arange(tl + 1)
+        smp = row[(pos // SCAN_TILE) % SAMPLE_STRIDE == 0]
+        nsv = len(smp)
+        expect = np.float32(K) * np.float32(nsv) / np.float32(tl + 1)
+        r = int(np.ceil(expect + np.float32(SAMPLE_SIGMAS) * np.sqrt(expect) + np.float32(8.0)))
+        if r >= nsv:
+            continue
+        tau = np.sort(smp)[::-1][r - 1]
+        kept = int((row > tau).sum())
+        redo += kept < K
+        compact += kept > cap
+    return redo, compact
+
+
 @pytest.mark.parametrize("stripe", ["tile", "pos"])
 @pytest.mark.parametrize("hot_sampled", [True, False], ids=["sample_too_high", "sample_too_low"])
 def test_mfma_sampled_threshold_stays_exact(hot_sampled, stripe, scan_path):
-    """The scan sets its admission threshold from every 16th tile. Keys that
-    make the sample unrepresentative must still give the exact top-K: a too
-    high sample forces the exact re-run, a too low one forces compactions."""
-    L, g, topk, c = 4096, 8, 128, 256
+    """Keys that make a threshold sample unrepresentative must still give the
+    exact top-K: a too high sample forces the exact re-run, a too low one
+    compactions. For the fused scan a model of its sample on the oracle's
+    scores confirms that the stripes reach those paths."""
+    L, g, topk, c = 2 * SAMPLE_STRIDE * SCAN_TILE, 8, 128, 256
     r = np.random.default_rng(11)
     q = r.integers(1, 4, size=(1, L, 64, 128)).astype(np.float64) / 4.0
     from workloads import to_storage
     q = to_storage(q, BF16)
     w = np.ldexp(1.0, r.integers(-3, 1, size=(1, L, 64))).astype(np.float32)
     k = _striped_keys(L, 3, hot_sampled, stripe)
+    if stripe == "tile" and scan_path == "fused":
+        redo, compact = _fused_scan_paths(q, w, k, g, c)
+        if hot_sampled:
+            assert redo > 0, "the stripes should make the sampled threshold too high"
+        else:
+            assert compact > 0, "the stripes should make the sampled threshold too low"
     tq, tw, tk = to_device(q, w, k)
     f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True,
                                          scan_path=scan_path)
@@ -263,7 +310,7 @@ def test_mfma_sampled_threshold_stays_exact(hot_sampled, stripe, scan_path):
     ref = oracle.reuse(q, w, k, g, topk)
     np.testing.assert_array_equal(r_i.cpu().numpy(), ref["indices"])
     np.testing.assert_array_equal(r_s.cpu().numpy(), ref["scores"])
-    rows = np.r_[0:64, 1000:1010, 2047:2050, 4000:4096]
+    rows = np.r_[0:64, 1000:1010, 8190:8200, L - 96:L]
     ref = oracle.dense(q, w, k, topk, rows=rows)
     np.testing.assert_array_equal(d_i.cpu().numpy()[0, rows], ref["indices"][0, rows])
     np.testing.assert_array_equal(d_s.cpu().numpy()[0, rows], ref["scores"][0, rows])
