@@ -6,9 +6,10 @@ proxy scan with top-c selection -> per-member re-score and top-k), inputs
 resident in HBM. Prints one JSON line:
 
   value        query positions per second (B * Lq / step time)
-  roofline     the fused proxy-scan kernel against the bf16 MFMA peak:
+  roofline     the fused proxy-scan kernel alone against the bf16 MFMA peak:
                algorithmic FLOPs per launch (2 d H sum_groups (t_last + 1))
-               over its average launch time from hipEvents on its stream
+               over its average launch time from hipEvents on its stream;
+               roofline_scan_select counts the group select kernel's time too
   cpu_baseline the CPU oracle on a stratified sample of the same groups
 
     python bench.py [--steps K] [--warmup W] [--variant refine|reuse|dense] [--g G]
@@ -31,9 +32,18 @@ from workloads import ALL, LONG_128K  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
-METRIC = "indexer query-positions/sec (Refine g=8, L=128K) + % of bf16 MFMA peak"
+HEADLINE_METRIC = "indexer query-positions/sec (Refine g=8, L=128K) + % of bf16 MFMA peak"
 SCAN_SRC = os.path.join(ROOT, "sparse_attention_indexer_proxy_amd", "csrc", "pivot_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_counters.json")
+
+
+def metric_name(W, variant, g):
+    """The headline metric string for its own configuration (128K Refine
+    g=8); the same form, naming the workload, for every other run."""
+    if W.name == "prefill_L131072" and variant == "refine" and g == 8:
+        return HEADLINE_METRIC
+    peak = "HBM bandwidth" if W.kind.startswith("decode") else "bf16 MFMA peak"
+    return f"indexer query-positions/sec ({variant.capitalize()} g={g}, {W.name}) + % of {peak}"
 
 
 def log(*a):
@@ -72,19 +82,20 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload_name, variant, g):
-    """HBM bytes per scan launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def recorded_counters(workload_name, variant, g):
+    """Figures from committed rocprofv3 counter runs of this workload (HBM
+    bytes per scan launch from FETCH_SIZE / WRITE_SIZE; the shader clock
+    from SQ_CYCLES over the scan's duration), if they were taken on the
+    current kernel source; else {}."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    key = f"{workload_name}/{variant}/g{g}"
-    ent = rec.get(key)
+        return {}
+    ent = rec.get(f"{workload_name}/{variant}/g{g}")
     if not ent or ent.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return ent.get("hbm_bytes_per_launch")
+        return {}
+    return ent
 
 
 def practical_peaks():
@@ -159,6 +170,33 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
             "sample": (f"{len(units)} of {per_seq * W.B} {'rows' if variant == 'dense' else 'groups'} "
                        f"evenly spaced over the sequence (same mean prefix as the full workload), "
                        f"{dt:.1f} s on {threads} threads")}
+
+
+def oracle_one_thread():
+    """The oracle on one thread for the two small workloads: the tiny f32
+    workload in full (Refine), and the exact 8K workload's Refine on 64
+    evenly spaced groups. Query positions/s each."""
+    import oracle
+    from workloads import EXACT, TINY, generate
+    before = oracle.num_threads()
+    oracle.set_threads(1)
+    out = {}
+    try:
+        for W, n in ((TINY, None), (EXACT, 64)):
+            q, w, k = generate(W)
+            G = -(-W.Lq // W.g)
+            groups = None if n is None else np.unique(np.linspace(0, G - 1, n).astype(np.int64))
+            oracle.refine(q, w, k, W.g, W.topk, W.c, groups=groups[:1] if groups is not None else [0],
+                          want_scores=False, want_cand=False)
+            t0 = time.perf_counter()
+            oracle.refine(q, w, k, W.g, W.topk, W.c, groups=groups, want_scores=False, want_cand=False)
+            dt = time.perf_counter() - t0
+            rows = W.Lq if groups is None else len(groups) * W.g
+            out[W.name] = {"value": rows / dt, "unit": "query positions/s", "cores": 1,
+                           "sample": "all groups" if groups is None else f"{len(groups)} of {G} groups evenly spaced"}
+    finally:
+        oracle.set_threads(before)
+    return out
 
 
 def copy_calibration(torch, mib):
@@ -318,25 +356,41 @@ def main():
     kernels = {name: round(ms / max(n, 1), 4) for name, (ms, n) in stages.items() if n}
     log(f"[bench] {args.variant} g={g}: {ms_per_step:.3f} ms/step, kernels (ms/launch) {kernels}")
 
+    counters = recorded_counters(W.name, args.variant, g)
+    roofline_scan_select = None
     if W.kind.startswith("decode"):
         # one group per sequence: the split-key scan reads every key once and
         # meets it with only H rows, so HBM bounds it
         kbytes = scan_key_bytes(W)
         gbs = kbytes / scan_avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                    "traffic": None, "kernel": "split-key proxy scan (k_scan_split)", "bytes_per_launch": kbytes}
+                    "traffic": None, "kernel": "split-key proxy scan, eq. (5) score rows (k_scan_split)",
+                    "bytes_per_launch": kbytes}
     else:
         roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": recorded_traffic(W.name, args.variant, g),
-                    "kernel": "proxy scan + top-K selection (k_scan_mfma)", "flops_per_launch": sflops}
+                    "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": counters.get("hbm_bytes_per_launch"),
+                    "kernel": "fused proxy scan, eq. (5) with its streaming top-K filter (k_scan_mfma alone)",
+                    "flops_per_launch": sflops}
+        sel_ms, sel_n = stages["scan_select"]
+        if sel_n:
+            both_s = scan_avg_s + sel_ms / sel_n / 1e3
+            a2 = sflops / both_s / 1e12
+            roofline_scan_select = {
+                "bound": "mfma", "achieved": a2, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a2 / MFMA_BF16_PEAK_TFLOPS,
+                "kernel": "proxy scan + its final top-K / top-c select, eqs. (5)-(7) (k_scan_mfma + k_select_groups)",
+                "flops_per_launch": sflops}
 
     cpu = None
+    one_thread = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(q, w, k, W, args.variant, g, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
+        one_thread = oracle_one_thread()
+        log(f"[bench] oracle on one thread: {one_thread}")
 
     res = {
-        "metric": METRIC,
+        "metric": metric_name(W, args.variant, g),
         "value": value,
         "unit": "query positions/s",
         "n_gpus": 1,
@@ -352,7 +406,10 @@ def main():
                    "query_rows": W.Lq, "heads": W.H, "dim": W.d, "g": g, "topk": W.topk,
                    "c": W.c if args.variant == "refine" else None, "parallelism": "single GPU"},
         "roofline": roofline,
+        "roofline_scan_select": roofline_scan_select,
         "cpu_baseline": cpu,
+        "oracle_one_thread": one_thread,
+        "sclk_ghz_observed": counters.get("sclk_ghz"),
         "median_call_ms": median_call_ms,
         "practical_peak": practical,
         "scan_frac_of_practical_mfma": (achieved / practical["mfma_bf16_random_tflops"]

@@ -68,6 +68,8 @@ def load(path: str | None = None):
     lib.oracle_scores_at.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, i64, vp, i64, vp]
     lib.oracle_scores_at.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_set_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
     return lib
 
@@ -99,6 +101,13 @@ def _c(a):
 
 def num_threads(lib_path=None) -> int:
     return load(lib_path).oracle_num_threads()
+
+
+def set_threads(n: int, lib_path=None) -> None:
+    """OpenMP threads of later oracle calls in this process (results do not
+    depend on it)."""
+    if load(lib_path).oracle_set_threads(int(n)) != 0:
+        raise ValueError("threads must be >= 1")
 
 
 def groups_of(Lq: int, g: int) -> int:

@@ -501,6 +501,16 @@ int oracle_scores_at(const oracle_problem *p, int32_t proxy, int32_t g, int32_t 
     return rc;
 }
 
+/* Threads of the OpenMP loops above (n >= 1); results never depend on it. */
+int oracle_set_threads(int32_t n)
+{
+    if (n < 1) return OR_BAD_ARG;
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#endif
+    return OR_OK;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

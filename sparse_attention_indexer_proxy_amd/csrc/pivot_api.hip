@@ -120,7 +120,7 @@ struct Layout {
     bool pool;
     bool few;               // few groups: split scan into score rows + block selects
     int scan_splits, refine_splits;
-    size_t qbar, wbar, buf, buf_n, smp, rows, cand, cand_n, cand_sc, scratch, nvalid, total;
+    size_t qbar, wbar, buf, buf_n, smp, rows, hist, cand, cand_n, cand_sc, scratch, nvalid, total;
 };
 
 // Below this many groups the per-group fused scan cannot fill 256 CUs; the
@@ -254,9 +254,13 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
         int64_t ss = (kSplitScanWorkgroups + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.scan_splits = static_cast<int>(ss < most ? ss : most);
         const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 127) / 128;  // refine tiles of 128
-        int64_t rs = (512 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
+        // refine: as many slices of C per group as fill the 256 CUs once
+        // (each workgroup then scores several tiles, so its start-up
+        // latency is paid once)
+        int64_t rs = (256 + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.refine_splits = static_cast<int>(rs < ctiles ? rs : ctiles);
         l.rows = take(groups * static_cast<size_t>(p->lk) * sizeof(float));
+        l.hist = take(groups * static_cast<size_t>(l.scan_splits) * pivot::row_hist_bins() * sizeof(uint32_t));
     } else {
         l.scan_splits = l.refine_splits = 1;
         l.buf = take(groups * 2 * cap * sizeof(float));
@@ -384,6 +388,7 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     sl.rows = nullptr;
     if (L.few) {
         sl.rows = reinterpret_cast<float *>(base + L.rows);
+        sl.hist = reinterpret_cast<uint32_t *>(base + L.hist);
         {
             StageTimer tm(PIVOT_STAGE_SCAN, s);
             st = hip_status(pivot::launch_scan_split(sh, sl, L.scan_splits, s), "split scan launch");
@@ -400,6 +405,8 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
         rs.out_sc = sl.out_sc;
         rs.out_count = sl.out_count;
         rs.out_stride = sl.out_stride;
+        rs.hist = sl.hist;
+        rs.hist_splits = L.scan_splits;
         StageTimer tm(PIVOT_STAGE_SELECT, s);
         st = hip_status(pivot::launch_select_rows(sh, rs, s), "select launch");
     } else {

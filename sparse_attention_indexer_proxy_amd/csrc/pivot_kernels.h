@@ -55,6 +55,7 @@ struct ScanLaunch {
     int out_stride;
     int to_candidates;
     float *rows;        // [B, G, Lk] score rows, or nullptr for selection
+    uint32_t *hist;     // split scan: [B*G, splits, row_hist_bins()] score counts
 };
 
 struct RefineLaunch {
@@ -107,6 +108,8 @@ struct RowSelectLaunch {
     const int32_t *cand;
     const int32_t *cand_n;
     int c;
+    const uint32_t *hist;  // kind 0: the split scan's score counts, or null
+    int hist_splits;
 };
 
 // O1-O3 diagnostics of index rows (pivot_diag.hip).
@@ -130,6 +133,8 @@ int stats_group_fits(int g, int k);
 bool mfma_shape(const LaunchShape &sh);
 // Sampled scores the fused scan keeps per group (its workspace share).
 int scan_sample_slots();
+// Score-count bins per split-scan workgroup (its workspace share).
+int row_hist_bins();
 // agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st);

@@ -290,6 +290,20 @@ __device__ __forceinline__ void hist_add_peel(bool in, uint32_t key, uint32_t pr
     if (other) atomicAdd(&hist[digit], 1u);
 }
 
+// One count per lane with `in` into bins[bin] (LDS); the lanes sharing the
+// first counted lane's bin add with one atomic, the others one each.
+__device__ __forceinline__ void bin_add(bool in, uint32_t bin, uint32_t *bins, int l)
+{
+    const uint64_t mm = ballot(in);
+    if (mm == 0) return;
+    const int first = __ffsll(static_cast<long long>(mm)) - 1;
+    const uint32_t b0 = lane_value(bin, first);
+    const bool other = in && bin != b0;
+    const uint64_t same = mm & ~ballot(other);
+    if (l == first) atomicAdd(&bins[b0], static_cast<uint32_t>(popc(same)));
+    if (other) atomicAdd(&bins[bin], 1u);
+}
+
 // Radix select over 8-bit digits of ord_key(score), most significant first,
 // with a per-wave 256-bin histogram in LDS. sc may point to global memory;
 // each lane keeps 8 loads in flight.
@@ -636,9 +650,17 @@ struct ScanArgs {
     SelectionOut out; // exact-order scan: selected in-kernel
     // kRows
     float *rows;  // [B, G, Lk]
+    uint32_t *hist;  // split scan: [B*G, splits, kRowHistBins] counts of the scores' leading key bits
 };
 
 constexpr int kTileKeys = 64;
+
+// The split scan counts every score of its key range by the leading
+// kRowHistBits bits of its order-preserving key (sign, exponent, 3 mantissa
+// bits: bins an eighth of an octave wide); the row select finds the bin that
+// holds the K-th largest score from these counts.
+constexpr int kRowHistBits = 12;
+constexpr int kRowHistBins = 1 << kRowHistBits;
 
 typedef __attribute__((address_space(1))) const void *global_cptr;
 typedef __attribute__((address_space(3))) void *lds_ptr;
@@ -1164,6 +1186,7 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
 {
     static_assert(H % 16 == 0 && D == 128, "B fragments assume 128-dim keys");
     constexpr int RB = H / 16;
+    __shared__ uint32_t hist[kRowHistBins];  // this workgroup's score counts
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -1171,11 +1194,21 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     const int split = blockIdx.x % splits;
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t tl = geo.t_last(b, m);
-    if (tl < 0) return;  // no key: nothing to score
-    const int nq = static_cast<int>(tl / kWave) + 1;  // quarters holding keys 0 .. tl
+    for (int i = threadIdx.x; i < kRowHistBins; i += kSplitWaves * 64) hist[i] = 0u;
+    __syncthreads();
+    // the workgroup's counts go out whatever it scored (zeros when nothing)
+    auto flush_hist = [&]() {
+        __syncthreads();
+        uint32_t *out = a.hist + (gid * splits + split) * kRowHistBins;
+        for (int i = threadIdx.x; i < kRowHistBins; i += kSplitWaves * 64) out[i] = hist[i];
+    };
+    const int nq = tl < 0 ? 0 : static_cast<int>(tl / kWave) + 1;  // quarters holding keys 0 .. tl
     const int U = kSplitWaves * splits;
     const int u = kSplitWaves * split + wv;
-    if (u >= nq) return;  // no barrier below: a wave without a quarter just ends
+    if (u >= nq) {  // a wave without a quarter (or a group without keys)
+        flush_hist();
+        return;
+    }
     const int n = (nq - 1 - u) / U + 1;  // this wave's quarters: qidx(i), i < n
 
     const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
@@ -1267,6 +1300,9 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
         const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
             row + q0, 0, static_cast<uint32_t>((left < kWave ? left : kWave) * sizeof(float)), 0x00020000);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), out, l * 4, 0, 0);
+        // count the lanes' scores (keys <= tl) by their leading key bits;
+        // the lanes sharing the first lane's bin add with one atomic
+        bin_add(l < left, ord_key(score) >> (32 - kRowHistBits), hist, l);
     };
     // UNROLL quarters per trip (a multiple of 2 and of DEPTH), so the key
     // slots and the entry arrays trade roles without copies (a copy of a
@@ -1280,6 +1316,7 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
 #pragma unroll
     for (int k = 0; k < UNROLL - 1; ++k)
         if (i + k <= last) quarter(i + k, k % DEPTH, e[k % 2], e[(k + 1) % 2]);
+    flush_hist();
 }
 
 // --------------------------------------------------- block-wide select
@@ -1291,6 +1328,8 @@ struct RowSelectArgs {
     Geo geo;
     int kind;              // 0: group rows (decode scan); 1: member rows (split refine)
     const float *rows;     // kind 0: [B*G, Lk]; kind 1: scratch [B*G, g, c]
+    const uint32_t *hist;  // kind 0: the split scan's score counts [B*G, splits, kRowHistBins]
+    int splits;
     int K;                 // kind 0: c (to candidates) or topk (to member rows); kind 1: topk
     int to_candidates;     // kind 0 only
     int32_t *out_idx;      // rows [B, Lq, topk] or candidates [B, G, c]
@@ -1781,7 +1820,6 @@ __device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, Blo
 }
 
 constexpr int kSurvivors = 12288;  // LDS capacity of the prefilter (entries)
-constexpr int kSampleMax = 8192;   // sampled scores (held in registers)
 
 __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
 {
@@ -1797,30 +1835,48 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         int n = static_cast<int>(tl1 > 0 ? tl1 : 0);
         const float *row = a.rows + gid * geo.Lk;
 
-        // Sampled prefilter: tau from every stride-th score, then a stable
-        // compaction of the scores > tau into LDS, where the exact select
-        // runs. Falls back to the full row when the survivors overflow LDS
-        // or are fewer than K (a sample that overshoots).
+        // Prefilter from the split scan's counts of the row's scores by
+        // their leading key bits: the bin holding the K-th largest score,
+        // then a stable compaction of the scores at or above that bin into
+        // LDS, where the exact select runs. Falls back to the full row when
+        // those entries overflow LDS.
         uint32_t key[kSelRegs];
         bool in_lds = false, in_regs = false;
-        if (n > 4 * a.K && 3 * a.K <= kSurvivors) {
-            const int stride = n / kSampleMax + 1 > 16 ? n / kSampleMax + 1 : 16;
-            const int ns = (n + stride - 1) / stride;  // <= kSampleMax
-            float x[kSelRegs];
-#pragma unroll
-            for (int e = 0; e < kSelRegs; ++e) {
-                const int i = e * kSelThreads + tid;
-                x[e] = e * kSelThreads < ns ? load_as<kGlobal>(row, static_cast<int64_t>(i < ns ? i : ns - 1) * stride)
-                                            : 0.0f;
+        if (n > 2 * a.K && a.hist) {
+            static_assert(kRowHistBins == 4 * kSelThreads, "four bins per thread");
+            const int l = tid & (kWave - 1), wv = tid >> 6;
+            uint32_t c4[4] = {0u, 0u, 0u, 0u};
+            const uint32_t *hg = a.hist + gid * a.splits * kRowHistBins + 4 * tid;
+            for (int sp = 0; sp < a.splits; ++sp) {
+                const uint4 h = *reinterpret_cast<const uint4 *>(hg + sp * kRowHistBins);
+                c4[0] += h.x;
+                c4[1] += h.y;
+                c4[2] += h.z;
+                c4[3] += h.w;
             }
-#pragma unroll
-            for (int e = 0; e < kSelRegs; ++e) key[e] = e * kSelThreads + tid < ns ? ord_key(x[e]) : 0u;
-            const float expect = static_cast<float>(a.K) * static_cast<float>(ns) / static_cast<float>(n);
-            const int r = static_cast<int>(ceilf(expect + kSampleSigmas * sqrtf(expect) + 8.0f));
-            if (r < ns) {
-                // keep keys strictly above the r-th sampled key
-                const Sel ts = block_select_regs(key, ns, r, sh);
-                const int kept = block_filter_above(row, n, key_float(ts.kth), sel_scores, sel_pos, kSurvivors, sh);
+            // counts above each thread's bins: a block suffix sum (higher
+            // threads hold higher bins)
+            const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
+            const uint32_t suf = wave_suffix_sum(tot);  // within the wave, from this lane up
+            if (l == 0) sh.wave_sum[0][wv] = static_cast<int>(lane_value(suf, 0));
+            __syncthreads();
+            uint32_t higher = 0u;  // counts of the waves above this one
+            for (int x = wv + 1; x < kSelWaves; ++x) higher += static_cast<uint32_t>(sh.wave_sum[0][x]);
+            uint32_t above = higher + suf - tot;  // entries in bins above this thread's
+            const uint32_t K = static_cast<uint32_t>(a.K);
+            if (above < K && above + tot >= K) {
+                int bsel = 3;
+                while (above + c4[bsel] < K) above += c4[bsel--];
+                sh.bcast[0] = static_cast<uint32_t>(4 * tid + bsel);  // the bin holding the K-th largest
+                sh.bcast[1] = above + c4[bsel];                       // entries in it and above it
+            }
+            __syncthreads();
+            const uint32_t bin = sh.bcast[0], keep = sh.bcast[1];
+            __syncthreads();
+            if (keep <= static_cast<uint32_t>(kSurvivors) && bin > 0u) {
+                // keys >= bin << 20, i.e. scores above the float of the key just below
+                const float tau = key_float((bin << (32 - kRowHistBits)) - 1u);
+                const int kept = block_filter_above(row, n, tau, sel_scores, sel_pos, kSurvivors, sh);
                 if (kept >= a.K && kept <= kSurvivors) {
                     n = kept;
                     in_lds = true;
@@ -2917,6 +2973,7 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.H = sh.H;
     a.D = sh.D;
     a.rows = L.rows;
+    a.hist = L.hist;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
     if (sh.pages.table)
         e = launch(&k_scan_split<64, 128, true>, grid, dim3(kSplitWaves * 64), st, a, splits);
@@ -2926,6 +2983,7 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
 }
 
 int scan_sample_slots() { return kSampleSlots; }
+int row_hist_bins() { return kRowHistBins; }
 
 int group_select_slabs(int cap)
 {
@@ -3006,6 +3064,8 @@ hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, h
     a.cand = L.cand;
     a.cand_n = L.cand_n;
     a.c = L.c;
+    a.hist = L.hist;
+    a.splits = L.hist_splits;
     const int64_t jobs = L.kind == 0 ? sh.B * L.G : sh.B * sh.Lq;
     e = launch(&k_select_rows, dim3(static_cast<uint32_t>(jobs)), dim3(kSelThreads), st, a);
     return e;

@@ -314,3 +314,44 @@ def test_mfma_sampled_threshold_stays_exact(hot_sampled, stripe, scan_path):
     ref = oracle.dense(q, w, k, topk, rows=rows)
     np.testing.assert_array_equal(d_i.cpu().numpy()[0, rows], ref["indices"][0, rows])
     np.testing.assert_array_equal(d_s.cpu().numpy()[0, rows], ref["scores"][0, rows])
+
+
+# Exact inputs on the fused path at the headline's selection sizes, so every
+# slab count of the register selects runs on data whose result is unique:
+# group select K = c = 4096 (survivor buffer of 8192: 128 slabs), K = k =
+# 2048 (64 slabs) and K = 700 (1408: 32 slabs), the member select over c =
+# 4096 (64 slabs), and c = 5000 (buffer beyond the register selects: the
+# streaming radix select, and the in-kernel member select of the refine).
+SLAB_CASES = [
+    # name, L, g, topk, c
+    ("k2048_c4096", 16384, 8, 2048, 4096),
+    ("k700_c1400", 12288, 8, 700, 1400),
+    ("k3000_c5000", 16384, 8, 3000, 5000),
+]
+
+
+@pytest.mark.parametrize("case", SLAB_CASES, ids=[c[0] for c in SLAB_CASES])
+def test_fused_selects_bitwise_at_every_slab_count(case):
+    name, L, g, topk, c = case
+    q, w, k = exact_random(zlib.crc32(name.encode()) % 1000, 1, L, L, 64, 128, BF16, w_levels=(-3, 0))
+    tq, tw, tk = to_device(q, w, k)
+    print(f"[slabs] {name}: GPU", flush=True)
+    f_i, f_s, f_c, f_n = pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, return_candidates=True,
+                                         scan_path="fused")
+    r_i, r_s = pv.index_reuse(tq, tw, tk, g, topk, return_scores=True, scan_path="fused")
+    d_i, d_s = pv.index_dense(tq, tw, tk, topk, return_scores=True, scan_path="fused")
+    torch.cuda.synchronize()
+    print(f"[slabs] {name}: oracle refine", flush=True)
+    ref = oracle.refine(q, w, k, g, topk, c)
+    np.testing.assert_array_equal(f_n.cpu().numpy(), ref["cand_n"])
+    np.testing.assert_array_equal(f_c.cpu().numpy(), ref["cand"])
+    np.testing.assert_array_equal(f_i.cpu().numpy(), ref["indices"])
+    np.testing.assert_array_equal(f_s.cpu().numpy(), ref["scores"])
+    print(f"[slabs] {name}: oracle reuse", flush=True)
+    ref = oracle.reuse(q, w, k, g, topk)
+    np.testing.assert_array_equal(r_i.cpu().numpy(), ref["indices"])
+    np.testing.assert_array_equal(r_s.cpu().numpy(), ref["scores"])
+    rows = np.unique(np.r_[0:40, topk - 8:topk + 8, np.linspace(0, L - 1, 160).astype(np.int64), L - 40:L])
+    ref = oracle.dense(q, w, k, topk, rows=rows)
+    np.testing.assert_array_equal(d_i.cpu().numpy()[0, rows], ref["indices"][0, rows])
+    np.testing.assert_array_equal(d_s.cpu().numpy()[0, rows], ref["scores"][0, rows])
