@@ -253,7 +253,8 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
         const int64_t most = (quarters + 3) / 4;
         int64_t ss = (kSplitScanWorkgroups + static_cast<int64_t>(groups) - 1) / static_cast<int64_t>(groups);
         l.scan_splits = static_cast<int>(ss < most ? ss : most);
-        const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + 127) / 128;  // refine tiles of 128
+        const int64_t rt = pivot::refine_tile();
+        const int64_t ctiles = (int64_t(variant == PIVOT_REFINE ? c : 1) + rt - 1) / rt;  // refine tiles
         // refine: as many slices of C per group as fill the 256 CUs once
         // (each workgroup then scores several tiles, so its start-up
         // latency is paid once)

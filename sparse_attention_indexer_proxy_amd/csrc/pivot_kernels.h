@@ -135,6 +135,8 @@ bool mfma_shape(const LaunchShape &sh);
 int scan_sample_slots();
 // Score-count bins per split-scan workgroup (its workspace share).
 int row_hist_bins();
+// Candidates per refine tile.
+int refine_tile();
 // agg: 0 mean of the members (eq. 4), 1 first member, 2 last member.
 hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, const float *w, void *qbar,
                        float *wbar, int agg, hipStream_t st);

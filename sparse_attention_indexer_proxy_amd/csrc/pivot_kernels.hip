@@ -1319,6 +1319,67 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     flush_hist();
 }
 
+// Raw buffer descriptor over n 32-bit entries at p (gfx9 family: fourth
+// word 0x00020000 = 32-bit data format, no swizzle); loads past the end
+// return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *p, int n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n * 4, 0x00020000);
+}
+
+// Number of keys in kv[] that are >= x (a wave-uniform count).
+template <int N>
+__device__ __forceinline__ int count_ge(const uint32_t (&kv)[N], uint32_t x)
+{
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) n += popc(ballot(kv[i] >= x));
+    return n;
+}
+
+constexpr int kMsMid = 1024;    // LDS keys per wave for the final bits (a bin bisected in registers)
+
+// The K-th largest key when it lies in a bin [lo, hi] whose n keys are in
+// mid (LDS) and `above` keys exceed the bin: the largest x in [lo, hi] with
+// above + #{bin keys >= x} >= K, plus the keys above it and equal to it
+// (counted over the bin alone), with the bin held R keys per lane.
+struct BinKth {
+    uint32_t kth;
+    int n_gt, n_eq;
+};
+
+template <int R>
+__device__ __forceinline__ BinKth bisect_bin(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above, int K)
+{
+    const int l = lane_id();
+    uint32_t mv[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int j = kWave * q + l;
+        mv[q] = j < n ? mid[j] : 0u;
+    }
+    while (lo < hi) {
+        const uint32_t x = lo + (hi - lo) / 2u + 1u;
+        if (above + count_ge(mv, x) >= K)
+            lo = x;
+        else
+            hi = x - 1u;
+    }
+    BinKth r;
+    r.kth = lo;
+    r.n_gt = above + (lo == 0xFFFFFFFFu ? 0 : count_ge(mv, lo + 1u));
+    r.n_eq = above + count_ge(mv, lo) - r.n_gt;
+    return r;
+}
+
+__device__ __forceinline__ BinKth bisect_bin_any(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above,
+                                                 int K)
+{
+    if (n <= kWave) return bisect_bin<1>(mid, n, lo, hi, above, K);
+    if (n <= 4 * kWave) return bisect_bin<4>(mid, n, lo, hi, above, K);
+    return bisect_bin<kMsMid / kWave>(mid, n, lo, hi, above, K);
+}
+
 // --------------------------------------------------- block-wide select
 // Selection of one row by a whole workgroup (1024 threads), for rows too
 // long for one wave: the proxy rows of the split scan and the member rows of
@@ -1834,12 +1895,42 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         const int64_t tl1 = geo.t_last(b, m) + 1;
         int n = static_cast<int>(tl1 > 0 ? tl1 : 0);
         const float *row = a.rows + gid * geo.Lk;
+        const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
+        const int64_t stride = a.out_stride;
+        int32_t *ci = a.out_idx + gid * a.out_stride;
+        float *cs = a.out_sc ? a.out_sc + gid * a.out_stride : nullptr;
+        auto emit = [&](int slot, int32_t p, float v) {
+            if (a.to_candidates) {
+                ci[slot] = p;
+                if (cs) cs[slot] = v;
+            } else {
+                for (int64_t r = r0; r < r1; ++r) {
+                    a.out_idx[(b * geo.Lq + r) * stride + slot] = p;
+                    if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + slot] = v;
+                }
+            }
+        };
+        auto finish = [&](int got) {
+            if (a.to_candidates) {
+                for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
+                    ci[t] = -1;
+                    if (cs) cs[t] = -INFINITY;
+                }
+                if (a.out_count && tid == 0) a.out_count[gid] = got;
+                return;
+            }
+            for (int64_t r = r0; r < r1; ++r) {
+                for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
+                    a.out_idx[(b * geo.Lq + r) * stride + t] = -1;
+                    if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + t] = -INFINITY;
+                }
+            }
+        };
 
-        // Prefilter from the split scan's counts of the row's scores by
-        // their leading key bits: the bin holding the K-th largest score,
-        // then a stable compaction of the scores at or above that bin into
-        // LDS, where the exact select runs. Falls back to the full row when
-        // those entries overflow LDS.
+        // The split scan's counts of the row's scores by their leading key
+        // bits give the bin holding the K-th largest score; the scores at or
+        // above that bin are compacted into LDS, where the exact select
+        // runs. Falls back to the full row when they overflow LDS.
         uint32_t key[kSelRegs];
         bool in_lds = false, in_regs = false;
         if (n > 2 * a.K && a.hist) {
@@ -1868,10 +1959,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
                 int bsel = 3;
                 while (above + c4[bsel] < K) above += c4[bsel--];
                 sh.bcast[0] = static_cast<uint32_t>(4 * tid + bsel);  // the bin holding the K-th largest
-                sh.bcast[1] = above + c4[bsel];                       // entries in it and above it
+                sh.bcast[1] = above;                                  // entries in higher bins
+                sh.bcast[2] = c4[bsel];                               // entries in it
             }
             __syncthreads();
-            const uint32_t bin = sh.bcast[0], keep = sh.bcast[1];
+            const uint32_t bin = sh.bcast[0], keep = sh.bcast[1] + sh.bcast[2];
             __syncthreads();
             if (keep <= static_cast<uint32_t>(kSurvivors) && bin > 0u) {
                 // keys >= bin << 20, i.e. scores above the float of the key just below
@@ -1890,38 +1982,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
             in_regs = true;
         }
         const Sel s = in_regs ? block_select_regs(key, n, a.K, sh) : block_select(row, n, a.K, sh);
-        if (a.to_candidates) {
-            int32_t *ci = a.out_idx + gid * a.out_stride;
-            float *cs = a.out_sc ? a.out_sc + gid * a.out_stride : nullptr;
-            auto emit = [&](int slot, int32_t p, float v) {
-                ci[slot] = p;
-                if (cs) cs[slot] = v;
-            };
-            const int got = in_lds ? block_emit<kLds>(sel_scores, sel_pos, n, s, sh, emit)
-                                   : block_emit<kGlobal>(row, nullptr, n, s, sh, emit);
-            for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
-                ci[t] = -1;
-                if (cs) cs[t] = -INFINITY;
-            }
-            if (a.out_count && tid == 0) a.out_count[gid] = got;
-            return;
-        }
-        const int64_t r0 = geo.first_row(m), r1 = geo.end_row(m);
-        const int64_t stride = a.out_stride;
-        auto emit = [&](int slot, int32_t p, float v) {
-            for (int64_t r = r0; r < r1; ++r) {
-                a.out_idx[(b * geo.Lq + r) * stride + slot] = p;
-                if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + slot] = v;
-            }
-        };
         const int got = in_lds ? block_emit<kLds>(sel_scores, sel_pos, n, s, sh, emit)
                                : block_emit<kGlobal>(row, nullptr, n, s, sh, emit);
-        for (int64_t r = r0; r < r1; ++r) {
-            for (int t = got + tid; t < a.out_stride; t += kSelThreads) {
-                a.out_idx[(b * geo.Lq + r) * stride + t] = -1;
-                if (a.out_sc) a.out_sc[(b * geo.Lq + r) * stride + t] = -INFINITY;
-            }
-        }
+        finish(got);
         return;
     }
     // kind 1: member row = blockIdx.x over flat query rows
@@ -2043,32 +2106,13 @@ struct MemberSelectArgs {
     float *out_sc;              // nullable
 };
 
-// Raw buffer descriptor over n 32-bit entries at p (gfx9 family: fourth
-// word 0x00020000 = 32-bit data format, no swizzle); loads past the end
-// return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *p, int n)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n * 4, 0x00020000);
-}
-
 constexpr int kMsWaves = 4;     // rows (one per wave) per workgroup
-constexpr int kMsMid = 1024;    // LDS keys per wave for the final bits
 constexpr int kMsChunk = 16;    // slabs of positions loaded at a time
 #ifndef PIVOT_HIST_BINS
 #define PIVOT_HIST_BINS 512
 #endif
 constexpr int kHistBins = PIVOT_HIST_BINS;  // value-range bins of the one-pass histogram
 static_assert(kHistBins % kWave == 0, "whole bins per lane");
-
-// Number of keys in kv[] that are >= x (a wave-uniform count).
-template <int N>
-__device__ __forceinline__ int count_ge(const uint32_t (&kv)[N], uint32_t x)
-{
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) n += popc(ballot(kv[i] >= x));
-    return n;
-}
 
 // Wave-uniform max / min: the prefix-scan pattern of wave_incl_sum, read
 // from the last lane.
@@ -2109,47 +2153,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 // repeated key (many exact zeros), which ends the search. emit(slot,
 // position, score) is called for every selected entry, slots dense and
 // ascending; positions are loaded a chunk ahead. Returns the count.
-// The K-th largest key when it lies in a bin [lo, hi] whose n keys are in
-// mid (LDS) and `above` keys exceed the bin: the largest x in [lo, hi] with
-// above + #{bin keys >= x} >= K, plus the keys above it and equal to it
-// (counted over the bin alone), with the bin held R keys per lane.
-struct BinKth {
-    uint32_t kth;
-    int n_gt, n_eq;
-};
-
-template <int R>
-__device__ __forceinline__ BinKth bisect_bin(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above, int K)
-{
-    const int l = lane_id();
-    uint32_t mv[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        const int j = kWave * q + l;
-        mv[q] = j < n ? mid[j] : 0u;
-    }
-    while (lo < hi) {
-        const uint32_t x = lo + (hi - lo) / 2u + 1u;
-        if (above + count_ge(mv, x) >= K)
-            lo = x;
-        else
-            hi = x - 1u;
-    }
-    BinKth r;
-    r.kth = lo;
-    r.n_gt = above + (lo == 0xFFFFFFFFu ? 0 : count_ge(mv, lo + 1u));
-    r.n_eq = above + count_ge(mv, lo) - r.n_gt;
-    return r;
-}
-
-__device__ __forceinline__ BinKth bisect_bin_any(const uint32_t *mid, int n, uint32_t lo, uint32_t hi, int above,
-                                                 int K)
-{
-    if (n <= kWave) return bisect_bin<1>(mid, n, lo, hi, above, K);
-    if (n <= 4 * kWave) return bisect_bin<4>(mid, n, lo, hi, above, K);
-    return bisect_bin<kMsMid / kWave>(mid, n, lo, hi, above, K);
-}
-
 // Slot passed for the entries not selected when the emitter drops
 // out-of-range slots (its stores go through a buffer resource of the row).
 constexpr int kNoSlot = 0x1FFFFFFF;  // times 4 bytes: past any row, still a positive int
@@ -2625,6 +2628,13 @@ __device__ __forceinline__ int prefix_le(const int32_t *C, int n, int64_t t)
     return done;
 }
 
+// Candidates per refine tile (two tiles in LDS: 2 x 32 KiB at 128).
+#ifndef PIVOT_REFINE_TILE
+#define PIVOT_REFINE_TILE 128
+#endif
+constexpr int kRefineTile = PIVOT_REFINE_TILE;
+static_assert(kRefineTile % 64 == 0, "whole 64-candidate quarters");
+
 // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
 // workgroup i is given unit (i % 8) * (n / 8) + i / 8 and each XCD's L2
 // serves a contiguous run of units (the tail beyond a multiple of 8 keeps
@@ -2650,7 +2660,7 @@ __global__ __launch_bounds__(NW * 64) void k_refine_mfma(RefineArgs a)
 {
     static_assert(H % 16 == 0 && D == 128, "tile layout assumes 128-dim keys (16 chunks of 8 bf16 per row)");
     constexpr int RB = H / 16;
-    constexpr int NT = 2 * kTileKeys;          // candidates per tile
+    constexpr int NT = kRefineTile;            // candidates per tile
     constexpr int NQ = NT / kWave;             // 64-candidate quarters per tile
     constexpr int kSlices = NT * D * 2 / 1024; // 1 KiB slices per tile (32)
     constexpr int kMaxSlices = kSlices / NW;   // per wave
@@ -2984,6 +2994,7 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
 
 int scan_sample_slots() { return kSampleSlots; }
 int row_hist_bins() { return kRowHistBins; }
+int refine_tile() { return kRefineTile; }
 
 int group_select_slabs(int cap)
 {
