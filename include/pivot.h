@@ -36,6 +36,9 @@
  *   candidate_counts  [batch, G]       int32 (optional Refine output, |C|)
  *   where G = ceil(lq / g).
  *
+ * Alignment: q, w and k start on 16-byte boundaries (any torch allocation
+ * does); the workspace on 256-byte boundaries.
+ *
  * Ownership and execution: the caller owns every buffer (the library never
  * allocates or frees device memory). All work is enqueued on `stream` (a
  * hipStream_t passed as void*; NULL = default stream) and the call returns

@@ -242,10 +242,13 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
         off = align_up(off + bytes);
         return at;
     };
-    l.qbar = l.pool ? take(groups * p->heads * p->dim * elt) : 0;
-    l.wbar = l.pool ? take(groups * p->heads * sizeof(float)) : 0;
     l.few = pivot::mfma_shape(sh) &&
             (cfg.path == PIVOT_PATH_SPLIT || (cfg.path == PIVOT_PATH_AUTO && static_cast<int64_t>(groups) < kFewGroups));
+    // the proxies go through HBM only where the pool kernel forms them (the
+    // fused MFMA scan forms them from the member rows itself)
+    const bool pool_kernel = l.pool && (l.few || !pivot::mfma_shape(sh));
+    l.qbar = pool_kernel ? take(groups * p->heads * p->dim * elt) : 0;
+    l.wbar = pool_kernel ? take(groups * p->heads * sizeof(float)) : 0;
     if (l.few) {
         // split scan: about kSplitScanWorkgroups workgroups of four waves
         // over all groups, each wave streaming at least one 64-key quarter
@@ -333,8 +336,9 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
         return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", L.total, ws ? ws_bytes : size_t(0));
     if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
         return fail(PIVOT_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-    if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0)
-        return fail(PIVOT_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(w) % 16 != 0)
+        return fail(PIVOT_ERR_INVALID_ARG, "q, w and k must be 16-byte aligned");
 
     pivot::LaunchShape sh = shape_of(p);
     sh.lens = kin.lens;
@@ -344,7 +348,10 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
 
     const void *qsrc = q;
     const float *wsrc = w;
-    if (L.pool) {
+    // the fused MFMA scan forms each group's proxy from the member rows
+    // itself (the same arithmetic as k_pool): no proxy round trip through HBM
+    const bool pool_inline = L.pool && !L.few && pivot::mfma_shape(sh);
+    if (L.pool && !pool_inline) {
         void *qbar = base + L.qbar;
         float *wbar = reinterpret_cast<float *>(base + L.wbar);
         {
@@ -365,6 +372,8 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     pivot::ScanLaunch sl{};
     sl.qsrc = qsrc;
     sl.wsrc = wsrc;
+    sl.pool_inline = pool_inline ? 1 : 0;
+    sl.agg = cfg.agg;
     sl.k = k;
     sl.G = L.G;
     sl.g = L.g;

@@ -40,8 +40,10 @@ struct LaunchShape {
 // One scan launch: eq. (5) for every group, then either the streaming
 // selection of the best K (rows != nullptr selects the score-row output).
 struct ScanLaunch {
-    const void *qsrc;   // [B, G, H, D]
-    const float *wsrc;  // [B, G, H]
+    const void *qsrc;   // [B, G, H, D], or with pool_inline the queries [B, Lq, H, D]
+    const float *wsrc;  // [B, G, H], or with pool_inline the weights [B, Lq, H]
+    int pool_inline;    // fused MFMA scan only: form each group's proxy (eq. 4) in the kernel
+    int agg;            // pool_inline: 0 mean, 1 first member, 2 last member
     const void *k;      // [B, Lk, D]
     int64_t G;
     int g;

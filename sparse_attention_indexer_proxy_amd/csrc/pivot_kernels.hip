@@ -637,8 +637,10 @@ __global__ __launch_bounds__(256) void k_pool(const T *__restrict__ q, const flo
 enum ScanMode { kFilter = 0, kRows = 1 };
 
 struct ScanArgs {
-    const void *qsrc;   // [B, G, H, D] proxies (the queries themselves when g == 1)
-    const float *wsrc;  // [B, G, H]
+    const void *qsrc;   // [B, G, H, D] proxies (the queries themselves when g == 1), or, with
+    const float *wsrc;  // [B, G, H]    pool_inline, the member rows q [B, Lq, H, D], w [B, Lq, H]
+    int pool_inline;    // fused scan: 1 = form each group's proxy (eq. 4) from its members' rows
+    int agg;            // pool_inline: 0 mean, 1 first member, 2 last member
     Keys keys;          // [B, Lk, D] contiguous, or paged
     Geo geo;
     int H, D;
@@ -652,8 +654,6 @@ struct ScanArgs {
     float *rows;  // [B, G, Lk]
     uint32_t *hist;  // split scan: [B*G, splits, kRowHistBins] counts of the scores' leading key bits
 };
-
-constexpr int kTileKeys = 64;
 
 // The split scan counts every score of its key range by the leading
 // kRowHistBits bits of its order-preserving key (sign, exponent, 3 mantissa
@@ -824,6 +824,95 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
     }
 }
 
+// eq. (4) inside the scan: the proxy of rows [r0, r1) of q (row stride H D)
+// straight into this lane's A fragments and w slots, with the arithmetic of
+// k_pool (fp32 sum in member order, one IEEE division by the member count,
+// RNE to bf16; the first / last member copied unchanged for agg 1 / 2). The
+// member rows are requested eight at a time, four fragments per round, so a
+// round costs one memory latency.
+template <int H>
+__device__ __forceinline__ void pool_a(const uint16_t *q, const float *w, int64_t r0, int64_t r1, int agg, int l,
+                                       bf16x8 (&afr)[H / 16][4], float (&wr)[H / 16][4])
+{
+    constexpr int RB = H / 16, D = 128;
+    if (agg != 0) {
+        const int64_t r = agg == 1 ? r0 : r1 - 1;
+        load_a<H>(q + r * H * D, l, afr);
+        load_w<H>(w + r * H, l, wr);
+        return;
+    }
+    const float gm = static_cast<float>(r1 - r0);
+    constexpr int kRows = 8, kFrags = 4;
+#pragma unroll
+    for (int f0 = 0; f0 < RB * 4; f0 += kFrags) {
+        float acc[kFrags][8];
+#pragma unroll
+        for (int j = 0; j < kFrags; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+        for (int64_t r = r0; r < r1; r += kRows) {
+            uint4 v[kRows][kFrags];
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const int64_t rr = r + i < r1 ? r + i : r1 - 1;  // a short batch repeats its last row
+#pragma unroll
+                for (int j = 0; j < kFrags; ++j) {
+                    const int f = f0 + j, rb = f / 4, kb = f % 4;
+                    v[i][j] = *reinterpret_cast<const uint4 *>(q + (rr * H + 16 * rb + (l & 15)) * D + 32 * kb +
+                                                               8 * (l >> 4));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                if (r + i < r1) {
+#pragma unroll
+                    for (int j = 0; j < kFrags; ++j) {
+                        const uint32_t u[4] = {v[i][j].x, v[i][j].y, v[i][j].z, v[i][j].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[j][e] = acc[j][e] + bf16_bits_to_float(static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2))));
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kFrags; ++j) {
+            uint32_t u[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                u[e] = static_cast<uint32_t>(float_to_bf16_rne(acc[j][2 * e] / gm)) |
+                       static_cast<uint32_t>(float_to_bf16_rne(acc[j][2 * e + 1] / gm)) << 16;
+            const int f = f0 + j;
+            afr[f / 4][f % 4] = __builtin_bit_cast(bf16x8, uint4{u[0], u[1], u[2], u[3]});
+        }
+    }
+    // w: the lane's four heads of each 16-head block are contiguous (one
+    // float4 per member and block), requested for eight members at once
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t r = r0; r < r1; r += kRows) {
+            float4 v[kRows];
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const int64_t rr = r + i < r1 ? r + i : r1 - 1;
+                v[i] = *reinterpret_cast<const float4 *>(w + rr * H + 16 * rb + 4 * (l >> 4));
+            }
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                if (r + i < r1) {
+                    sum[0] = sum[0] + v[i].x;
+                    sum[1] = sum[1] + v[i].y;
+                    sum[2] = sum[2] + v[i].z;
+                    sum[3] = sum[3] + v[i].w;
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wr[rb][v] = sum[v] / gm;
+    }
+}
+
 // Sampled admission threshold (filter mode). Before the full pass the WG
 // scores every `stride`-th tile; each wave sets tau a few standard deviations
 // below its sample's estimate of the K-th best score, so the full pass admits
@@ -927,8 +1016,14 @@ __global__ __launch_bounds__(kScanWaves * 64) void k_scan_mfma(ScanArgs a)
 
     bf16x8 afr[RB][4];
     float wr[RB][4];
-    load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
-    load_w<H>(a.wsrc + gid * H, l, wr);
+    if (a.pool_inline) {
+        const int64_t mm = active ? m : blk * kScanWaves;
+        pool_a<H>(static_cast<const uint16_t *>(a.qsrc) + b * geo.Lq * H * D, a.wsrc + b * geo.Lq * H,
+                  geo.first_row(mm), geo.end_row(mm), a.agg, l, afr, wr);
+    } else {
+        load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
+        load_w<H>(a.wsrc + gid * H, l, wr);
+    }
 
     Filter f;
     f.K = a.K;
@@ -2896,6 +2991,8 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
     a.buf_s = L.buf;
     a.buf_n = L.buf_n;
     a.smp = L.smp;
+    a.pool_inline = L.pool_inline;
+    a.agg = L.agg;
     a.out = SelectionOut{L.out_idx, L.out_sc, L.out_count, L.out_stride, L.to_candidates};
     a.rows = L.rows;
     const int64_t blocks = sh.B * ((L.G + 3) / 4);

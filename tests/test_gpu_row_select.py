@@ -1,7 +1,8 @@
 """GPU parity of the few-groups (decode) path against the oracle, aimed at
-the block-wide row selects: the group rows (sampled prefilter into LDS, the
-register radix select, the fallbacks to the full row) and the member rows of
-the split refine (held in registers up to c = 4096, streamed beyond).
+the block-wide row selects: the group rows (prefilter into LDS from the split
+scan's score counts, the register radix select, the fallbacks to the full
+row) and the member rows of the split refine (held in registers up to
+c = 4096, streamed beyond).
 
 Exact inputs (q, k in {-3..3}/4, w powers of two) make every score exact, so
 candidate sets, indices and scores must match bit for bit, ties included.
@@ -45,7 +46,8 @@ def _check_refine_and_reuse(q, w, k, g, topk, c):
 
 # name, B, Lk, c, topk: member rows in registers (c <= 4096) or streamed
 # (c > 4096); group rows selected in registers (prefix <= 16384), through
-# the sampled prefilter (prefix > 4c, 3c <= 12288) or streamed (the rest)
+# the count-driven prefilter (prefix > 2c, the threshold bin and above within
+# 12288 entries) or streamed (the rest)
 CASES = [
     ("c4095_regs", 2, 9000, 4095, 1000),
     ("c4096_regs", 2, 9000, 4096, 2048),
@@ -65,11 +67,11 @@ def test_decode_shapes_match_oracle_bitwise(case):
     _check_refine_and_reuse(q, w, k, 4, topk, c)
 
 
-@pytest.mark.parametrize("hot_sampled", [True, False], ids=["sample_too_high", "sample_too_low"])
-def test_row_prefilter_falls_back_exactly(hot_sampled):
-    """Every 16th position of a row is what the group-row select samples:
-    hot sampled keys set τ too high (fewer than c survivors), cold ones too
-    low (more survivors than LDS holds); both fall back to the full row."""
+@pytest.mark.parametrize("hot_sampled", [True, False], ids=["hot_every_16th", "cold_every_16th"])
+def test_row_prefilter_on_periodic_hot_keys(hot_sampled):
+    """Rows whose hot keys sit on every 16th position (or everywhere else):
+    the threshold bin comes from the scan's exact counts, so either way the
+    prefilter keeps exactly the entries at or above it."""
     Lk, c, topk = 40000, 1024, 256
     r = np.random.default_rng(21)
     q = to_storage(r.integers(1, 4, size=(1, 4, 64, 128)).astype(np.float64) / 4.0, BF16)
@@ -84,4 +86,15 @@ def test_all_equal_scores_select_the_earliest_positions():
     B, Lk, c, topk = 2, 9000, 2048, 512
     q, w, _ = exact_random(31, B, 4, Lk, 64, 128, BF16)
     k = np.tile(exact_random(32, 1, 1, 1, 1, 128, BF16)[2], (B, Lk, 1))
+    _check_refine_and_reuse(q, w, k, 4, topk, c)
+
+
+def test_crowded_threshold_bin_falls_back_to_the_full_row():
+    """All but the first 100 keys equal: the bin holding the c-th largest
+    score holds about 40000 entries, more than the LDS prefilter takes, so
+    the group select streams the full row (and ties go to the lower
+    position)."""
+    B, Lk, c, topk = 1, 40000, 1024, 256
+    q, w, k = exact_random(33, B, 4, Lk, 64, 128, BF16)
+    k[:, 100:] = k[:, 100:101]
     _check_refine_and_reuse(q, w, k, 4, topk, c)
