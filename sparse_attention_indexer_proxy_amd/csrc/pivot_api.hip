@@ -246,7 +246,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
             (cfg.path == PIVOT_PATH_SPLIT || (cfg.path == PIVOT_PATH_AUTO && static_cast<int64_t>(groups) < kFewGroups));
     // the proxies go through HBM only where the pool kernel forms them (the
     // fused MFMA scan forms them from the member rows itself)
-    const bool pool_kernel = l.pool && (l.few || !pivot::mfma_shape(sh));
+    const bool pool_kernel = l.pool && !pivot::mfma_shape(sh);
     l.qbar = pool_kernel ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = pool_kernel ? take(groups * p->heads * sizeof(float)) : 0;
     if (l.few) {
@@ -348,9 +348,10 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
 
     const void *qsrc = q;
     const float *wsrc = w;
-    // the fused MFMA scan forms each group's proxy from the member rows
-    // itself (the same arithmetic as k_pool): no proxy round trip through HBM
-    const bool pool_inline = L.pool && !L.few && pivot::mfma_shape(sh);
+    // the MFMA scans (fused and split) form each group's proxy from the
+    // member rows themselves (the same arithmetic as k_pool): no pool launch
+    // and no proxy round trip through HBM
+    const bool pool_inline = L.pool && pivot::mfma_shape(sh);
     if (L.pool && !pool_inline) {
         void *qbar = base + L.qbar;
         float *wbar = reinterpret_cast<float *>(base + L.wbar);

@@ -42,7 +42,7 @@ struct LaunchShape {
 struct ScanLaunch {
     const void *qsrc;   // [B, G, H, D], or with pool_inline the queries [B, Lq, H, D]
     const float *wsrc;  // [B, G, H], or with pool_inline the weights [B, Lq, H]
-    int pool_inline;    // fused MFMA scan only: form each group's proxy (eq. 4) in the kernel
+    int pool_inline;    // MFMA scans (fused, split): form each group's proxy (eq. 4) in the kernel
     int agg;            // pool_inline: 0 mean, 1 first member, 2 last member
     const void *k;      // [B, Lk, D]
     int64_t G;

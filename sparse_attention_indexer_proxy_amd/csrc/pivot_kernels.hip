@@ -639,7 +639,7 @@ enum ScanMode { kFilter = 0, kRows = 1 };
 struct ScanArgs {
     const void *qsrc;   // [B, G, H, D] proxies (the queries themselves when g == 1), or, with
     const float *wsrc;  // [B, G, H]    pool_inline, the member rows q [B, Lq, H, D], w [B, Lq, H]
-    int pool_inline;    // fused scan: 1 = form each group's proxy (eq. 4) from its members' rows
+    int pool_inline;    // MFMA scans: 1 = form each group's proxy (eq. 4) from its members' rows
     int agg;            // pool_inline: 0 mean, 1 first member, 2 last member
     Keys keys;          // [B, Lk, D] contiguous, or paged
     Geo geo;
@@ -824,93 +824,98 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
     }
 }
 
-// eq. (4) inside the scan: the proxy of rows [r0, r1) of q (row stride H D)
-// straight into this lane's A fragments and w slots, with the arithmetic of
-// k_pool (fp32 sum in member order, one IEEE division by the member count,
-// RNE to bf16; the first / last member copied unchanged for agg 1 / 2). The
-// member rows are requested eight at a time, four fragments per round, so a
-// round costs one memory latency.
+// eq. (4) inside the scan: row block rb (heads 16 rb .. 16 rb + 15) of the
+// proxy of rows [r0, r1) of q (row stride H D) straight into this lane's A
+// fragments and w slots, with the arithmetic of k_pool (fp32 sum in member
+// order, one IEEE division by the member count, RNE to bf16; the first /
+// last member copied unchanged for agg 1 / 2). The member rows are
+// requested eight at a time, the block's four fragments together, so eight
+// members cost one memory latency.
+template <int H>
+__device__ __forceinline__ void pool_rb(const uint16_t *q, const float *w, int64_t r0, int64_t r1, int agg, int l,
+                                        int rb, bf16x8 (&afr)[4], float (&wr)[4])
+{
+    constexpr int D = 128;
+    if (agg != 0) {
+        const int64_t r = agg == 1 ? r0 : r1 - 1;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            afr[kb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(q + (r * H + 16 * rb + (l & 15)) * D + 32 * kb + 8 * (l >> 4)));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wr[v] = w[r * H + 16 * rb + 4 * (l >> 4) + v];
+        return;
+    }
+    const float gm = static_cast<float>(r1 - r0);
+    constexpr int kRows = 8;
+    float acc[4][8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[kb][e] = 0.0f;
+    for (int64_t r = r0; r < r1; r += kRows) {
+        uint4 v[kRows][4];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t rr = r + i < r1 ? r + i : r1 - 1;  // a short batch repeats its last row
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                v[i][kb] =
+                    *reinterpret_cast<const uint4 *>(q + (rr * H + 16 * rb + (l & 15)) * D + 32 * kb + 8 * (l >> 4));
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            if (r + i < r1) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const uint32_t u[4] = {v[i][kb].x, v[i][kb].y, v[i][kb].z, v[i][kb].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[kb][e] = acc[kb][e] + bf16_bits_to_float(static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2))));
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            u[e] = static_cast<uint32_t>(float_to_bf16_rne(acc[kb][2 * e] / gm)) |
+                   static_cast<uint32_t>(float_to_bf16_rne(acc[kb][2 * e + 1] / gm)) << 16;
+        afr[kb] = __builtin_bit_cast(bf16x8, uint4{u[0], u[1], u[2], u[3]});
+    }
+    // w: the lane's four heads of the block are contiguous (one float4 per
+    // member), requested for eight members at once
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t r = r0; r < r1; r += kRows) {
+        float4 v[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t rr = r + i < r1 ? r + i : r1 - 1;
+            v[i] = *reinterpret_cast<const float4 *>(w + rr * H + 16 * rb + 4 * (l >> 4));
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            if (r + i < r1) {
+                sum[0] = sum[0] + v[i].x;
+                sum[1] = sum[1] + v[i].y;
+                sum[2] = sum[2] + v[i].z;
+                sum[3] = sum[3] + v[i].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wr[v] = sum[v] / gm;
+}
+
+// The whole proxy (every row block) in this lane's A fragments and w slots.
 template <int H>
 __device__ __forceinline__ void pool_a(const uint16_t *q, const float *w, int64_t r0, int64_t r1, int agg, int l,
                                        bf16x8 (&afr)[H / 16][4], float (&wr)[H / 16][4])
 {
-    constexpr int RB = H / 16, D = 128;
-    if (agg != 0) {
-        const int64_t r = agg == 1 ? r0 : r1 - 1;
-        load_a<H>(q + r * H * D, l, afr);
-        load_w<H>(w + r * H, l, wr);
-        return;
-    }
-    const float gm = static_cast<float>(r1 - r0);
-    constexpr int kRows = 8, kFrags = 4;
 #pragma unroll
-    for (int f0 = 0; f0 < RB * 4; f0 += kFrags) {
-        float acc[kFrags][8];
-#pragma unroll
-        for (int j = 0; j < kFrags; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
-        for (int64_t r = r0; r < r1; r += kRows) {
-            uint4 v[kRows][kFrags];
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const int64_t rr = r + i < r1 ? r + i : r1 - 1;  // a short batch repeats its last row
-#pragma unroll
-                for (int j = 0; j < kFrags; ++j) {
-                    const int f = f0 + j, rb = f / 4, kb = f % 4;
-                    v[i][j] = *reinterpret_cast<const uint4 *>(q + (rr * H + 16 * rb + (l & 15)) * D + 32 * kb +
-                                                               8 * (l >> 4));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                if (r + i < r1) {
-#pragma unroll
-                    for (int j = 0; j < kFrags; ++j) {
-                        const uint32_t u[4] = {v[i][j].x, v[i][j].y, v[i][j].z, v[i][j].w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[j][e] = acc[j][e] + bf16_bits_to_float(static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2))));
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kFrags; ++j) {
-            uint32_t u[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                u[e] = static_cast<uint32_t>(float_to_bf16_rne(acc[j][2 * e] / gm)) |
-                       static_cast<uint32_t>(float_to_bf16_rne(acc[j][2 * e + 1] / gm)) << 16;
-            const int f = f0 + j;
-            afr[f / 4][f % 4] = __builtin_bit_cast(bf16x8, uint4{u[0], u[1], u[2], u[3]});
-        }
-    }
-    // w: the lane's four heads of each 16-head block are contiguous (one
-    // float4 per member and block), requested for eight members at once
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t r = r0; r < r1; r += kRows) {
-            float4 v[kRows];
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const int64_t rr = r + i < r1 ? r + i : r1 - 1;
-                v[i] = *reinterpret_cast<const float4 *>(w + rr * H + 16 * rb + 4 * (l >> 4));
-            }
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                if (r + i < r1) {
-                    sum[0] = sum[0] + v[i].x;
-                    sum[1] = sum[1] + v[i].y;
-                    sum[2] = sum[2] + v[i].z;
-                    sum[3] = sum[3] + v[i].w;
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) wr[rb][v] = sum[v] / gm;
-    }
+    for (int rb = 0; rb < H / 16; ++rb) pool_rb<H>(q, w, r0, r1, agg, l, rb, afr[rb], wr[rb]);
 }
 
 // Sampled admission threshold (filter mode). Before the full pass the WG
@@ -1282,6 +1287,8 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     static_assert(H % 16 == 0 && D == 128, "B fragments assume 128-dim keys");
     constexpr int RB = H / 16;
     __shared__ uint32_t hist[kRowHistBins];  // this workgroup's score counts
+    __shared__ uint4 pool_f[RB][4][kWave];   // pool_inline: the proxy's A fragments, per lane
+    __shared__ float4 pool_w[RB][kWave];     // and its w slots
     const Geo &geo = a.geo;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -1290,6 +1297,20 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t tl = geo.t_last(b, m);
     for (int i = threadIdx.x; i < kRowHistBins; i += kSplitWaves * 64) hist[i] = 0u;
+    if (a.pool_inline) {
+        // eq. (4) once per workgroup: wave wv pools row blocks wv, wv + 4,
+        // ... of the group's proxy from the member rows and leaves them in
+        // LDS for every wave (the pool kernel and its HBM round trip go)
+        for (int rb = wv; rb < RB; rb += kSplitWaves) {
+            bf16x8 f[4];
+            float wq[4];
+            pool_rb<H>(static_cast<const uint16_t *>(a.qsrc) + b * geo.Lq * H * D, a.wsrc + b * geo.Lq * H,
+                       geo.first_row(m), geo.end_row(m), a.agg, l, rb, f, wq);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) pool_f[rb][kb][l] = __builtin_bit_cast(uint4, f[kb]);
+            pool_w[rb][l] = float4{wq[0], wq[1], wq[2], wq[3]};
+        }
+    }
     __syncthreads();
     // the workgroup's counts go out whatever it scored (zeros when nothing)
     auto flush_hist = [&]() {
@@ -1312,8 +1333,21 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
 
     bf16x8 afr[RB][4];
     float wr[RB][4];
-    load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
-    load_w<H>(a.wsrc + gid * H, l, wr);
+    if (a.pool_inline) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) afr[rb][kb] = __builtin_bit_cast(bf16x8, pool_f[rb][kb][l]);
+            const float4 v = pool_w[rb][l];
+            wr[rb][0] = v.x;
+            wr[rb][1] = v.y;
+            wr[rb][2] = v.z;
+            wr[rb][3] = v.w;
+        }
+    } else {
+        load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
+        load_w<H>(a.wsrc + gid * H, l, wr);
+    }
 
     // the wave's i-th quarter: the groups start their sweeps at staggered
     // offsets (group gid of N at nq gid / N), so that the groups do not
@@ -2033,12 +2067,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
             const int l = tid & (kWave - 1), wv = tid >> 6;
             uint32_t c4[4] = {0u, 0u, 0u, 0u};
             const uint32_t *hg = a.hist + gid * a.splits * kRowHistBins + 4 * tid;
-            for (int sp = 0; sp < a.splits; ++sp) {
-                const uint4 h = *reinterpret_cast<const uint4 *>(hg + sp * kRowHistBins);
-                c4[0] += h.x;
-                c4[1] += h.y;
-                c4[2] += h.z;
-                c4[3] += h.w;
+            // the splits' counts are requested kHistBatch at a time (a short
+            // batch re-reads the last split and drops it), so a batch costs
+            // one memory latency, not one per split
+            constexpr int kHistBatch = 16;
+            for (int sp0 = 0; sp0 < a.splits; sp0 += kHistBatch) {
+                uint4 h[kHistBatch];
+#pragma unroll
+                for (int j = 0; j < kHistBatch; ++j) {
+                    const int sp = sp0 + j < a.splits ? sp0 + j : a.splits - 1;
+                    h[j] = *reinterpret_cast<const uint4 *>(hg + sp * kRowHistBins);
+                }
+#pragma unroll
+                for (int j = 0; j < kHistBatch; ++j) {
+                    const bool in = sp0 + j < a.splits;
+                    c4[0] += in ? h[j].x : 0u;
+                    c4[1] += in ? h[j].y : 0u;
+                    c4[2] += in ? h[j].z : 0u;
+                    c4[3] += in ? h[j].w : 0u;
+                }
             }
             // counts above each thread's bins: a block suffix sum (higher
             // threads hold higher bins)
@@ -3079,6 +3126,8 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.geo = Geo{sh.B, L.G, sh.Lq, sh.Lk, L.g, sh.lens};
     a.H = sh.H;
     a.D = sh.D;
+    a.pool_inline = L.pool_inline;
+    a.agg = L.agg;
     a.rows = L.rows;
     a.hist = L.hist;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
