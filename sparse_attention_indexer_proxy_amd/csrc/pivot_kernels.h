@@ -135,7 +135,7 @@ int stats_group_fits(int g, int k);
 bool mfma_shape(const LaunchShape &sh);
 // Sampled scores the fused scan keeps per group (its workspace share).
 int scan_sample_slots();
-// Score-count bins per split-scan workgroup (its workspace share).
+// Score-count words per split-scan workgroup (its workspace share).
 int row_hist_bins();
 // Candidates per refine tile.
 int refine_tile();

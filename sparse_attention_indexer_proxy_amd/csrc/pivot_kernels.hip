@@ -652,15 +652,20 @@ struct ScanArgs {
     SelectionOut out; // exact-order scan: selected in-kernel
     // kRows
     float *rows;  // [B, G, Lk]
-    uint32_t *hist;  // split scan: [B*G, splits, kRowHistBins] counts of the scores' leading key bits
+    uint32_t *hist;  // split scan: [B*G, splits, kRowHistWords] counts of the scores' leading key bits
 };
 
 // The split scan counts every score of its key range by the leading
 // kRowHistBits bits of its order-preserving key (sign, exponent, 3 mantissa
 // bits: bins an eighth of an octave wide); the row select finds the bin that
-// holds the K-th largest score from these counts.
+// holds the K-th largest score from these counts. Each workgroup writes the
+// kRowHistBins fine counts, then kRowCoarseBins coarse ones (sixteen fine
+// bins each, two octaves), so the select finds the coarse bin first and then
+// reads only its sixteen fine counts.
 constexpr int kRowHistBits = 12;
 constexpr int kRowHistBins = 1 << kRowHistBits;
+constexpr int kRowCoarseBins = kRowHistBins / 16;
+constexpr int kRowHistWords = kRowHistBins + kRowCoarseBins;
 
 typedef __attribute__((address_space(1))) const void *global_cptr;
 typedef __attribute__((address_space(3))) void *lds_ptr;
@@ -828,10 +833,9 @@ __device__ __forceinline__ void load_w(const float *src, int l, float (&wr)[H / 
 // proxy of rows [r0, r1) of q (row stride H D) straight into this lane's A
 // fragments and w slots, with the arithmetic of k_pool (fp32 sum in member
 // order, one IEEE division by the member count, RNE to bf16; the first /
-// last member copied unchanged for agg 1 / 2). The member rows are
-// requested eight at a time, the block's four fragments together, so eight
-// members cost one memory latency.
-template <int H>
+// last member copied unchanged for agg 1 / 2). The q and w rows of ROWS
+// members are requested together, so ROWS members cost one memory latency.
+template <int H, int ROWS = 8>
 __device__ __forceinline__ void pool_rb(const uint16_t *q, const float *w, int64_t r0, int64_t r1, int agg, int l,
                                         int rb, bf16x8 (&afr)[4], float (&wr)[4])
 {
@@ -842,29 +846,35 @@ __device__ __forceinline__ void pool_rb(const uint16_t *q, const float *w, int64
         for (int kb = 0; kb < 4; ++kb)
             afr[kb] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const uint4 *>(q + (r * H + 16 * rb + (l & 15)) * D + 32 * kb + 8 * (l >> 4)));
-#pragma unroll
-        for (int v = 0; v < 4; ++v) wr[v] = w[r * H + 16 * rb + 4 * (l >> 4) + v];
+        const float4 v = *reinterpret_cast<const float4 *>(w + r * H + 16 * rb + 4 * (l >> 4));
+        wr[0] = v.x;
+        wr[1] = v.y;
+        wr[2] = v.z;
+        wr[3] = v.w;
         return;
     }
     const float gm = static_cast<float>(r1 - r0);
-    constexpr int kRows = 8;
     float acc[4][8];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[kb][e] = 0.0f;
-    for (int64_t r = r0; r < r1; r += kRows) {
-        uint4 v[kRows][4];
+    // w: the lane's four heads of the block are contiguous (one float4 per member)
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t r = r0; r < r1; r += ROWS) {
+        uint4 v[ROWS][4];
+        float4 vw[ROWS];
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
+        for (int i = 0; i < ROWS; ++i) {
             const int64_t rr = r + i < r1 ? r + i : r1 - 1;  // a short batch repeats its last row
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 v[i][kb] =
                     *reinterpret_cast<const uint4 *>(q + (rr * H + 16 * rb + (l & 15)) * D + 32 * kb + 8 * (l >> 4));
+            vw[i] = *reinterpret_cast<const float4 *>(w + rr * H + 16 * rb + 4 * (l >> 4));
         }
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
+        for (int i = 0; i < ROWS; ++i) {
             if (r + i < r1) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
@@ -873,6 +883,10 @@ __device__ __forceinline__ void pool_rb(const uint16_t *q, const float *w, int64
                     for (int e = 0; e < 8; ++e)
                         acc[kb][e] = acc[kb][e] + bf16_bits_to_float(static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2))));
                 }
+                sum[0] = sum[0] + vw[i].x;
+                sum[1] = sum[1] + vw[i].y;
+                sum[2] = sum[2] + vw[i].z;
+                sum[3] = sum[3] + vw[i].w;
             }
         }
     }
@@ -885,26 +899,6 @@ __device__ __forceinline__ void pool_rb(const uint16_t *q, const float *w, int64
                    static_cast<uint32_t>(float_to_bf16_rne(acc[kb][2 * e + 1] / gm)) << 16;
         afr[kb] = __builtin_bit_cast(bf16x8, uint4{u[0], u[1], u[2], u[3]});
     }
-    // w: the lane's four heads of the block are contiguous (one float4 per
-    // member), requested for eight members at once
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t r = r0; r < r1; r += kRows) {
-        float4 v[kRows];
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const int64_t rr = r + i < r1 ? r + i : r1 - 1;
-            v[i] = *reinterpret_cast<const float4 *>(w + rr * H + 16 * rb + 4 * (l >> 4));
-        }
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            if (r + i < r1) {
-                sum[0] = sum[0] + v[i].x;
-                sum[1] = sum[1] + v[i].y;
-                sum[2] = sum[2] + v[i].z;
-                sum[3] = sum[3] + v[i].w;
-            }
-        }
-    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) wr[v] = sum[v] / gm;
 }
@@ -915,7 +909,7 @@ __device__ __forceinline__ void pool_a(const uint16_t *q, const float *w, int64_
                                        bf16x8 (&afr)[H / 16][4], float (&wr)[H / 16][4])
 {
 #pragma unroll
-    for (int rb = 0; rb < H / 16; ++rb) pool_rb<H>(q, w, r0, r1, agg, l, rb, afr[rb], wr[rb]);
+    for (int rb = 0; rb < H / 16; ++rb) pool_rb<H, 4>(q, w, r0, r1, agg, l, rb, afr[rb], wr[rb]);
 }
 
 // Sampled admission threshold (filter mode). Before the full pass the WG
@@ -1286,7 +1280,7 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
 {
     static_assert(H % 16 == 0 && D == 128, "B fragments assume 128-dim keys");
     constexpr int RB = H / 16;
-    __shared__ uint32_t hist[kRowHistBins];  // this workgroup's score counts
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kRowHistBins];  // this workgroup's score counts
     __shared__ uint4 pool_f[RB][4][kWave];   // pool_inline: the proxy's A fragments, per lane
     __shared__ float4 pool_w[RB][kWave];     // and its w slots
     const Geo &geo = a.geo;
@@ -1297,57 +1291,30 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     const int64_t b = gid / geo.G, m = gid % geo.G;
     const int64_t tl = geo.t_last(b, m);
     for (int i = threadIdx.x; i < kRowHistBins; i += kSplitWaves * 64) hist[i] = 0u;
-    if (a.pool_inline) {
-        // eq. (4) once per workgroup: wave wv pools row blocks wv, wv + 4,
-        // ... of the group's proxy from the member rows and leaves them in
-        // LDS for every wave (the pool kernel and its HBM round trip go)
-        for (int rb = wv; rb < RB; rb += kSplitWaves) {
-            bf16x8 f[4];
-            float wq[4];
-            pool_rb<H>(static_cast<const uint16_t *>(a.qsrc) + b * geo.Lq * H * D, a.wsrc + b * geo.Lq * H,
-                       geo.first_row(m), geo.end_row(m), a.agg, l, rb, f, wq);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) pool_f[rb][kb][l] = __builtin_bit_cast(uint4, f[kb]);
-            pool_w[rb][l] = float4{wq[0], wq[1], wq[2], wq[3]};
-        }
-    }
-    __syncthreads();
     // the workgroup's counts go out whatever it scored (zeros when nothing)
     auto flush_hist = [&]() {
         __syncthreads();
-        uint32_t *out = a.hist + (gid * splits + split) * kRowHistBins;
+        uint32_t *out = a.hist + (gid * splits + split) * kRowHistWords;
         for (int i = threadIdx.x; i < kRowHistBins; i += kSplitWaves * 64) out[i] = hist[i];
+        static_assert(kRowCoarseBins == kSplitWaves * 64, "one coarse bin per thread");
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(hist + 16 * threadIdx.x);
+        uint32_t c = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = h4[i];
+            c += v.x + v.y + v.z + v.w;
+        }
+        out[kRowHistBins + threadIdx.x] = c;
     };
     const int nq = tl < 0 ? 0 : static_cast<int>(tl / kWave) + 1;  // quarters holding keys 0 .. tl
     const int U = kSplitWaves * splits;
     const int u = kSplitWaves * split + wv;
-    if (u >= nq) {  // a wave without a quarter (or a group without keys)
-        flush_hist();
-        return;
-    }
-    const int n = (nq - 1 - u) / U + 1;  // this wave's quarters: qidx(i), i < n
+    const bool has = u < nq;  // wave-uniform: this wave has quarters
+    const int n = has ? (nq - 1 - u) / U + 1 : 0;  // this wave's quarters: qidx(i), i < n
 
     const uint16_t *kbase = static_cast<const uint16_t *>(a.keys.base);
     const int64_t lkb = geo.lk(b);
     float *row = a.rows + gid * geo.Lk;
-
-    bf16x8 afr[RB][4];
-    float wr[RB][4];
-    if (a.pool_inline) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) afr[rb][kb] = __builtin_bit_cast(bf16x8, pool_f[rb][kb][l]);
-            const float4 v = pool_w[rb][l];
-            wr[rb][0] = v.x;
-            wr[rb][1] = v.y;
-            wr[rb][2] = v.z;
-            wr[rb][3] = v.w;
-        }
-    } else {
-        load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
-        load_w<H>(a.wsrc + gid * H, l, wr);
-    }
 
     // the wave's i-th quarter: the groups start their sweeps at staggered
     // offsets (group gid of N at nq gid / N), so that the groups do not
@@ -1395,8 +1362,53 @@ __global__ __launch_bounds__(kSplitWaves * 64, 2) void k_scan_split(ScanArgs a, 
     constexpr int DEPTH = PAGED ? 1 : 2;
     bf16x8 bq[DEPTH][4][4];
     int32_t e[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    // the first quarter's keys are requested before the proxy is formed, so
+    // their latency and the proxy's overlap
+    if (has) {
+        load_entries(0, e[1]);
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
+        for (int cb = 0; cb < 4; ++cb) load_block(0, cb, e[1], bq[0][cb]);
+    }
+    if (a.pool_inline) {
+        // eq. (4) once per workgroup: wave wv pools row blocks wv, wv + 4,
+        // ... of the group's proxy from the member rows and leaves them in
+        // LDS for every wave (no pool launch, no proxy round trip through
+        // HBM); four members per memory round trip
+        for (int rb = wv; rb < RB; rb += kSplitWaves) {
+            bf16x8 f[4];
+            float wq[4];
+            pool_rb<H, 4>(static_cast<const uint16_t *>(a.qsrc) + b * geo.Lq * H * D, a.wsrc + b * geo.Lq * H,
+                          geo.first_row(m), geo.end_row(m), a.agg, l, rb, f, wq);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) pool_f[rb][kb][l] = __builtin_bit_cast(uint4, f[kb]);
+            pool_w[rb][l] = float4{wq[0], wq[1], wq[2], wq[3]};
+        }
+    }
+    __syncthreads();
+    if (!has) {  // a wave without a quarter (or a group without keys)
+        flush_hist();
+        return;
+    }
+
+    bf16x8 afr[RB][4];
+    float wr[RB][4];
+    if (a.pool_inline) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) afr[rb][kb] = __builtin_bit_cast(bf16x8, pool_f[rb][kb][l]);
+            const float4 v = pool_w[rb][l];
+            wr[rb][0] = v.x;
+            wr[rb][1] = v.y;
+            wr[rb][2] = v.z;
+            wr[rb][3] = v.w;
+        }
+    } else {
+        load_a<H>(static_cast<const uint16_t *>(a.qsrc) + gid * H * D, l, afr);
+        load_w<H>(a.wsrc + gid * H, l, wr);
+    }
+#pragma unroll
+    for (int d = 1; d < DEPTH; ++d) {
         load_entries(d < last ? d : last, e[1]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) load_block(d < last ? d : last, cb, e[1], bq[d][cb]);
@@ -1518,7 +1530,7 @@ struct RowSelectArgs {
     Geo geo;
     int kind;              // 0: group rows (decode scan); 1: member rows (split refine)
     const float *rows;     // kind 0: [B*G, Lk]; kind 1: scratch [B*G, g, c]
-    const uint32_t *hist;  // kind 0: the split scan's score counts [B*G, splits, kRowHistBins]
+    const uint32_t *hist;  // kind 0: the split scan's score counts [B*G, splits, kRowHistWords]
     int splits;
     int K;                 // kind 0: c (to candidates) or topk (to member rows); kind 1: topk
     int to_candidates;     // kind 0 only
@@ -1540,11 +1552,7 @@ struct BlockShared {
     uint32_t bcast[4];
     uint32_t key_and[kSelWaves], key_or[kSelWaves];  // block_select_keys
     uint32_t small[4 * kWave];                        // block_select_keys: the last bin's keys
-    // block_filter_above: per-chunk survivor counts and their offsets, in
-    // (slot e, wave) order, double-buffered over chunks
-    alignas(16) int fcnt[2][kSelWaves * kSelWaves];
-    alignas(16) int foff[2][kSelWaves * kSelWaves];
-    int ftot[2];
+    uint32_t digit_hist[256];                         // block_select_bin: one histogram for the block
 };
 
 // Exclusive prefix over the block's threads of per-thread counts c0, c1 in
@@ -1696,7 +1704,7 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v)
 constexpr int kSmall = 4 * kWave;
 
 template <int N, class Valid, class Any>
-__device__ Sel block_select_keys(const uint32_t (&key)[N], Valid &&valid, Any &&any, int n, int K, BlockShared &sh)
+__device__ __forceinline__ Sel block_select_keys(const uint32_t (&key)[N], Valid &&valid, Any &&any, int n, int K, BlockShared &sh)
 {
     Sel r;
     if (n <= K) {
@@ -1844,7 +1852,7 @@ __device__ Sel block_select_keys(const uint32_t (&key)[N], Valid &&valid, Any &&
     return r;
 }
 
-__device__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, BlockShared &sh)
+__device__ __forceinline__ Sel block_select_regs(const uint32_t (&key)[kSelRegs], int n, int K, BlockShared &sh)
 {
     const int tid = threadIdx.x;
     return block_select_keys(
@@ -1868,83 +1876,6 @@ __device__ __forceinline__ void block_load_keys(const float *sc, int n, uint32_t
     for (int e = 0; e < kSelRegs; ++e) key[e] = e * kSelThreads + tid < n ? ord_key(x[e]) : 0u;
 }
 
-// Stable compaction of the entries of sc[0, n) (global memory, n >= 1)
-// whose score is above tau into out_v / out_p (score, position; LDS), in
-// ascending position; returns their number. A float comparison: the kept
-// set is {key > ord_key(tau)} (or {score > 0} when tau is -0), a threshold
-// set either way. A chunk whose survivors would pass cap is counted but not
-// written (the caller then falls back to the full row). A chunk is
-// kFiltRegs * kSelThreads entries, entry j0 + e * kSelThreads + tid in
-// thread tid, so each load instruction reads 256 contiguous bytes per wave
-// and a whole chunk is in flight while the previous one is compacted. Two
-// barriers per chunk: the (slot, wave) survivor counts are scanned by wave 0.
-constexpr int kFiltRegs = 16;
-
-__device__ int block_filter_above(const float *sc, int n, float tau, float *out_v, int32_t *out_p, int cap,
-                                  BlockShared &sh)
-{
-    static_assert(kFiltRegs == kSelWaves && kSelWaves * kSelWaves == 4 * kWave, "scan layout: 4 counts per lane");
-    constexpr int CH = kFiltRegs * kSelThreads;
-    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
-    float vn[kFiltRegs];
-    auto fetch = [&](int j0) {
-#pragma unroll
-        for (int e = 0; e < kFiltRegs; ++e) {
-            const int j = j0 + e * kSelThreads + tid;
-            vn[e] = load_as<kGlobal>(sc, j < n ? j : n - 1);
-        }
-    };
-    int base = 0, par = 0;
-    auto chunk = [&](int j0, auto tail) {
-        float v[kFiltRegs];
-#pragma unroll
-        for (int e = 0; e < kFiltRegs; ++e) v[e] = vn[e];
-        if (j0 + CH < n) fetch(j0 + CH);
-        bool keep[kFiltRegs];
-        uint32_t cnt_l = 0;  // lane e < kFiltRegs: this wave's survivors in slot e
-#pragma unroll
-        for (int e = 0; e < kFiltRegs; ++e) {
-            keep[e] = v[e] > tau;
-            if constexpr (decltype(tail)::value) keep[e] = keep[e] && j0 + e * kSelThreads + tid < n;
-            // the ballot outside the conditional: every lane takes part
-            const uint32_t c = static_cast<uint32_t>(popc(ballot(keep[e])));
-            cnt_l = l == e ? c : cnt_l;
-        }
-        if (l < kFiltRegs) sh.fcnt[par][l * kSelWaves + wv] = static_cast<int>(cnt_l);
-        __syncthreads();
-        if (wv == 0) {
-            const int4 c = *reinterpret_cast<const int4 *>(sh.fcnt[par] + 4 * l);
-            const int tot = c.x + c.y + c.z + c.w;
-            const int ex = static_cast<int>(wave_incl_sum(static_cast<uint32_t>(tot))) - tot;
-            *reinterpret_cast<int4 *>(sh.foff[par] + 4 * l) = int4{ex, ex + c.x, ex + c.x + c.y, ex + c.x + c.y + c.z};
-            if (l == kWave - 1) sh.ftot[par] = ex + tot;
-        }
-        __syncthreads();
-        // lane e holds this wave's offset for slot e
-        const uint32_t off_l = l < kFiltRegs ? static_cast<uint32_t>(sh.foff[par][l * kSelWaves + wv]) : 0u;
-        const int chunk_total = sh.ftot[par];
-        if (base + chunk_total <= cap) {
-#pragma unroll
-            for (int e = 0; e < kFiltRegs; ++e) {
-                const uint64_t km = ballot(keep[e]);
-                if (keep[e]) {
-                    const int slot = base + static_cast<int>(lane_value(off_l, e)) + mbcnt(km);
-                    store_as<kLds>(out_v, slot, v[e]);
-                    store_as<kLds>(out_p, slot, j0 + e * kSelThreads + tid);
-                }
-            }
-        }
-        base += chunk_total;
-        par ^= 1;
-    };
-    fetch(0);
-    int j0 = 0;
-    for (; j0 + CH <= n; j0 += CH) chunk(j0, std::false_type{});
-    if (j0 < n) chunk(j0, std::true_type{});
-    __syncthreads();  // the compacted entries are visible to the block
-    return base;
-}
-
 // Walk sc[0..n) in order (AS: the address space of sc and pos) and call
 // emit(slot, position, score) for every entry selected by s, where position
 // is pos[j] (or j when pos is null); slots are dense and ascending. One
@@ -1952,7 +1883,7 @@ __device__ int block_filter_above(const float *sc, int n, float tau, float *out_
 // to it: an entry's slot is (entries above before it) + min(equal entries
 // before it, quota).
 template <int AS, class F>
-__device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, BlockShared &sh, F &&emit)
+__device__ __forceinline__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, BlockShared &sh, F &&emit)
 {
     constexpr int CH = kVec * kSelThreads;
     const int tid = threadIdx.x;
@@ -2011,6 +1942,261 @@ __device__ int block_emit(const float *sc, const int32_t *pos, int n, Sel s, Blo
 
 constexpr int kSurvivors = 12288;  // LDS capacity of the prefilter (entries)
 
+// The fine bin holding the K-th largest of a row's scores, from the split
+// scan's counts at h ([splits][kRowHistWords]: kRowHistBins fine counts,
+// then kRowCoarseBins coarse ones): the coarse counts are summed over the
+// splits (one 16-byte load per thread per 16 splits), wave 0 finds the
+// coarse bin, then only its sixteen fine counts are read from every split.
+// above: entries in higher bins; inbin: entries in the bin.
+struct RowBin {
+    bool found;
+    uint32_t bin, above, inbin;
+};
+
+__device__ __forceinline__ RowBin row_bin(const uint32_t *h, int splits, int K, BlockShared &sh)
+{
+    static_assert(kRowCoarseBins == 4 * kWave && kSelThreads == 16 * kWave, "coarse layout: 4 bins per lane, 16 splits per pass");
+    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+    uint32_t *flat = &sh.hist[0][0];
+    // level 1: thread tid sums coarse bins 4 l .. 4 l + 3 of splits wv, wv + 16, ...
+    uint4 c = {0u, 0u, 0u, 0u};
+    for (int sp = wv; sp < splits; sp += kSelWaves) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(h + static_cast<int64_t>(sp) * kRowHistWords + kRowHistBins + 4 * l);
+        c.x += v.x;
+        c.y += v.y;
+        c.z += v.z;
+        c.w += v.w;
+    }
+    *reinterpret_cast<uint4 *>(flat + wv * kRowCoarseBins + 4 * l) = c;
+    __syncthreads();
+    if (wv == 0) {
+        uint32_t c4[4] = {0u, 0u, 0u, 0u};
+        for (int r = 0; r < kSelWaves; ++r) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(flat + r * kRowCoarseBins + 4 * l);
+            c4[0] += v.x;
+            c4[1] += v.y;
+            c4[2] += v.z;
+            c4[3] += v.w;
+        }
+        const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
+        const uint32_t suf = wave_suffix_sum(tot);  // lanes l and above (higher bins)
+        uint32_t above = suf - tot;
+        const uint32_t Ku = static_cast<uint32_t>(K);
+        if (l == 0) sh.bcast[3] = 0u;  // not found unless a lane finds it
+        if (above < Ku && above + tot >= Ku) {
+            int bsel = 3;
+            while (above + c4[bsel] < Ku) above += c4[bsel--];
+            sh.bcast[0] = static_cast<uint32_t>(4 * l + bsel);  // the coarse bin
+            sh.bcast[1] = above;                                // entries in higher coarse bins
+            sh.bcast[3] = 1u;
+        }
+    }
+    __syncthreads();
+    RowBin r{};
+    r.found = sh.bcast[3] != 0u;
+    if (!r.found) {
+        __syncthreads();
+        return r;
+    }
+    const uint32_t cb = sh.bcast[0];
+    // level 2: the sixteen fine counts of the coarse bin, summed over the
+    // splits (thread tid: fine bin tid % 16 of splits tid / 16, + 64, ...)
+    uint32_t f = 0u;
+    for (int sp = tid >> 4; sp < splits; sp += kSelThreads / 16)
+        f += h[static_cast<int64_t>(sp) * kRowHistWords + 16 * cb + (tid & 15)];
+    // the 64 partial sums of each fine bin: lanes of equal tid % 16 in a
+    // wave hold the same bin, so four lanes add (two lane swaps), then wave
+    // 0 adds the 16 waves' sums (lane i: bin i)
+    f += __shfl_xor(f, 16);
+    f += __shfl_xor(f, 32);
+    __syncthreads();  // level 1's counts are read
+    if (l < 16) flat[wv * 16 + l] = f;
+    __syncthreads();
+    if (wv == 0) {
+        uint32_t fi = 0u;
+        if (l < 16)
+            for (int r2 = 0; r2 < kSelWaves; ++r2) fi += flat[16 * r2 + l];
+        // lane i holds fine bin i; the bin where the count from above first
+        // reaches K (bins above it: lanes above)
+        const uint32_t suf = wave_suffix_sum(l < 16 ? fi : 0u);
+        const uint32_t above = sh.bcast[1] + suf - fi;
+        const uint32_t Ku = static_cast<uint32_t>(K);
+        const bool here = l < 16 && above < Ku && (above + fi >= Ku || l == 0);
+        const uint64_t hm = ballot(here);
+        const int src = hm ? 63 - __clzll(static_cast<long long>(hm)) : 0;  // the highest such bin
+        if (l == src) {
+            sh.bcast[0] = 16 * cb + static_cast<uint32_t>(l);
+            sh.bcast[1] = above;
+            sh.bcast[2] = fi;
+        }
+    }
+    __syncthreads();
+    r.bin = sh.bcast[0];
+    r.above = sh.bcast[1];
+    r.inbin = sh.bcast[2];
+    __syncthreads();  // bcast read before a next use rewrites it
+    return r;
+}
+
+// The K-th largest of the n scores in sc (LDS), each at or above bin (the
+// leading kRowHistBits bits of its order-preserving key), every one above
+// the bin taken: a radix select over the remaining 20 key bits of the bin's
+// keys (digits of 8, 8 and 4 bits) by the whole workgroup; per digit every
+// thread counts its keys into one 256-bin LDS histogram and wave 0 picks
+// the digit (three barriers per digit). The first digit's counts give the
+// bin's size, hence the rank of the K-th largest within it. found: that
+// rank lies in the bin (else the caller selects otherwise).
+__device__ __forceinline__ Sel block_select_bin(const float *sc, int n, int K, uint32_t bin, BlockShared &sh,
+                                                bool *found)
+{
+    const int tid = threadIdx.x, l = tid & 63;
+    uint32_t *hist = sh.digit_hist;
+    uint32_t prefix = bin << (32 - kRowHistBits), pmask = ~0u << (32 - kRowHistBits);
+    int remaining = 0;
+    Sel r;
+    r.all = false;
+    r.kth = 0u;
+    r.quota = 0;
+    for (int p = 0; p < 3; ++p) {
+        const int shift = p == 0 ? 12 : (p == 1 ? 4 : 0);
+        const uint32_t dmask = p == 2 ? 0xFu : 0xFFu;
+        if (tid < 256) hist[tid] = 0u;
+        __syncthreads();
+        for (int j = tid; j < n; j += kSelThreads) {
+            const uint32_t k = ord_key(load_as<kLds>(sc, j));
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            const uint32_t c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+            const uint32_t tot = c0 + c1 + c2 + c3;
+            const uint32_t suf = wave_suffix_sum(tot);
+            int rem = remaining;
+            if (p == 0) {
+                // the bin holds suf(lane 0) keys; the n - that many above it are all taken
+                const int nb = static_cast<int>(lane_value(suf, 0));
+                rem = K - (n - nb);
+                if (tid == 0) sh.bcast[2] = rem >= 1 && rem <= nb ? 1u : 0u;
+            }
+            const uint32_t ru = static_cast<uint32_t>(rem);
+            const uint32_t above = suf - tot;
+            if (rem >= 1 && above < ru && ru <= suf) {
+                uint32_t cum = above, dig;
+                if (cum + c3 >= ru) {
+                    dig = 4 * l + 3;
+                } else {
+                    cum += c3;
+                    if (cum + c2 >= ru) {
+                        dig = 4 * l + 2;
+                    } else {
+                        cum += c2;
+                        if (cum + c1 >= ru) {
+                            dig = 4 * l + 1;
+                        } else {
+                            cum += c1;
+                            dig = 4 * l;
+                        }
+                    }
+                }
+                sh.bcast[0] = dig;
+                sh.bcast[1] = static_cast<uint32_t>(rem) - cum;  // remaining after this digit
+            }
+        }
+        __syncthreads();
+        if (sh.bcast[2] == 0u) {  // uniform: the rank is not in the bin
+            __syncthreads();
+            *found = false;
+            return r;
+        }
+        remaining = static_cast<int>(sh.bcast[1]);
+        prefix |= sh.bcast[0] << shift;
+        pmask |= dmask << shift;
+        __syncthreads();  // bcast read before the next digit rewrites it
+    }
+    *found = true;
+    r.kth = prefix;
+    r.quota = remaining;
+    return r;
+}
+
+// Stable compaction of the entries of sc[0, n) whose score is above tau into
+// out_v / out_p (score, position; LDS) in ascending position; returns their
+// number (entries past cap are counted, not written). The row is read in
+// segments of kSelWaves * 4096 entries, a whole segment in registers at once
+// (wave w: entries 4096 w .. + 4096, sixteen 16-byte loads per lane), so a
+// segment costs one memory latency. A float comparison: the kept set is
+// {key > ord_key(tau)} (or {score > 0} when tau is -0), a threshold set either
+// way.
+__device__ __forceinline__ int block_filter_regs(const float *sc, int n, float tau, float *out_v, int32_t *out_p, int cap,
+                                                 BlockShared &sh)
+{
+    constexpr int E = 16, PER_WAVE = E * 4 * kWave, SEG = kSelWaves * PER_WAVE;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // entries past n read as zero through the buffer's bounds (whole
+    // 16-byte groups: the row's storage extends to a multiple of four
+    // entries) and are masked below
+    const __amdgpu_buffer_rsrc_t rs = row_buffer(sc, (n + 3) & ~3);
+    int base = 0;
+    for (int s0 = 0; s0 < n; s0 += SEG) {
+        const int w0 = s0 + wv * PER_WAVE;  // wave-uniform
+        uint32_t v[E][4];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * l, 4 * (w0 + e * 4 * kWave), 0);
+            v[e][0] = x[0];
+            v[e][1] = x[1];
+            v[e][2] = x[2];
+            v[e][3] = x[3];
+        }
+        // entry w0 + 256 e + 4 l + u is kept when 4 l + u < n - w0 - 256 e
+        // (a wave-uniform bound per group, so no per-entry position is held)
+        uint32_t km[E];  // kept sub-entries of each group (bits 0..3)
+        uint32_t tot = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int lim = n - w0 - e * 4 * kWave;
+            uint32_t m = 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m |= (4 * l + u < lim && __uint_as_float(v[e][u]) > tau) ? (1u << u) : 0u;
+            km[e] = m;
+            tot += static_cast<uint32_t>(__builtin_popcount(m));
+        }
+        const uint32_t wt = wave_sum(tot);
+        if (l == 0) sh.wave_sum[0][wv] = static_cast<int>(wt);
+        __syncthreads();
+        int woff = 0, stot = 0;
+        for (int x = 0; x < kSelWaves; ++x) {
+            const int c = sh.wave_sum[0][x];
+            woff += x < wv ? c : 0;
+            stot += c;
+        }
+        __syncthreads();  // wave_sum read before the next segment rewrites it
+        int off = base + woff;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t c = static_cast<uint32_t>(__builtin_popcount(km[e]));
+            const uint32_t incl = wave_incl_sum(c);
+            int slot = off + static_cast<int>(incl - c);
+            const int g0 = w0 + e * 4 * kWave;  // wave-uniform
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if ((km[e] >> u) & 1u) {
+                    if (slot < cap) {
+                        store_as<kLds>(out_v, slot, __uint_as_float(v[e][u]));
+                        store_as<kLds>(out_p, slot, g0 + 4 * l + u);
+                    }
+                    ++slot;
+                }
+            }
+            off += static_cast<int>(lane_value(incl, kWave - 1));
+        }
+        base += stot;
+    }
+    __syncthreads();  // the compacted entries are visible to the block
+    return base;
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
 {
     __shared__ BlockShared sh;
@@ -2057,73 +2243,47 @@ __global__ __launch_bounds__(kSelThreads) void k_select_rows(RowSelectArgs a)
         };
 
         // The split scan's counts of the row's scores by their leading key
-        // bits give the bin holding the K-th largest score; the scores at or
-        // above that bin are compacted into LDS, where the exact select
-        // runs. Falls back to the full row when they overflow LDS.
-        uint32_t key[kSelRegs];
-        bool in_lds = false, in_regs = false;
+        // bits give the bin holding the K-th largest score (coarse counts
+        // first, then the chosen coarse bin's sixteen fine ones); the scores
+        // at or above that bin are compacted into LDS, every one above the
+        // bin is taken, and the exact select runs over the bin's keys alone.
+        // Falls back to the full row when the survivors overflow LDS.
+        bool in_lds = false, in_bin = false;
+        uint32_t bin = 0u;
         if (n > 2 * a.K && a.hist) {
-            static_assert(kRowHistBins == 4 * kSelThreads, "four bins per thread");
-            const int l = tid & (kWave - 1), wv = tid >> 6;
-            uint32_t c4[4] = {0u, 0u, 0u, 0u};
-            const uint32_t *hg = a.hist + gid * a.splits * kRowHistBins + 4 * tid;
-            // the splits' counts are requested kHistBatch at a time (a short
-            // batch re-reads the last split and drops it), so a batch costs
-            // one memory latency, not one per split
-            constexpr int kHistBatch = 16;
-            for (int sp0 = 0; sp0 < a.splits; sp0 += kHistBatch) {
-                uint4 h[kHistBatch];
-#pragma unroll
-                for (int j = 0; j < kHistBatch; ++j) {
-                    const int sp = sp0 + j < a.splits ? sp0 + j : a.splits - 1;
-                    h[j] = *reinterpret_cast<const uint4 *>(hg + sp * kRowHistBins);
-                }
-#pragma unroll
-                for (int j = 0; j < kHistBatch; ++j) {
-                    const bool in = sp0 + j < a.splits;
-                    c4[0] += in ? h[j].x : 0u;
-                    c4[1] += in ? h[j].y : 0u;
-                    c4[2] += in ? h[j].z : 0u;
-                    c4[3] += in ? h[j].w : 0u;
-                }
-            }
-            // counts above each thread's bins: a block suffix sum (higher
-            // threads hold higher bins)
-            const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
-            const uint32_t suf = wave_suffix_sum(tot);  // within the wave, from this lane up
-            if (l == 0) sh.wave_sum[0][wv] = static_cast<int>(lane_value(suf, 0));
-            __syncthreads();
-            uint32_t higher = 0u;  // counts of the waves above this one
-            for (int x = wv + 1; x < kSelWaves; ++x) higher += static_cast<uint32_t>(sh.wave_sum[0][x]);
-            uint32_t above = higher + suf - tot;  // entries in bins above this thread's
-            const uint32_t K = static_cast<uint32_t>(a.K);
-            if (above < K && above + tot >= K) {
-                int bsel = 3;
-                while (above + c4[bsel] < K) above += c4[bsel--];
-                sh.bcast[0] = static_cast<uint32_t>(4 * tid + bsel);  // the bin holding the K-th largest
-                sh.bcast[1] = above;                                  // entries in higher bins
-                sh.bcast[2] = c4[bsel];                               // entries in it
-            }
-            __syncthreads();
-            const uint32_t bin = sh.bcast[0], keep = sh.bcast[1] + sh.bcast[2];
-            __syncthreads();
-            if (keep <= static_cast<uint32_t>(kSurvivors) && bin > 0u) {
+            const RowBin rb = row_bin(a.hist + gid * a.splits * kRowHistWords, a.splits, a.K, sh);
+            if (rb.found && rb.above + rb.inbin <= static_cast<uint32_t>(kSurvivors) && rb.bin > 0u) {
+                bin = rb.bin;
                 // keys >= bin << 20, i.e. scores above the float of the key just below
                 const float tau = key_float((bin << (32 - kRowHistBits)) - 1u);
-                const int kept = block_filter_above(row, n, tau, sel_scores, sel_pos, kSurvivors, sh);
+                const int kept = block_filter_regs(row, n, tau, sel_scores, sel_pos, kSurvivors, sh);
                 if (kept >= a.K && kept <= kSurvivors) {
                     n = kept;
-                    in_lds = true;
-                    block_load_keys<kLds>(sel_scores, n, key);
-                    in_regs = true;
+                    in_lds = in_bin = true;
                 }
             }
         }
-        if (!in_regs && n <= kSelRegs * kSelThreads) {
-            block_load_keys<kGlobal>(row, n, key);
-            in_regs = true;
+        Sel s;
+        bool have_s = false;
+        if (in_bin) {
+            // every kept key above the chosen bin is taken; the K-th
+            // largest is found among the bin's keys
+            bool found = false;
+            s = block_select_bin(sel_scores, n, a.K, bin, sh, &found);
+            have_s = found;
         }
-        const Sel s = in_regs ? block_select_regs(key, n, a.K, sh) : block_select(row, n, a.K, sh);
+        if (!have_s) {
+            uint32_t key[kSelRegs];
+            if (n <= kSelRegs * kSelThreads) {
+                if (in_lds)
+                    block_load_keys<kLds>(sel_scores, n, key);
+                else
+                    block_load_keys<kGlobal>(row, n, key);
+                s = block_select_regs(key, n, a.K, sh);
+            } else {
+                s = block_select(row, n, a.K, sh);
+            }
+        }
         const int got = in_lds ? block_emit<kLds>(sel_scores, sel_pos, n, s, sh, emit)
                                : block_emit<kGlobal>(row, nullptr, n, s, sh, emit);
         finish(got);
@@ -3139,7 +3299,7 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
 }
 
 int scan_sample_slots() { return kSampleSlots; }
-int row_hist_bins() { return kRowHistBins; }
+int row_hist_bins() { return kRowHistWords; }
 int refine_tile() { return kRefineTile; }
 
 int group_select_slabs(int cap)

@@ -1,7 +1,8 @@
 """GPU parity of the few-groups (decode) path against the oracle, aimed at
-the block-wide row selects: the group rows (prefilter into LDS from the split
-scan's score counts, the register radix select, the fallbacks to the full
-row) and the member rows of the split refine (held in registers up to
+the block-wide row selects: the group rows (the threshold bin from the split
+scan's coarse and fine score counts, the register-resident prefilter into
+LDS, the radix select over the bin's keys, the fallbacks to the full row)
+and the member rows of the split refine (held in registers up to
 c = 4096, streamed beyond).
 
 Exact inputs (q, k in {-3..3}/4, w powers of two) make every score exact, so
@@ -47,7 +48,8 @@ def _check_refine_and_reuse(q, w, k, g, topk, c):
 # name, B, Lk, c, topk: member rows in registers (c <= 4096) or streamed
 # (c > 4096); group rows selected in registers (prefix <= 16384), through
 # the count-driven prefilter (prefix > 2c, the threshold bin and above within
-# 12288 entries) or streamed (the rest)
+# 12288 entries; the exact select then runs over the threshold bin's keys) or
+# streamed (the rest)
 CASES = [
     ("c4095_regs", 2, 9000, 4095, 1000),
     ("c4096_regs", 2, 9000, 4096, 2048),
@@ -57,6 +59,10 @@ CASES = [
     ("prefilter_c1024", 2, 30000, 1024, 256),
     ("streamed_row_c5000", 1, 20000, 5000, 2048),  # no prefilter (3c > LDS), row > 16384: streamed select
     ("k1_c1", 2, 3000, 1, 1),
+    # one row of 100003 keys: the prefilter reads it in two register segments
+    # (65536 entries each, the second ragged) and sums the counts of
+    # hundreds of scan splits (both count levels loop over the splits)
+    ("prefilter_two_segments", 1, 100003, 4096, 2048),
 ]
 
 
