@@ -2133,9 +2133,12 @@ __device__ __forceinline__ int block_filter_regs(const float *sc, int n, float t
     constexpr int E = 16, PER_WAVE = E * 4 * kWave, SEG = kSelWaves * PER_WAVE;
     const int tid = threadIdx.x, l = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // entries past n read as zero through the buffer's bounds (whole
-    // 16-byte groups: the row's storage extends to a multiple of four
-    // entries) and are masked below
+    // entries past n read as zero through the buffer's bounds and are
+    // masked below. The bound is rounded up to whole 16-byte groups: the
+    // rows are the split scan's [B*G, Lk] floats in the workspace, whose
+    // regions are padded to 256 bytes, so the up to three floats read past
+    // a row end (the next row's, or the padding after the last row) lie
+    // inside the workspace.
     const __amdgpu_buffer_rsrc_t rs = row_buffer(sc, (n + 3) & ~3);
     int base = 0;
     for (int s0 = 0; s0 < n; s0 += SEG) {
