@@ -162,8 +162,15 @@ def cpu_baseline(q, w, k, W, variant, g, budget_s):
     n = int(max(threads, min(per_seq * W.B, budget_s / per_unit)))
     n = max(threads, n // threads * threads)
     units = np.unique(np.linspace(0, per_seq * W.B - 1, n).astype(np.int64))
+    # in at most four chunks (each call also allocates the workload's output
+    # rows), with a progress line each: a long budget runs for minutes
+    chunk = max(threads * 64, -(-len(units) // 4))
     t0 = time.perf_counter()
-    run(units)
+    for i in range(0, len(units), chunk):
+        run(units[i:i + chunk])
+        if len(units) > chunk:
+            log(f"[bench] cpu baseline: {min(i + chunk, len(units))} of {len(units)} units, "
+                f"{time.perf_counter() - t0:.0f} s")
     dt = time.perf_counter() - t0
     return {"value": len(units) * rows_per_unit / dt, "unit": "query positions/s", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model(), "nproc": os.cpu_count(),
