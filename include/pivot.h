@@ -284,7 +284,9 @@ pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32
  * the number of launches into launches[s] (arrays of PIVOT_STAGES entries;
  * either may be NULL), then forgets the records. Disabling also forgets them. */
 #define PIVOT_STAGES 5
-/* POOL: eq. (4); SCAN: eq. (5) with its streaming filter; SCAN_SELECT: the
+/* POOL: eq. (4) as its own launch (shapes without an MFMA scan; the MFMA
+ * scans pool inside and record none); SCAN: eq. (5) with its streaming
+ * filter; SCAN_SELECT: the
  * group's final top-k / top-c of eqs. (6)-(7) when the scan leaves survivors
  * for a separate kernel; SELECT: per-row selects (eq. (9), few-groups rows);
  * REFINE: eq. (8). */

@@ -245,7 +245,7 @@ pivot_status plan(const pivot_problem *p, const Cfg &cfg, bool paged, Layout *L)
     l.few = pivot::mfma_shape(sh) &&
             (cfg.path == PIVOT_PATH_SPLIT || (cfg.path == PIVOT_PATH_AUTO && static_cast<int64_t>(groups) < kFewGroups));
     // the proxies go through HBM only where the pool kernel forms them (the
-    // fused MFMA scan forms them from the member rows itself)
+    // MFMA scans, fused and split, form them from the member rows themselves)
     const bool pool_kernel = l.pool && !pivot::mfma_shape(sh);
     l.qbar = pool_kernel ? take(groups * p->heads * p->dim * elt) : 0;
     l.wbar = pool_kernel ? take(groups * p->heads * sizeof(float)) : 0;
