@@ -7,7 +7,8 @@ configuration the benchmark times.
                         row (dense) + every-row structure
   prefill_L131072       Refine and Reuse for g in {4, 8, 16} and dense (g = 1):
                         float rule on 512 evenly spaced groups for Refine g=8,
-                        on sampled groups/rows otherwise + every-row structure;
+                        128 for the other Refine and Reuse cases and 64 rows
+                        (plus the k boundary) for dense + every-row structure;
                         repeated calls bit-identical
   mtp_decode            Refine, float rule on every group (32 sequences);
                         repeated calls bit-identical
@@ -159,7 +160,7 @@ def test_prefill_32k_dense(prefill32k):
 
 @pytest.mark.parametrize("g", [8, 4, 16])
 def test_long_128k_refine(prefill128k, g):
-    _refine_case(prefill128k, LONG_128K, g, 512 if g == 8 else 10)
+    _refine_case(prefill128k, LONG_128K, g, 512 if g == 8 else 128)
 
 
 def test_long_128k_repeat_calls_are_bit_identical(prefill128k):
@@ -176,11 +177,11 @@ def test_long_128k_repeat_calls_are_bit_identical(prefill128k):
 
 @pytest.mark.parametrize("g", [8, 4, 16])
 def test_long_128k_reuse(prefill128k, g):
-    _reuse_case(prefill128k, LONG_128K, g, 10)
+    _reuse_case(prefill128k, LONG_128K, g, 128)
 
 
 def test_long_128k_dense(prefill128k):
-    _dense_case(prefill128k, LONG_128K, 6)
+    _dense_case(prefill128k, LONG_128K, 64)
 
 
 # ------------------------------------------------------------------- decode
