@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--workload", default=LONG_128K.name, choices=sorted(ALL))
     ap.add_argument("--variant", default="refine", choices=["refine", "reuse", "dense"])
     ap.add_argument("--g", type=int, default=None, help="group size (default: the workload's)")
+    ap.add_argument("--order", default="position", choices=["position", "score"],
+                    help="row order: ascending position (default) or rank order (adds the rank pass)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true",
@@ -297,7 +299,7 @@ def main():
         pool, table = paged_layout(k, lens, 64, W.seed)
         tpool = to_device(q[:1], w[:1], pool)[2]
         ttable, tlens = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
-        kcfg = pv.make_config(variant=variant_id, g=g, topk=W.topk, c=W.c)
+        kcfg = pv.make_config(variant=variant_id, g=g, topk=W.topk, c=W.c, order=args.order)
         ws = None
         log(f"[bench] ragged: lengths {int(lens.min())}..{int(lens.max())}, {pool.shape[0]} pages of 64 keys")
     else:
@@ -305,9 +307,13 @@ def main():
                          dtype=torch.uint8, device=dev)
         log(f"[bench] workspace {ws.numel() / 2**30:.2f} GiB")
 
+    ocfg = pv.make_config(variant=variant_id, g=g, topk=W.topk, c=W.c, order=args.order)
+
     def step():
         if ragged:
             return pv.index_kv(tq, tw, tpool, tlens, ttable, page_size=64, lk=W.Lk, cfg=kcfg)
+        if args.order != "position":
+            return pv.index(tq, tw, tk, ocfg, workspace=ws)
         if args.variant == "refine":
             return pv.index_refine(tq, tw, tk, g, W.topk, W.c, workspace=ws)
         if args.variant == "reuse":
@@ -411,7 +417,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{W.name} PIVOT-{args.variant}", "batch": W.B, "seq_len": W.Lk,
                    "query_rows": W.Lq, "heads": W.H, "dim": W.d, "g": g, "topk": W.topk,
-                   "c": W.c if args.variant == "refine" else None, "parallelism": "single GPU"},
+                   "c": W.c if args.variant == "refine" else None, "parallelism": "single GPU",
+                   **({"order": args.order} if args.order != "position" else {})},
         "roofline": roofline,
         "roofline_scan_select": roofline_scan_select,
         "cpu_baseline": cpu,

@@ -23,7 +23,8 @@
  *     q storage type (RNE); wbar stays fp32;
  *   - selection order: higher score first, equal scores by lower position;
  *   - every output row lists the selected positions in ASCENDING order,
- *     followed by -1 (scores: the matching values, then -INFINITY);
+ *     followed by -1 (scores: the matching values, then -INFINITY), unless
+ *     the config asks for rank order (pivot_config.order);
  *   - a row holds min(k, #eligible keys) valid entries; |C| = min(c, t_last+1).
  *
  * Layouts (dense, row-major, device memory unless stated):
@@ -56,11 +57,12 @@
  * as (batch * G * lk + batch * lq * min(c, lk)) * heads * dim, returns
  * PIVOT_ERR_UNSUPPORTED instead of running slowly.
  *
- * Departure from a score-ordered TopK: rows list positions in ascending
- * order, not by descending score. T_t is a set in the pages' definitions;
- * the kernels' selections are stable compactions in position order, and a
- * sort by score would add a k-entry sort per row that sparse attention does
- * not need. Callers that want score order sort (scores, indices) per row.
+ * Row order: by default rows list positions in ascending order, not by
+ * descending score. T_t is a set in the pages' definitions; the kernels'
+ * selections are stable compactions in position order, and sparse attention
+ * over T_t does not need a ranking. pivot_config.order = PIVOT_ORDER_SCORE
+ * (pivot_index, pivot_index_kv, pivot_index_static) adds one pass that puts
+ * every row in rank order (score descending, equal scores by lower position).
  */
 #ifndef PIVOT_H
 #define PIVOT_H
@@ -72,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PIVOT_ABI_VERSION 6
+#define PIVOT_ABI_VERSION 7
 
 typedef enum {
     PIVOT_OK = 0,
@@ -107,6 +109,19 @@ typedef enum { PIVOT_AGG_MEAN = 0, PIVOT_AGG_FIRST = 1, PIVOT_AGG_LAST = 2 } piv
  *   PIVOT_PATH_AUTO   SPLIT below 256 groups (batch * ceil(lq / g)), else
  *                     FUSED. */
 typedef enum { PIVOT_PATH_AUTO = 0, PIVOT_PATH_FUSED = 1, PIVOT_PATH_SPLIT = 2 } pivot_scan_path;
+
+/* Order of the entries inside an output row (indices and scores alike; the
+ * pages define T_t = TopK(I_{t,:}, k) as a set, eq. (1), and fix no order):
+ *   PIVOT_ORDER_POSITION  ascending position, then -1 (the default; what the
+ *                         kernels emit, and what pivot_index_stats reads);
+ *   PIVOT_ORDER_SCORE     rank order: score descending, equal scores by
+ *                         lower position (the selection rule itself), then
+ *                         -1. A pass over the finished rows permutes each
+ *                         row in place (one read and one write of indices
+ *                         and scores); it needs the scores output (its sort
+ *                         key) and 1 <= topk <= 8192. The Refine candidate
+ *                         set C stays in ascending position. */
+typedef enum { PIVOT_ORDER_POSITION = 0, PIVOT_ORDER_SCORE = 1 } pivot_order;
 
 /* Default guardrail of PIVOT_AUTO: the key count below which dense (g = 1) is
  * faster than PIVOT-Refine (g = 8, k = 2048, c = 4096) on MI355X, measured on
@@ -163,10 +178,13 @@ typedef struct {
     int32_t auto_variant;  /* PIVOT_AUTO: PIVOT_REUSE or PIVOT_REFINE above the guardrail */
     int32_t scan_path;     /* pivot_scan_path; 0 = PIVOT_PATH_AUTO */
     int64_t dense_below;   /* PIVOT_AUTO: dense when lk < dense_below; 0 = PIVOT_DENSE_BELOW_DEFAULT */
+    int32_t order;         /* pivot_order of the output rows; 0 = PIVOT_ORDER_POSITION */
+    int32_t reserved;      /* must be 0 */
 } pivot_config;
 
 /* Defaults: Refine, g = 8, topk = 2048, c = 4096, mean proxy, group rows,
- * auto_variant = Refine, automatic scan path, default guardrail. */
+ * auto_variant = Refine, automatic scan path, default guardrail, rows in
+ * ascending position. */
 pivot_status pivot_config_init(pivot_config *cfg);
 
 /* The variant a pivot_index call with this config runs (resolves PIVOT_AUTO). */
@@ -283,19 +301,20 @@ pivot_status pivot_index_stats(int64_t batch, int64_t lq, int32_t k, const int32
  * recorded events, adds the elapsed milliseconds of each stage into ms[s] and
  * the number of launches into launches[s] (arrays of PIVOT_STAGES entries;
  * either may be NULL), then forgets the records. Disabling also forgets them. */
-#define PIVOT_STAGES 5
+#define PIVOT_STAGES 6
 /* POOL: eq. (4) as its own launch (shapes without an MFMA scan; the MFMA
  * scans pool inside and record none); SCAN: eq. (5) with its streaming
  * filter; SCAN_SELECT: the
  * group's final top-k / top-c of eqs. (6)-(7) when the scan leaves survivors
  * for a separate kernel; SELECT: per-row selects (eq. (9), few-groups rows);
- * REFINE: eq. (8). */
+ * REFINE: eq. (8); ORDER: the rank-order pass of PIVOT_ORDER_SCORE. */
 typedef enum {
     PIVOT_STAGE_POOL = 0,
     PIVOT_STAGE_SCAN = 1,
     PIVOT_STAGE_SELECT = 2,
     PIVOT_STAGE_REFINE = 3,
-    PIVOT_STAGE_SCAN_SELECT = 4
+    PIVOT_STAGE_SCAN_SELECT = 4,
+    PIVOT_STAGE_ORDER = 5
 } pivot_stage;
 pivot_status pivot_timing_enable(int32_t on);
 pivot_status pivot_timing_read(double *ms, int64_t *launches);

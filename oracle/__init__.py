@@ -120,13 +120,40 @@ def _agg(agg) -> int:
     return AGGREGATIONS[agg]
 
 
+def rank_order(indices, scores):
+    """Rows in rank order: the selected entries by score, highest first, equal
+    scores by lower position, then the -1 padding (T_t = TopK(I_{t,:}, k) of
+    eq. (1), and of eqs. (6) and (9), listed in the order its selection rule
+    ranks them; the rows of ``run`` list the same set in ascending position).
+    indices [..., k] int32, scores [..., k] float32; returns new arrays."""
+    idx = np.asarray(indices)
+    sc = np.asarray(scores)
+    if idx.shape != sc.shape:
+        raise ValueError("indices and scores must have the same shape")
+    fi = idx.reshape(-1, idx.shape[-1])
+    fs = sc.reshape(-1, sc.shape[-1]).astype(np.float64)
+    pad = fi < 0
+    # np.lexsort: the last key is the primary one
+    order = np.lexsort((fi, -np.where(pad, 0.0, fs), pad), axis=-1)
+    out_i = np.take_along_axis(fi, order, axis=-1).reshape(idx.shape).astype(np.int32)
+    out_s = np.take_along_axis(sc.reshape(fi.shape), order, axis=-1).reshape(sc.shape).astype(np.float32)
+    return out_i, out_s
+
+
 def run(variant: int, q, w, k, topk: int, g: int = 1, c: int = 0, units=None, cand_in=None,
-        cand_in_n=None, want_scores=True, want_cand=True, lib_path=None, agg="mean", member_causal=False):
+        cand_in_n=None, want_scores=True, want_cand=True, lib_path=None, agg="mean", member_causal=False,
+        order="position"):
     """Run one variant. Returns a dict with 'indices', 'scores' (or None),
     'cand'/'cand_n' (Refine), 'counters' = (proxy, refine, dense) dot counts.
     Rows outside the requested ``units`` stay at -2 (indices) / nan (scores).
     ``agg`` picks the proxy (mean of eq. (4), or the first / last member);
-    ``member_causal`` (Reuse) bounds each member's top-k by its own t."""
+    ``member_causal`` (Reuse) bounds each member's top-k by its own t;
+    ``order`` "position" lists each row's set in ascending position, "score"
+    in rank order (``rank_order``; needs the scores)."""
+    if order not in ("position", "score"):
+        raise ValueError('order must be "position" or "score"')
+    if order == "score" and not want_scores:
+        raise ValueError("rank order needs the scores")
     q, w, k = _c(q), _c(w), _c(k)
     prob = _problem(q, w, k)
     B, Lq = prob.B, prob.Lq
@@ -153,6 +180,8 @@ def run(variant: int, q, w, k, topk: int, g: int = 1, c: int = 0, units=None, ca
                                     _ptr(counters))
     if rc != 0:
         raise ValueError(f"oracle_run failed with code {rc}")
+    if order == "score":
+        idx, sc = rank_order(idx, sc)
     return {"indices": idx, "scores": sc, "cand": cand, "cand_n": cand_n,
             "counters": tuple(float(x) for x in counters)}
 

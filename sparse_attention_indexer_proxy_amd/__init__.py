@@ -22,12 +22,13 @@ import torch
 __all__ = ["PivotError", "index_dense", "index_reuse", "index_refine", "index", "index_kv", "index_static", "resolve_variant", "pool",
            "index_stats",
            "proxy_scores", "workspace_size", "library_path", "load_library", "timing_enable", "timing_read",
-           "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "SCAN_PATHS", "DENSE_BELOW_DEFAULT",
+           "make_config", "Config", "DENSE", "REUSE", "REFINE", "AUTO", "AGGREGATIONS", "SCAN_PATHS", "ORDERS", "DENSE_BELOW_DEFAULT",
            "STAGES"]
 
 DENSE, REUSE, REFINE, AUTO = 0, 1, 2, 3
 AGGREGATIONS = {"mean": 0, "first": 1, "last": 2}
 SCAN_PATHS = {"auto": 0, "fused": 1, "split": 2}  # pivot_scan_path of the header
+ORDERS = {"position": 0, "score": 1}  # pivot_order of the header
 DENSE_BELOW_DEFAULT = 8192  # PIVOT_DENSE_BELOW_DEFAULT of the header
 _F32, _BF16 = 0, 1
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +41,7 @@ EXPORTED = ("pivot_workspace_size", "pivot_index_dense", "pivot_index_reuse", "p
             "pivot_pool", "pivot_pool_ex", "pivot_proxy_scores", "pivot_index_stats", "pivot_timing_enable",
             "pivot_timing_read",
             "pivot_status_str", "pivot_last_error", "pivot_abi_version")
-STAGES = ("pool", "scan", "select", "refine", "scan_select")
+STAGES = ("pool", "scan", "select", "refine", "scan_select", "order")
 
 
 class PivotError(RuntimeError):
@@ -58,7 +59,8 @@ class Config(ctypes.Structure):
     """pivot_config of the header."""
     _fields_ = [("variant", ctypes.c_int32), ("g", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("c", ctypes.c_int32), ("aggregation", ctypes.c_int32), ("member_causal", ctypes.c_int32),
-                ("auto_variant", ctypes.c_int32), ("scan_path", ctypes.c_int32), ("dense_below", ctypes.c_int64)]
+                ("auto_variant", ctypes.c_int32), ("scan_path", ctypes.c_int32), ("dense_below", ctypes.c_int64),
+                ("order", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Keys(ctypes.Structure):
@@ -180,9 +182,12 @@ def _workspace(prob, variant, g, topk, c, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _outputs(prob, topk, device, return_scores):
+def _outputs(prob, topk, device, return_scores, cfg=None):
+    """Index rows and, when asked for or needed as the rank-order sort key,
+    score rows."""
+    need = return_scores or (cfg is not None and cfg.order == ORDERS["score"])
     idx = torch.empty((prob.batch, prob.lq, topk), dtype=torch.int32, device=device)
-    sc = torch.empty((prob.batch, prob.lq, topk), dtype=torch.float32, device=device) if return_scores else None
+    sc = torch.empty((prob.batch, prob.lq, topk), dtype=torch.float32, device=device) if need else None
     return idx, sc
 
 
@@ -253,13 +258,17 @@ def index_refine(q, w, k, g: int, topk: int, c: int | None = None, *, return_sco
 
 def make_config(variant: int = REFINE, g: int = 8, topk: int = 2048, c: int | None = None,
                 aggregation: str = "mean", member_causal: bool = False, auto_variant: int = REFINE,
-                dense_below: int = 0, scan_path: str = "auto") -> Config:
+                dense_below: int = 0, scan_path: str = "auto", order: str = "position") -> Config:
     """A pivot_config (c defaults to 2k; dense_below 0 = the library's
-    guardrail; scan_path "auto", "fused" or "split")."""
+    guardrail; scan_path "auto", "fused" or "split"; order "position"
+    (ascending positions) or "score" (rank order: score descending, equal
+    scores by lower position))."""
     if aggregation not in AGGREGATIONS:
         raise ValueError(f"aggregation must be one of {sorted(AGGREGATIONS)}")
     if scan_path not in SCAN_PATHS:
         raise ValueError(f"scan_path must be one of {sorted(SCAN_PATHS)}")
+    if order not in ORDERS:
+        raise ValueError(f"order must be one of {sorted(ORDERS)}")
     cfg = Config()
     _check(load_library().pivot_config_init(ctypes.byref(cfg)))
     cfg.variant, cfg.g, cfg.topk = variant, g, topk
@@ -268,6 +277,7 @@ def make_config(variant: int = REFINE, g: int = 8, topk: int = 2048, c: int | No
     cfg.member_causal = 1 if member_causal else 0
     cfg.auto_variant, cfg.dense_below = auto_variant, dense_below
     cfg.scan_path = SCAN_PATHS[scan_path]
+    cfg.order = ORDERS[order]
     return cfg
 
 
@@ -283,7 +293,7 @@ def index(q, w, k, cfg: Config | None = None, *, return_scores: bool = False, re
           workspace=None, stream=None, **knobs):
     """The indexer under one config: ``cfg`` from ``make_config`` or the
     same keywords (variant, g, topk, c, aggregation, member_causal,
-    auto_variant, dense_below). variant=AUTO is the short-context guardrail:
+    auto_variant, dense_below, scan_path, order). variant=AUTO is the short-context guardrail:
     dense below ``dense_below`` keys, else ``auto_variant``. Candidates are
     returned (None when the call resolved to another variant) only with
     return_candidates."""
@@ -298,7 +308,7 @@ def index(q, w, k, cfg: Config | None = None, *, return_scores: bool = False, re
     if workspace is None:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
     wsb = workspace.numel() * workspace.element_size()
-    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores, cfg)
     cand = cand_n = None
     if return_candidates:
         resolved = ctypes.c_int32(0)
@@ -328,7 +338,7 @@ def index_static(q, w, k, cfg: Config | None = None, *, return_scores: bool = Fa
         raise TypeError("pass either cfg or keywords")
     prob, q, w, k, sq = _prepare(q, w, k)
     lib = load_library()
-    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores, cfg)
     cand = cand_n = None
     if return_candidates:
         resolved = ctypes.c_int32(0)
@@ -400,7 +410,7 @@ def index_kv(q, w, k, seq_lens=None, page_table=None, *, page_size: int = 0, lk:
     if workspace is None:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
     wsb = workspace.numel() * workspace.element_size()
-    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores)
+    idx, sc = _outputs(prob, cfg.topk, q.device, return_scores, cfg)
     cand = cand_n = None
     if return_candidates:
         resolved = ctypes.c_int32(0)

@@ -112,6 +112,7 @@ struct Cfg {
     int agg;      // pivot_aggregation
     bool causal;  // member-causal Reuse
     int path;     // pivot_scan_path
+    bool rank;    // rows in rank order (PIVOT_ORDER_SCORE)
 };
 
 struct Layout {
@@ -191,6 +192,13 @@ pivot_status resolve(const pivot_problem *p, const pivot_config *cfg, Cfg *out)
     if (cfg->scan_path < PIVOT_PATH_AUTO || cfg->scan_path > PIVOT_PATH_SPLIT)
         return fail(PIVOT_ERR_INVALID_ARG, "unknown scan_path %d", cfg->scan_path);
     c.path = cfg->scan_path;
+    if (cfg->reserved != 0) return fail(PIVOT_ERR_INVALID_ARG, "pivot_config.reserved must be 0");
+    if (cfg->order != PIVOT_ORDER_POSITION && cfg->order != PIVOT_ORDER_SCORE)
+        return fail(PIVOT_ERR_INVALID_ARG, "unknown order %d", cfg->order);
+    c.rank = cfg->order == PIVOT_ORDER_SCORE;
+    if (c.rank && (c.topk < 1 || c.topk > pivot::rank_rows_max()))
+        return fail(PIVOT_ERR_UNSUPPORTED, "PIVOT_ORDER_SCORE needs 1 <= topk <= %d (got %d)",
+                    pivot::rank_rows_max(), c.topk);
     *out = c;
     return PIVOT_OK;
 }
@@ -321,9 +329,11 @@ pivot_status check_keys(const pivot_problem *p, const pivot_keys *keys, KeysIn *
     return PIVOT_OK;
 }
 
-pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const KeysIn &kin,
-                 int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts, void *ws,
-                 size_t ws_bytes, void *stream)
+// The indexer's kernels up to the finished rows (each row's set in ascending
+// position).
+pivot_status run_rows(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const KeysIn &kin,
+                      int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts, void *ws,
+                      size_t ws_bytes, void *stream)
 {
     Layout L;
     const void *k = kin.k;
@@ -511,6 +521,22 @@ pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const fl
     return hip_status(pivot::launch_select_rows(sh, ms, s), "member select launch");
 }
 
+// run_rows, then (PIVOT_ORDER_SCORE) the rank-order pass over every row.
+pivot_status run(const pivot_problem *p, const Cfg &cfg, const void *q, const float *w, const KeysIn &kin,
+                 int32_t *indices, float *scores, int32_t *candidates, int32_t *cand_counts, void *ws,
+                 size_t ws_bytes, void *stream)
+{
+    if (cfg.rank && !scores)
+        return fail(PIVOT_ERR_INVALID_ARG, "PIVOT_ORDER_SCORE needs the scores output (its sort key)");
+    if (cfg.rank && p->batch * p->lq > 0x7FFFFFFF)
+        return fail(PIVOT_ERR_UNSUPPORTED, "PIVOT_ORDER_SCORE sorts at most 2^31 - 1 rows per call");
+    pivot_status st = run_rows(p, cfg, q, w, kin, indices, scores, candidates, cand_counts, ws, ws_bytes, stream);
+    if (st != PIVOT_OK || !cfg.rank) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    StageTimer tm(PIVOT_STAGE_ORDER, s);
+    return hip_status(pivot::launch_rank_rows(indices, scores, p->batch * p->lq, cfg.topk, s), "rank order launch");
+}
+
 Cfg basic(int variant, int32_t g, int32_t topk, int32_t c)
 {
     Cfg cfg{};
@@ -576,6 +602,7 @@ pivot_status pivot_config_init(pivot_config *cfg)
     cfg->auto_variant = PIVOT_REFINE;
     cfg->scan_path = PIVOT_PATH_AUTO;
     cfg->dense_below = 0;
+    cfg->order = PIVOT_ORDER_POSITION;
     return PIVOT_OK;
 }
 

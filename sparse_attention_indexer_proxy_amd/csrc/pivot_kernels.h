@@ -155,5 +155,10 @@ hipError_t launch_select_rows(const LaunchShape &sh, const RowSelectLaunch &L, h
 // Register-resident member selection needs c <= 4096; returns its slab count or 0.
 int member_select_slabs(int c);
 hipError_t launch_select_members(const LaunchShape &sh, const MemberSelectLaunch &L, hipStream_t st);
+// Rank order (pivot_order.hip): rows [rows, k] of positions and scores
+// reordered in place by score descending, equal scores by lower position,
+// -1 padding last; k <= rank_rows_max().
+int rank_rows_max();
+hipError_t launch_rank_rows(int32_t *idx, float *sc, int64_t rows, int k, hipStream_t st);
 
 }  // namespace pivot

@@ -135,6 +135,12 @@ def test_config_init_defaults(pivot_lib):
     (dict(variant=pv.REUSE, member_causal=1), 0),
     (dict(variant=pv.AUTO, auto_variant=pv.REUSE, member_causal=1), 0),
     (dict(aggregation=2), 0),
+    (dict(order=2), 1),                                         # unknown row order
+    (dict(reserved=1), 1),
+    (dict(order=1), 0),                                         # rank order, topk 16
+    (dict(order=1, topk=8192, c=8192), 0),                      # the rank pass's widest row
+    (dict(order=1, topk=8193, c=8200), 2),
+    (dict(order=0, topk=8193, c=8200), 0),
 ])
 def test_config_validation(pivot_lib, kw, expect):
     prob = _prob(Lq=4096, Lk=4096)
@@ -228,3 +234,24 @@ def test_config_scan_path_is_checked(pivot_lib):
     assert pivot_lib.pivot_index_workspace_size(ctypes.byref(prob), ctypes.byref(cfg), ctypes.byref(out)) == 1
     with pytest.raises(ValueError):
         pv.make_config(scan_path="elsewhere")
+
+
+def test_rank_order_needs_the_score_buffer(pivot_lib):
+    """PIVOT_ORDER_SCORE sorts rows by their scores: a call without the score
+    output is refused before anything is enqueued (no device needed)."""
+    prob = _prob(Lq=4096, Lk=4096)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: the check comes first
+    st = pivot_lib.pivot_index(ctypes.byref(prob), ctypes.byref(_cfg(order=1)), fake, fake, fake, fake, None, None,
+                               None, fake, 1 << 30, None)
+    assert st == 1
+    assert "scores" in pivot_lib.pivot_last_error().decode()
+
+
+def test_config_struct_matches_header():
+    """The binding's Config mirrors pivot_config field by field (48 bytes)."""
+    text = open(HEADER).read()
+    end = text.index("} pivot_config;")
+    body = text[text.rindex("typedef struct {", 0, end):end]
+    names = re.findall(r"(?:int32_t|int64_t)\s+(\w+);", body)
+    assert names == [f[0] for f in pv.Config._fields_]
+    assert ctypes.sizeof(pv.Config) == 48

@@ -121,6 +121,13 @@ def _check_oracle(gold, dtype, lib=None):
         r = oracle.reuse(q, w, k, G_SIZE, K, agg=agg, **kw)
         _check_rows(r["indices"], r["scores"], gold, f"reuse_{agg}_k2")
 
+    r = oracle.dense(q, w, k, 3, order="score", **kw)
+    _check_rows(r["indices"], r["scores"], gold, "dense_k3_rank")
+    r = oracle.refine(q, w, k, G_SIZE, K, 3, order="score", **kw)
+    _check_rows(r["indices"], r["scores"], gold, "refine_c3_rank")
+    r = oracle.reuse(q, w, k, G_SIZE, K, member_causal=True, order="score", **kw)
+    _check_rows(r["indices"], r["scores"], gold, "reuse_causal_k2_rank")
+
     for c in (3, 2):
         r = oracle.refine(q, w, k, G_SIZE, K, c, **kw)
         _check_rows(r["indices"], r["scores"], gold, f"refine_c{c}")
@@ -228,6 +235,17 @@ def test_library_reproduces_the_worked_example(gold, shape, pivot_lib):
         _check_rows(host(i), host(s), gold, f"refine_c{c}")
         np.testing.assert_array_equal(host(cand)[0], _idx(gold, f"refine_c{c}.cand"))
         np.testing.assert_array_equal(host(cand_n)[0], gold[f"refine_c{c}.cand_n"][0].astype(np.int32))
+
+    i, s = pv.index(tq, tw, tk, variant=pv.DENSE, g=1, topk=3, order="score", return_scores=True)
+    _check_rows(host(i), host(s), gold, "dense_k3_rank")
+    i, s = pv.index(tq, tw, tk, variant=pv.REFINE, g=G_SIZE, topk=K, c=3, order="score", return_scores=True)
+    _check_rows(host(i), host(s), gold, "refine_c3_rank")
+    i, s = pv.index(tq, tw, tk, variant=pv.REUSE, g=G_SIZE, topk=K, member_causal=True, order="score",
+                    return_scores=True)
+    _check_rows(host(i), host(s), gold, "reuse_causal_k2_rank")
+    # without return_scores the binding still hands the library a score buffer (the sort key)
+    i = pv.index(tq, tw, tk, variant=pv.REUSE, g=G_SIZE, topk=K, member_causal=True, order="score")
+    np.testing.assert_array_equal(host(i).reshape(L, -1), _idx(gold, "reuse_causal_k2_rank.idx"))
 
     i, s = pv.index_dense(tq, tw, tk, K, return_scores=True)
     st = pv.index_stats(i, s, d=1, g=G_SIZE)
