@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--workload", default=LONG_128K.name, choices=sorted(ALL))
     ap.add_argument("--variant", default="refine", choices=["refine", "reuse", "dense"])
     ap.add_argument("--g", type=int, default=None, help="group size (default: the workload's)")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="indexer heads (default: the workload's 64; 32 runs the 32-head MFMA kernels)")
     ap.add_argument("--order", default="position", choices=["position", "score"],
                     help="row order: ascending position (default) or rank order (adds the rank pass)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget")
@@ -284,6 +286,8 @@ def main():
     import sparse_attention_indexer_proxy_amd as pv
 
     W = ALL[args.workload]
+    if args.heads:
+        W = W.replace(H=args.heads, name=f"{W.name}_H{args.heads}")
     g = 1 if args.variant == "dense" else (args.g or W.g)
     t0 = time.perf_counter()
     from workloads import generate, to_device, seq_lens, paged_layout

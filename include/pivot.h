@@ -48,8 +48,8 @@
  * then describes it (thread-local). Calls are re-entrant; calls that share a
  * workspace must not overlap on different streams.
  *
- * Kernels: bf16 with heads == 64 and dim == 128 runs on bf16 MFMA with fp32
- * accumulation, at any size. Every other shape, and f32 inputs, runs the exact-order kernels:
+ * Kernels: bf16 with heads == 64 or 32 and dim == 128 runs on bf16 MFMA with
+ * fp32 accumulation, at any size. Every other shape, and f32 inputs, runs the exact-order kernels:
  * one lane per key, fp32 in the definition's order (heads ascending, dims
  * ascending, one rounding per product and per sum), so their results equal
  * a plain CPU evaluation bit for bit. They are meant for small problems: a
@@ -96,7 +96,7 @@ typedef enum { PIVOT_DENSE = 0, PIVOT_REUSE = 1, PIVOT_REFINE = 2, PIVOT_AUTO = 
  * the last member's own q and w taken unchanged. */
 typedef enum { PIVOT_AGG_MEAN = 0, PIVOT_AGG_FIRST = 1, PIVOT_AGG_LAST = 2 } pivot_aggregation;
 
-/* Which proxy-scan kernel family runs on the MFMA shape (bf16, 64 heads,
+/* Which proxy-scan kernel family runs on the MFMA shapes (bf16, 64 or 32 heads,
  * 128 dims); the results are the same either way:
  *   PIVOT_PATH_FUSED  one wave per group streams the group's key prefix
  *                     through LDS tiles shared by 8 groups and keeps only the

@@ -136,8 +136,8 @@ constexpr int64_t kFewGroups = 256;
 // deep per wave, so long-lived waves keep HBM busy).
 constexpr int64_t kSplitScanWorkgroups = PIVOT_SPLIT_SCAN_WGS;
 
-// Shapes without an MFMA kernel (f32, or bf16 with heads != 64 or dim !=
-// 128) run the exact-order kernels: one lane per key, fp32 in the
+// Shapes without an MFMA kernel (f32, or bf16 with heads other than 32 or
+// 64, or dim != 128) run the exact-order kernels: one lane per key, fp32 in the
 // definition's order. They are meant for small problems (and for bit-exact
 // checks); a call whose scan and refine need more multiply-adds than this is
 // refused rather than run slowly.
@@ -151,7 +151,7 @@ pivot_status check_exact_work(const pivot_problem *p, int64_t G, int64_t c)
     const double macs = pairs * double(p->heads) * double(p->dim);
     if (macs > kExactMaxMacs)
         return fail(PIVOT_ERR_UNSUPPORTED,
-                    "no MFMA kernel for %s with %d heads and dim %d (MFMA: bf16, 64 heads, dim 128); the exact-order "
+                    "no MFMA kernel for %s with %d heads and dim %d (MFMA: bf16, 64 or 32 heads, dim 128); the exact-order "
                     "kernels take at most 2^36 multiply-adds per call, this one needs about %.3g",
                     p->dtype == PIVOT_BF16 ? "bf16" : "f32", p->heads, p->dim, macs);
     return PIVOT_OK;

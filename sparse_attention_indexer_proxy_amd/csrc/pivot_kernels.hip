@@ -757,7 +757,9 @@ template <int RB, int NBLK, class Emit>
 __device__ __forceinline__ void tile_step(const bf16x8 (&afr)[RB][4], const float (&wr)[RB][4], const uint16_t *tile,
                                           int l, f32x4 (&carry)[RB], float (&pc)[3], bool have_prev, Emit &&emit)
 {
-    static_assert(RB == 4, "one reduction element per MFMA needs 16 MFMAs per block");
+    // a block is 4 RB MFMAs and leaves 4 RB accumulator elements per lane:
+    // one element of block cb - 1 is reduced beside each MFMA of block cb
+    static_assert(RB >= 1 && RB <= 4, "16 to 64 heads");
     static_assert(NBLK % 4 == 0 && NBLK >= 4, "whole 64-key quarters");
     f32x4 acc[2][RB];
     bf16x8 bq[2][4];
@@ -776,9 +778,11 @@ __device__ __forceinline__ void tile_step(const bf16x8 (&afr)[RB][4], const floa
             for (int rb = 0; rb < RB; ++rb) {
                 ac[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[rb][kb], bq[cb & 1][kb],
                                                                 kb == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : ac[rb], 0, 0, 0);
-                // element (kb, rb) of block cb - 1: accumulator kb, lane slot rb
-                const float relu = __int_as_float(max(__float_as_int(pv[kb][rb]), 0));
-                sum = fmaf(wr[kb][rb], relu, sum);
+                // element kb RB + rb of block cb - 1: accumulator (kb RB + rb) / 4,
+                // lane slot (kb RB + rb) % 4 (for RB = 4: accumulator kb, slot rb)
+                const int el = kb * RB + rb;
+                const float relu = __int_as_float(max(__float_as_int(pv[el >> 2][el & 3]), 0));
+                sum = fmaf(wr[el >> 2][el & 3], relu, sum);
                 asm volatile("" : "+v"(sum));  // keep the partial sum here, beside this MFMA
                 PIVOT_SCHED_FENCE();
             }
@@ -3184,7 +3188,7 @@ hipError_t launch_pool(const LaunchShape &sh, int g, int64_t G, const void *q, c
     return e;
 }
 
-bool mfma_shape(const LaunchShape &sh) { return sh.bf16 && sh.H == 64 && sh.D == 128; }
+bool mfma_shape(const LaunchShape &sh) { return sh.bf16 && (sh.H == 32 || sh.H == 64) && sh.D == 128; }
 
 hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t st)
 {
@@ -3212,14 +3216,25 @@ hipError_t launch_scan(const LaunchShape &sh, const ScanLaunch &L, hipStream_t s
         const dim3 mgrid(static_cast<uint32_t>(sh.B * ((L.G + kScanWaves - 1) / kScanWaves)));
         const dim3 mblock(kScanWaves * 64);
         const bool paged = sh.pages.table != nullptr;
-        if (rows && paged)
-            e = launch(&k_scan_mfma<64, 128, kRows, true>, mgrid, mblock, st, a);
-        else if (rows)
-            e = launch(&k_scan_mfma<64, 128, kRows, false>, mgrid, mblock, st, a);
-        else if (paged)
-            e = launch(&k_scan_mfma<64, 128, kFilter, true>, mgrid, mblock, st, a);
-        else
-            e = launch(&k_scan_mfma<64, 128, kFilter, false>, mgrid, mblock, st, a);
+        if (sh.H == 64) {
+            if (rows && paged)
+                e = launch(&k_scan_mfma<64, 128, kRows, true>, mgrid, mblock, st, a);
+            else if (rows)
+                e = launch(&k_scan_mfma<64, 128, kRows, false>, mgrid, mblock, st, a);
+            else if (paged)
+                e = launch(&k_scan_mfma<64, 128, kFilter, true>, mgrid, mblock, st, a);
+            else
+                e = launch(&k_scan_mfma<64, 128, kFilter, false>, mgrid, mblock, st, a);
+        } else {
+            if (rows && paged)
+                e = launch(&k_scan_mfma<32, 128, kRows, true>, mgrid, mblock, st, a);
+            else if (rows)
+                e = launch(&k_scan_mfma<32, 128, kRows, false>, mgrid, mblock, st, a);
+            else if (paged)
+                e = launch(&k_scan_mfma<32, 128, kFilter, true>, mgrid, mblock, st, a);
+            else
+                e = launch(&k_scan_mfma<32, 128, kFilter, false>, mgrid, mblock, st, a);
+        }
     } else if (sh.bf16) {
         if (rows)
             e = launch(&k_scan_exact<uint16_t, kRows>, grid, block, st, a);
@@ -3258,14 +3273,25 @@ hipError_t launch_refine(const LaunchShape &sh, const RefineLaunch &L, hipStream
     if (mfma_shape(sh)) {
         // 4 or 8 member waves; more members loop in rounds
         const bool paged = sh.pages.table != nullptr;
-        if (L.g <= 4 && paged)
-            e = launch(&k_refine_mfma<64, 128, 4, true>, grid, dim3(64 * 4), st, a);
-        else if (L.g <= 4)
-            e = launch(&k_refine_mfma<64, 128, 4, false>, grid, dim3(64 * 4), st, a);
-        else if (paged)
-            e = launch(&k_refine_mfma<64, 128, 8, true>, grid, dim3(64 * 8), st, a);
-        else
-            e = launch(&k_refine_mfma<64, 128, 8, false>, grid, dim3(64 * 8), st, a);
+        if (sh.H == 64) {
+            if (L.g <= 4 && paged)
+                e = launch(&k_refine_mfma<64, 128, 4, true>, grid, dim3(64 * 4), st, a);
+            else if (L.g <= 4)
+                e = launch(&k_refine_mfma<64, 128, 4, false>, grid, dim3(64 * 4), st, a);
+            else if (paged)
+                e = launch(&k_refine_mfma<64, 128, 8, true>, grid, dim3(64 * 8), st, a);
+            else
+                e = launch(&k_refine_mfma<64, 128, 8, false>, grid, dim3(64 * 8), st, a);
+        } else {
+            if (L.g <= 4 && paged)
+                e = launch(&k_refine_mfma<32, 128, 4, true>, grid, dim3(64 * 4), st, a);
+            else if (L.g <= 4)
+                e = launch(&k_refine_mfma<32, 128, 4, false>, grid, dim3(64 * 4), st, a);
+            else if (paged)
+                e = launch(&k_refine_mfma<32, 128, 8, true>, grid, dim3(64 * 8), st, a);
+            else
+                e = launch(&k_refine_mfma<32, 128, 8, false>, grid, dim3(64 * 8), st, a);
+        }
     } else if (sh.bf16) {
         e = launch(&k_refine_exact<uint16_t>, grid, dim3(256), st, a);
     } else {
@@ -3294,10 +3320,14 @@ hipError_t launch_scan_split(const LaunchShape &sh, const ScanLaunch &L, int spl
     a.rows = L.rows;
     a.hist = L.hist;
     const dim3 grid(static_cast<uint32_t>(sh.B * L.G * splits));
-    if (sh.pages.table)
+    if (sh.H == 64 && sh.pages.table)
         e = launch(&k_scan_split<64, 128, true>, grid, dim3(kSplitWaves * 64), st, a, splits);
-    else
+    else if (sh.H == 64)
         e = launch(&k_scan_split<64, 128, false>, grid, dim3(kSplitWaves * 64), st, a, splits);
+    else if (sh.pages.table)
+        e = launch(&k_scan_split<32, 128, true>, grid, dim3(kSplitWaves * 64), st, a, splits);
+    else
+        e = launch(&k_scan_split<32, 128, false>, grid, dim3(kSplitWaves * 64), st, a, splits);
     return e;
 }
 

@@ -209,18 +209,21 @@ def test_index_stats_validates_before_launch(pivot_lib):
     assert call(0, 8, 16, fake, None, 1, 1, out, None, None, None, None) == 1
 
 
-@pytest.mark.parametrize("H,D,dt", [(64, 128, 0), (32, 128, 1), (64, 64, 1)])
+@pytest.mark.parametrize("H,D,dt", [(64, 128, 0), (48, 128, 1), (64, 64, 1), (16, 128, 1)])
 def test_shapes_without_mfma_are_refused_above_the_exact_kernel_limit(pivot_lib, H, D, dt):
-    """f32 and bf16 shapes other than (64 heads, dim 128) run the exact-order
-    kernels only up to 2^36 multiply-adds per call: no slow fallback at size."""
+    """f32 and bf16 shapes other than (32 or 64 heads, dim 128) run the
+    exact-order kernels only up to 2^36 multiply-adds per call: no slow
+    fallback at size."""
     big = _prob(Lq=131072, Lk=131072, H=H, D=D, dt=dt)
     st, _ = _ws(pivot_lib, big, pv.REFINE, 8, 2048, 4096)
     assert st == 2
     assert "MFMA" in pivot_lib.pivot_last_error().decode()
     small = _prob(Lq=512, Lk=512, H=4, D=32, dt=0)  # the tiny f32 workload
     assert _ws(pivot_lib, small, pv.DENSE, 1, 16, 0)[0] == 0
-    mfma = _prob(Lq=131072, Lk=131072)  # bf16, 64 heads, dim 128: any size
-    assert _ws(pivot_lib, mfma, pv.DENSE, 1, 2048, 0)[0] == 0
+    for heads in (64, 32):  # bf16, 64 or 32 heads, dim 128: any size
+        mfma = _prob(Lq=131072, Lk=131072, H=heads)
+        assert _ws(pivot_lib, mfma, pv.DENSE, 1, 2048, 0)[0] == 0
+        assert _ws(pivot_lib, mfma, pv.REFINE, 8, 2048, 4096)[0] == 0
 
 
 def test_config_scan_path_is_checked(pivot_lib):

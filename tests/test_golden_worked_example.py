@@ -184,7 +184,7 @@ def _padded(gold, dtype, heads, dim):
     return to_storage(qp, dtype), wp.astype(np.float32), to_storage(kp, dtype)
 
 
-GPU_SHAPES = [(F32, 2, 4), (BF16, 2, 8), (BF16, 64, 128)]
+GPU_SHAPES = [(F32, 2, 4), (BF16, 2, 8), (BF16, 64, 128), (BF16, 32, 128)]
 
 
 @pytest.mark.gpu

@@ -113,6 +113,19 @@ def test_mfma_kernels_bitwise_on_exact_inputs(case, scan_path):
     _assert_bitwise(_gpu_all(q, w, k, g, topk, c, scan_path), _oracle_all(q, w, k, g, topk, c))
 
 
+MFMA32_EXACT_CASES = [c for c in MFMA_EXACT_CASES if c[0] in ("ragged_700", "g4_compactions", "decode_batch",
+                                                                 "L_below_k", "g16")]
+
+
+@pytest.mark.parametrize("case", MFMA32_EXACT_CASES, ids=[c[0] for c in MFMA32_EXACT_CASES])
+def test_mfma_32_heads_bitwise_on_exact_inputs(case, scan_path):
+    """The MFMA kernels compiled for 32 indexer heads (two 16-head row blocks
+    per group): bit for bit on exact inputs, both scan paths."""
+    name, B, Lq, Lk, g, topk, c, wl = case
+    q, w, k = exact_random(zlib.crc32(name.encode()) % 1000 + 7, B, Lq, Lk, 32, 128, BF16, w_levels=wl)
+    _assert_bitwise(_gpu_all(q, w, k, g, topk, c, scan_path), _oracle_all(q, w, k, g, topk, c))
+
+
 def test_mfma_all_equal_keys_fall_back_to_position(scan_path):
     L, g, topk, c = 200, 8, 16, 32
     q, w, _ = exact_random(5, 1, L, L, 64, 128, BF16)
@@ -126,10 +139,10 @@ def test_mfma_all_equal_keys_fall_back_to_position(scan_path):
     np.testing.assert_array_equal(gpu["reuse"][0], oracle.reuse(q, w, k, g, topk)["indices"])
 
 
-@pytest.mark.parametrize("seed", [1, 2])
-def test_mfma_kernels_float_rule_on_gaussian_inputs(seed, scan_path):
+@pytest.mark.parametrize("seed,H", [(1, 64), (2, 64), (3, 32)])
+def test_mfma_kernels_float_rule_on_gaussian_inputs(seed, H, scan_path):
     B, L, g, topk, c = 1, 600, 8, 24, 48
-    q, w, k = gauss_random(seed, B, L, L, 64, 128, BF16)
+    q, w, k = gauss_random(seed, B, L, L, H, 128, BF16)
     gpu = _gpu_all(q, w, k, g, topk, c, scan_path)
     ref = _oracle_all(q, w, k, g, topk, c)
     qf = q.view(np.uint16)

@@ -73,6 +73,8 @@ CASES = [
     # name, B, Lq, Lk, H, d, g, topk, c, dtype
     ("mfma_decode", 5, 4, 900, 64, 128, 4, 24, 48, BF16),
     ("mfma_prefill", 2, 300, 700, 64, 128, 8, 16, 32, BF16),
+    ("mfma32_decode", 3, 4, 900, 32, 128, 4, 24, 48, BF16),
+    ("mfma32_prefill", 2, 300, 700, 32, 128, 8, 16, 32, BF16),
     ("exact_decode", 4, 4, 300, 3, 8, 4, 6, 12, F32),
     ("exact_prefill_bf16", 3, 40, 90, 2, 16, 4, 5, 9, BF16),
 ]
@@ -84,7 +86,7 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_ragged_and_paged_match_oracle_bitwise(case, page, variant, path):
     name, B, Lq, Lk, H, d, g, topk, c, dt = case
-    if H != 64 and path == "split":
+    if H not in (32, 64) and path == "split":
         pytest.skip("the exact-order kernels have one scan path")
     seed = zlib.crc32(name.encode()) % 1000
     q, w, k = exact_random(seed, B, Lq, Lk, H, d, dt)

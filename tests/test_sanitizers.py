@@ -84,7 +84,7 @@ def test_abi_host_code_under_asan_and_ubsan(tmp_path):
         P = lambda B=1, Lq=64, Lk=64, H=64, D=128, dt=1: pv.Problem(B, Lq, Lk, H, D, dt)
         cases = [(P(), 2, 8, 16, 32), (P(Lq=65), 1, 8, 16, 0), (P(B=0), 0, 1, 16, 0), (P(), 1, 0, 16, 0),
                  (P(), 2, 8, 16, 8), (P(dt=7), 0, 1, 16, 0), (P(D=12), 0, 1, 16, 0),
-                 (P(Lk=2 ** 31, Lq=4), 0, 1, 16, 0), (P(), 9, 1, 16, 0), (P(H=32, Lq=131072, Lk=131072), 2, 8, 2048, 4096),
+                 (P(Lk=2 ** 31, Lq=4), 0, 1, 16, 0), (P(), 9, 1, 16, 0), (P(H=48, Lq=131072, Lk=131072), 2, 8, 2048, 4096),
                  (P(Lq=131072, Lk=131072), 2, 8, 2048, 4096), (P(B=32, Lq=4, Lk=65536), 2, 4, 2048, 4096)]
         got = [lib.pivot_workspace_size(ctypes.byref(p), v, g, k, c, ctypes.byref(sz)) for p, v, g, k, c in cases]
         assert got == [0, 1, 1, 1, 1, 1, 2, 1, 1, 2, 0, 0], got
