@@ -50,16 +50,19 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("variant", ["refine", "reuse"])
+@pytest.mark.parametrize("variant", ["refine", "reuse", "refine_rank"])
 def test_graph_replays_equal_eager_calls(case, variant):
     name, B, Lq, Lk, g, topk, c = case
     q0, w0, k0 = exact_random(61, B, Lq, Lk, 64, 128, BF16)
     tq, tw, tk = to_device(q0, w0, k0)
-    vid = pv.REFINE if variant == "refine" else pv.REUSE
+    vid = pv.REUSE if variant == "reuse" else pv.REFINE
     need = pv.workspace_size(vid, B, Lq, Lk, 64, 128, torch.bfloat16, g, topk, c)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    rank = pv.make_config(variant=pv.REFINE, g=g, topk=topk, c=c, order="score")
 
     def call(workspace):
+        if variant == "refine_rank":  # the rank-order pass after the selects
+            return pv.index(tq, tw, tk, rank, return_scores=True, workspace=workspace)
         if variant == "refine":
             return pv.index_refine(tq, tw, tk, g, topk, c, return_scores=True, workspace=workspace)
         return pv.index_reuse(tq, tw, tk, g, topk, return_scores=True, workspace=workspace)
@@ -80,7 +83,8 @@ def test_graph_replays_equal_eager_calls(case, variant):
         assert torch.equal(got_i, ref_i), f"{name} {variant} replay {step}: indices differ from the eager call"
         assert torch.equal(got_s, ref_s), f"{name} {variant} replay {step}: scores differ from the eager call"
         if step == 0:
-            ref = (oracle.refine(q, w, k, g, topk, c) if variant == "refine" else oracle.reuse(q, w, k, g, topk))
+            ref = (oracle.reuse(q, w, k, g, topk) if variant == "reuse" else
+                   oracle.refine(q, w, k, g, topk, c, order="score" if variant == "refine_rank" else "position"))
             np.testing.assert_array_equal(got_i.cpu().numpy(), ref["indices"])
             np.testing.assert_array_equal(got_s.cpu().numpy(), ref["scores"])
 
