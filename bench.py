@@ -428,6 +428,9 @@ def main():
         "cpu_baseline": cpu,
         "oracle_one_thread": one_thread,
         "sclk_ghz_observed": counters.get("sclk_ghz"),
+        "sclk_source": ("SQ_CYCLES per shader engine over the scan's traced duration, from the rocprofv3 counter run "
+                        "of this kernel source (profiles/scan_counters.json); not measured in this run"
+                        if counters.get("sclk_ghz") else None),
         "median_call_ms": median_call_ms,
         "practical_peak": practical,
         "scan_frac_of_practical_mfma": (achieved / practical["mfma_bf16_random_tflops"]
