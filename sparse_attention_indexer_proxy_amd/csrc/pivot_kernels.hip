@@ -2745,7 +2745,11 @@ __global__ __launch_bounds__(kMsWaves * kWave) void k_select_members(MemberSelec
 // position, written by k_scan_mfma) and writes the group's candidate set
 // (Refine) or the row of every member (Reuse, dense). NV > 0: the register
 // select above (cnt <= 64 NV); NV == 0: the streaming radix select over the
-// buffer in global memory, for any size.
+// buffer in global memory, for any size. Two waves per SIMD at least: at NV =
+// 128 the compiler would otherwise take 269 registers (one wave per SIMD);
+// capped at 256 it spills 13 loop-invariant values once (0.41 -> 0.25 ms at
+// 128K Refine g=8; the same cap on the member select, four waves at 128
+// registers, made it slower, 0.80 -> 0.86 ms).
 struct GroupSelectArgs {
     Geo geo;
     int K, cap;
@@ -2755,7 +2759,7 @@ struct GroupSelectArgs {
 };
 
 template <int NV>
-__global__ __launch_bounds__(kMsWaves * kWave) void k_select_groups(GroupSelectArgs a)
+__global__ __launch_bounds__(kMsWaves * kWave, 2) void k_select_groups(GroupSelectArgs a)
 {
     __shared__ uint32_t lds[kMsWaves][NV > 0 ? kMsMid + kHistBins + kWave : 256];
     const Geo &geo = a.geo;
