@@ -158,6 +158,16 @@ def test_prefill_32k_dense(prefill32k):
     _dense_case(prefill32k, PREFILL_32K, None)
 
 
+def test_prefill_32k_32_heads_refine_and_reuse():
+    """The 32K workload's generator with 32 indexer heads (the 32-head MFMA
+    kernels): 512 evenly spaced Refine and Reuse groups by the float rule."""
+    W = PREFILL_32K.replace(H=32, name="prefill_L32768_H32")
+    q, w, k = generate(W)
+    data = (q, w, k, to_device(q, w, k))
+    _refine_case(data, W, W.g, 512)
+    _reuse_case(data, W, W.g, 512)
+
+
 @pytest.mark.parametrize("g", [8, 4, 16])
 def test_long_128k_refine(prefill128k, g):
     _refine_case(prefill128k, LONG_128K, g, 512 if g == 8 else 128)
