@@ -81,12 +81,13 @@ MFMA_CASES = [
 ]
 
 
+@pytest.mark.parametrize("heads", [64, 32])
 @pytest.mark.parametrize("variant", ["dense", "reuse", "causal", "refine"])
 @pytest.mark.parametrize("case", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
-def test_mfma_rank_rows_bitwise(case, variant):
+def test_mfma_rank_rows_bitwise(case, variant, heads):
     name, B, Lq, Lk, g, topk, c = case
-    q, w, k = exact_random(zlib.crc32(name.encode()) % 1000, B, Lq, Lk, 64, 128, BF16)
-    print(f"[order] {name} {variant}", flush=True)
+    q, w, k = exact_random(zlib.crc32(name.encode()) % 1000, B, Lq, Lk, heads, 128, BF16)
+    print(f"[order] {name} {variant} H={heads}", flush=True)
     tq, tw, tk = to_device(q, w, k)
     gi, gs = _gpu(tq, tw, tk, variant, g, topk, c)
     ref = _oracle(q, w, k, variant, g, topk, c)
