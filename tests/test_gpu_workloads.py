@@ -79,6 +79,19 @@ def test_exact_workload_refine_and_reuse_bitwise(exact_data):
     np.testing.assert_array_equal(_np(r_s), ref["scores"])
 
 
+def test_exact_workload_rank_rows_bitwise(exact_data):
+    """The exact 8K workload's Refine rows in rank order (every row of k = 256)
+    equal the oracle's rows in rank order bit for bit."""
+    q, w, k, (tq, tw, tk) = exact_data
+    W = EXACT
+    i, sc = pv.index(tq, tw, tk, variant=pv.REFINE, g=W.g, topk=W.topk, c=W.c, order="score", return_scores=True)
+    torch.cuda.synchronize()
+    _say("[exact] oracle refine, rank order")
+    ref = oracle.refine(q, w, k, W.g, W.topk, W.c, order="score")
+    np.testing.assert_array_equal(_np(i), ref["indices"])
+    np.testing.assert_array_equal(_np(sc), ref["scores"])
+
+
 def test_exact_workload_dense_bitwise(exact_data):
     q, w, k, (tq, tw, tk) = exact_data
     W = EXACT
