@@ -141,6 +141,29 @@ def test_oracle_reproduces_the_worked_example(gold, dtype):
     _check_oracle(gold, dtype)
 
 
+def test_rank_rows_expose_planted_order_mistakes(gold):
+    """The hand-derived rank rows pin the order rule itself: the oracle's
+    dense top-3 put in rank order match them, while ranking equal scores by
+    the higher position, or ranking by ascending score, does not."""
+    q, w, k = _storage(gold, F32)
+    r = oracle.dense(q, w, k, 3)
+    idx, sc = r["indices"][0], r["scores"][0].astype(np.float64)
+    want = _idx(gold, "dense_k3_rank.idx")
+
+    def ranked(key):
+        out = np.full_like(idx, -1)
+        for t in range(L):
+            n = int((idx[t] >= 0).sum())
+            order = sorted(range(n), key=lambda j: key(sc[t, j], idx[t, j]))
+            out[t, :n] = idx[t, order]
+        return out
+
+    np.testing.assert_array_equal(ranked(lambda s_, p: (-s_, p)), want)
+    np.testing.assert_array_equal(oracle.rank_order(r["indices"], r["scores"])[0][0], want)
+    assert not np.array_equal(ranked(lambda s_, p: (-s_, -p)), want)   # ties by higher position
+    assert not np.array_equal(ranked(lambda s_, p: (s_, p)), want)      # lowest score first
+
+
 # Planted mistakes of the oracle (the same source edits as the pin battery's)
 # that the worked example must expose on its own. Two are out of its reach:
 # it has no short last group, and its proxies need no bf16 rounding.
